@@ -1,0 +1,13 @@
+"""fp64 CPU oracle for the log-mel front end.
+
+TEST INFRASTRUCTURE: only tests/, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it. It shares no code with the HIP
+library under ``log_mel_spectrogram_amd/`` and imports nothing from it.
+"""
+
+from .logmel_oracle import (  # noqa: F401
+    SAMPLE_RATE, N_FFT, HOP, N_BINS, N_MELS, F_MIN, F_MAX, LOG_FLOOR,
+    num_frames, frame_offsets, hamming_window, hz_to_mel, mel_to_hz,
+    mel_vertices_hz, mel_filterbank, frames_of, power_spectrum, mel_energy,
+    log_compress, logmel_frames, logmel_clip, logmel_packed, logmel_selected,
+)

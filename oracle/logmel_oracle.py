@@ -1,0 +1,207 @@
+"""Plain fp64 CPU oracle for the 128-bin log-mel front end.
+
+TEST INFRASTRUCTURE. Only tests/, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module. The product path
+(the HIP library and its Python binding) never imports, calls or links it, and
+this module imports nothing from the product path.
+
+What it computes, step by step, with the passage each step follows. "Page 1"
+is the tutorial "从零理解 ASR：音频基础、Qwen3-ASR 架构，以及离线 vs 流式推理原理"
+(marsggbo blog); its section 2.3 "Log-Mel Spectrogram 提取流水线" lists five
+steps, quoted here by number.
+
+1. Framing (page 1, §2.3 step 1 "分帧"): 400-sample frames (25 ms at 16 kHz)
+   every 160 samples (10 ms), no centring or padding. The page writes the
+   count for 30 s as (480000-400)/160+1; read as floor, and 0 frames for
+   fewer than 400 samples.
+2. Window (page 1, §2.3 step 2 "加窗", and the code of step 3, which calls
+   numpy's 400-point Hamming window): symmetric Hamming,
+   w[n] = 0.54 - 0.46 cos(2 pi n / 399), written out here rather than called.
+3. rFFT and power (page 1, §2.3 step 3 "FFT → 功率谱"): 400-point real FFT to
+   201 bins (0..8 kHz), power |X|^2 with no scaling. ``numpy.fft.rfft`` is
+   the library primitive for the transform; the tests pin it against a
+   brute-force DFT written as a double sum.
+4. Mel filterbank (page 1, §2.3 step 4 "Mel 滤波器组"): mel = 2595 log10(1 +
+   f/700); 128 triangular filters evenly spaced on the mel scale over
+   0..8000 Hz. Readings where the page is silent: the 130 triangle vertices
+   are evenly spaced in mel with the end vertices pinned to exactly 0 Hz and
+   8000 Hz; each triangle is linear in Hz between its vertices with peak 1
+   and no area normalisation. (The Hz-linear shape is a reading; the page
+   does not fix it.)
+5. Log (page 1, §2.3 step 5 "取对数"): natural log of max(mel energy, 1e-10),
+   numpy's maximum semantics (a NaN propagates).
+
+The output layout is frame-major [frames, 128] (page 1, the shape table after
+step 5). The streaming result is, by definition, this offline result on the
+concatenated stream.
+
+Everything here is fp64. The fp32 samples are upcast exactly.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+SAMPLE_RATE = 16000
+N_FFT = 400
+HOP = 160
+N_BINS = N_FFT // 2 + 1
+N_MELS = 128
+F_MIN = 0.0
+F_MAX = 8000.0
+LOG_FLOOR = 1e-10
+
+
+def num_frames(n_samples: int) -> int:
+    """Frame count of a clip of ``n_samples`` (page 1, §2.3 step 1).
+
+    floor((N - 400) / 160) + 1 for N >= 400, else 0. Exact integer arithmetic.
+    """
+    n = int(n_samples)
+    if n < N_FFT:
+        return 0
+    return (n - N_FFT) // HOP + 1
+
+
+def frame_offsets(sample_offsets) -> np.ndarray:
+    """Exclusive prefix sum of per-clip frame counts, int64, length n_clips+1.
+
+    Clip i holds samples [sample_offsets[i], sample_offsets[i+1]); its frames
+    are rows [result[i], result[i+1]) of the packed output.
+    """
+    so = [int(v) for v in np.asarray(sample_offsets).reshape(-1)]
+    out = [0]
+    for i in range(len(so) - 1):
+        out.append(out[-1] + num_frames(so[i + 1] - so[i]))
+    return np.asarray(out, dtype=np.int64)
+
+
+def hamming_window() -> np.ndarray:
+    """Symmetric 400-point Hamming window (page 1, §2.3 steps 2-3), fp64."""
+    n = np.arange(N_FFT, dtype=np.float64)
+    return 0.54 - 0.46 * np.cos(2.0 * np.pi * n / (N_FFT - 1))
+
+
+def hz_to_mel(f):
+    """HTK mel scale as printed in page 1, §2.3 step 4."""
+    return 2595.0 * np.log10(1.0 + np.asarray(f, dtype=np.float64) / 700.0)
+
+
+def mel_to_hz(m):
+    """Inverse of :func:`hz_to_mel`."""
+    return 700.0 * (10.0 ** (np.asarray(m, dtype=np.float64) / 2595.0) - 1.0)
+
+
+def mel_vertices_hz() -> np.ndarray:
+    """The 130 triangle vertices in Hz, evenly spaced in mel over 0..8000 Hz.
+
+    The end vertices are set to exactly F_MIN and F_MAX (the mel round trip
+    of 8000 Hz is 8000.000000000002 in fp64).
+    """
+    m = np.linspace(hz_to_mel(F_MIN), hz_to_mel(F_MAX), N_MELS + 2)
+    f = mel_to_hz(m)
+    f[0] = F_MIN
+    f[-1] = F_MAX
+    return f
+
+
+def mel_filterbank() -> np.ndarray:
+    """Dense [128, 201] fp64 filterbank (page 1, §2.3 step 4).
+
+    W[m, k] = max(0, min((phi_k - f_{m-1}) / (f_m - f_{m-1}),
+                         (f_{m+1} - phi_k) / (f_{m+1} - f_m)))
+    for filter m = 1..128 (row m-1), bin frequency phi_k = k * 16000 / 400.
+    """
+    f = mel_vertices_hz()
+    phi = np.arange(N_BINS, dtype=np.float64) * (SAMPLE_RATE / N_FFT)
+    W = np.zeros((N_MELS, N_BINS), dtype=np.float64)
+    for m in range(1, N_MELS + 1):
+        lo, mid, hi = f[m - 1], f[m], f[m + 1]
+        rise = (phi - lo) / (mid - lo)
+        fall = (hi - phi) / (hi - mid)
+        W[m - 1] = np.maximum(0.0, np.minimum(rise, fall))
+    return W
+
+
+_WINDOW = hamming_window()
+_FILTERBANK = mel_filterbank()
+
+
+def frames_of(x: np.ndarray) -> np.ndarray:
+    """[F, 400] fp64 frames of one clip (page 1, §2.3 step 1); frame f is
+    x[160 f : 160 f + 400]."""
+    x = np.asarray(x, dtype=np.float64).reshape(-1)
+    F = num_frames(x.size)
+    if F == 0:
+        return np.zeros((0, N_FFT), dtype=np.float64)
+    idx = HOP * np.arange(F)[:, None] + np.arange(N_FFT)[None, :]
+    return x[idx]
+
+
+def power_spectrum(frames: np.ndarray) -> np.ndarray:
+    """|rFFT(w * frame)|^2, [F, 201] fp64 (page 1, §2.3 steps 2-3)."""
+    spec = np.fft.rfft(frames * _WINDOW[None, :], n=N_FFT, axis=1)
+    return spec.real ** 2 + spec.imag ** 2
+
+
+def mel_energy(power: np.ndarray) -> np.ndarray:
+    """E[f, m] = sum_k W[m, k] P[f, k], [F, 128] fp64 (page 1, §2.3 step 4)."""
+    return power @ _FILTERBANK.T
+
+
+def log_compress(energy: np.ndarray) -> np.ndarray:
+    """ln(max(E, 1e-10)) with numpy maximum semantics (page 1, §2.3 step 5)."""
+    return np.log(np.maximum(energy, LOG_FLOOR))
+
+
+def logmel_frames(frames: np.ndarray):
+    """Whole chain on given [F, 400] frames. Returns (logmel, mel_energy)."""
+    E = mel_energy(power_spectrum(frames))
+    return log_compress(E), E
+
+
+def logmel_clip(x: np.ndarray, chunk: int = 65536):
+    """Log-mel of one clip: ([F, 128] fp64 log-mel, [F, 128] fp64 energy)."""
+    x = np.asarray(x, dtype=np.float64).reshape(-1)
+    F = num_frames(x.size)
+    L = np.empty((F, N_MELS), dtype=np.float64)
+    E = np.empty((F, N_MELS), dtype=np.float64)
+    for f0 in range(0, F, chunk):
+        f1 = min(F, f0 + chunk)
+        seg = x[HOP * f0: HOP * (f1 - 1) + N_FFT]
+        Lc, Ec = logmel_frames(frames_of(seg))
+        L[f0:f1] = Lc
+        E[f0:f1] = Ec
+    return L, E
+
+
+def logmel_packed(samples: np.ndarray, sample_offsets):
+    """Packed ragged batch: clip i is samples[so[i]:so[i+1]].
+
+    Returns (logmel [sum F, 128], energy [sum F, 128], frame_offsets).
+    """
+    so = np.asarray(sample_offsets, dtype=np.int64).reshape(-1)
+    fo = frame_offsets(so)
+    total = int(fo[-1])
+    L = np.empty((total, N_MELS), dtype=np.float64)
+    E = np.empty((total, N_MELS), dtype=np.float64)
+    for i in range(so.size - 1):
+        if fo[i + 1] == fo[i]:
+            continue
+        Li, Ei = logmel_clip(samples[so[i]:so[i + 1]])
+        L[fo[i]:fo[i + 1]] = Li
+        E[fo[i]:fo[i + 1]] = Ei
+    return L, E, fo
+
+
+def logmel_selected(samples: np.ndarray, sample_offsets, rows):
+    """Log-mel of selected output rows of a packed batch, one frame at a time
+    from its own 400 samples. Returns (logmel [R, 128], energy [R, 128])."""
+    so = np.asarray(sample_offsets, dtype=np.int64).reshape(-1)
+    fo = frame_offsets(so)
+    rows = np.asarray(rows, dtype=np.int64).reshape(-1)
+    clip = np.searchsorted(fo, rows, side="right") - 1
+    start = so[clip] + HOP * (rows - fo[clip])
+    frames = np.stack([np.asarray(samples[s:s + N_FFT], dtype=np.float64)
+                       for s in start]) if rows.size else np.zeros((0, N_FFT))
+    return logmel_frames(frames)

@@ -1,0 +1,346 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+None of these re-types the oracle's own formula and compares it with itself:
+each check comes from a page value, a closed form, an invariant, a textbook
+special case, or brute force written independently here. Each is chosen so
+that a plausible slip in the oracle (a periodic instead of symmetric window,
+a dropped 1/2, a wrong bin spacing, an off-by-one in framing, a log10 in
+place of ln, unpinned end vertices) fails at least one of them.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+# ---------------------------------------------------------------- page facts
+
+def test_page_parameters(golden_dir):
+    facts = json.load(open(os.path.join(golden_dir, "page_facts.json")))
+    assert O.SAMPLE_RATE == facts["sample_rate"]["value"]
+    assert O.N_FFT == facts["n_fft"]["value"]
+    assert O.HOP == facts["hop"]["value"]
+    assert O.N_BINS == facts["rfft_bins"]["value"]
+    assert O.N_MELS == facts["n_mels"]["value"]
+    assert O.LOG_FLOOR == facts["log_floor"]["value"]
+    assert len(O.hamming_window()) == facts["hamming_len"]["value"]
+    # 25 ms and 10 ms at 16 kHz
+    assert O.N_FFT == round(0.025 * O.SAMPLE_RATE)
+    assert O.HOP == round(0.010 * O.SAMPLE_RATE)
+    # mel formula constants (page 1, §2.3 step 4): evaluate at f = 700 Hz,
+    # where it is a * log10(2)
+    mf = facts["mel_formula"]
+    assert O.hz_to_mel(mf["b"]) == pytest.approx(mf["a"] * math.log10(2.0), rel=1e-15)
+
+
+def test_frame_count_page_example(golden_dir):
+    facts = json.load(open(os.path.join(golden_dir, "page_facts.json")))
+    ex = facts["frame_count_30s"]
+    exact = (ex["n_samples"] - 400) / 160 + 1          # 2998.5 as printed
+    F = O.num_frames(ex["n_samples"])
+    assert F == math.floor(exact) == 2998
+    assert abs(F - ex["page_value_approx"]) <= 2       # "≈ 3000"
+    assert O.num_frames(facts["samples_1s"]["value"]) == 98
+
+
+# ------------------------------------------------------------- framing pins
+
+def _brute_frame_count(n):
+    """Count starts s = 0, 160, 320, ... with a full 400-sample frame."""
+    c, s = 0, 0
+    while s + 400 <= n:
+        c += 1
+        s += 160
+    return c
+
+
+def test_frame_count_brute():
+    for n in list(range(0, 2400)) + [16000, 176000, 480000, 83_520_000 // 100]:
+        assert O.num_frames(n) == _brute_frame_count(n), n
+    # closed values (C truncation would give 1 for 241..399)
+    assert [O.num_frames(n) for n in (0, 241, 399, 400, 559, 560)] == [0, 0, 0, 1, 1, 2]
+    assert O.num_frames(83_520_000) == 521_998
+    assert O.num_frames(8000) == 48
+
+
+def test_frame_offsets_int64():
+    lens = [0, 399, 400, 401, 559, 560, 480000, 3_000_000_000]
+    so = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    fo = O.frame_offsets(so)
+    assert fo.dtype == np.int64
+    acc = [0]
+    for n in lens:
+        acc.append(acc[-1] + _brute_frame_count(n) if n < 10**6 else
+                   acc[-1] + (n - 400) // 160 + 1)
+    assert fo.tolist() == acc
+    assert so[-1] > 2**31 and fo[-1] == acc[-1]
+
+
+def test_frames_are_hop_strided():
+    x = np.arange(1000, dtype=np.float64)
+    fr = O.frames_of(x)
+    assert fr.shape == (4, 400)
+    for f in range(4):
+        assert np.array_equal(fr[f], np.arange(160 * f, 160 * f + 400))
+
+
+# -------------------------------------------------------------- window pins
+
+def test_window_closed_forms():
+    w = O.hamming_window()
+    # sum_{n=0}^{399} cos(2 pi n / 399) = 1 (a full period of 399 plus n=399)
+    assert w.sum() == pytest.approx(0.54 * 400 - 0.46 * 1.0, abs=1e-12)   # 215.54
+    # sum cos^2 = 200.5 -> sum w^2 = 158.569
+    assert (w ** 2).sum() == pytest.approx(
+        0.54 ** 2 * 400 - 2 * 0.54 * 0.46 * 1.0 + 0.46 ** 2 * 200.5, abs=1e-11)
+    assert np.allclose(w, w[::-1], atol=1e-15, rtol=0)          # symmetric
+    assert w[0] == pytest.approx(0.08, abs=1e-15)
+    assert w[399] == pytest.approx(0.08, abs=1e-15)
+    assert w.argmax() in (199, 200)
+
+
+def test_window_is_numpy_hamming():
+    # page 1 §2.3 step 3 calls numpy's Hamming window of length 400
+    assert np.max(np.abs(O.hamming_window() - np.hamming(400))) < 1e-15
+
+
+# ---------------------------------------------------------- transform pins
+
+def _brute_dft(y):
+    N = len(y)
+    n = np.arange(N)
+    X = np.zeros(N, dtype=np.complex128)
+    for k in range(N):
+        X[k] = np.sum(y * np.exp(-2j * np.pi * k * n / N))
+    return X
+
+
+def test_power_spectrum_vs_brute_dft():
+    rng = np.random.default_rng(1)
+    fr = rng.uniform(-1, 1, (3, 400))
+    P = O.power_spectrum(fr)
+    w = np.array([0.54 - 0.46 * math.cos(2 * math.pi * n / 399) for n in range(400)])
+    for i in range(3):
+        X = _brute_dft(fr[i] * w)
+        ref = np.abs(X[:201]) ** 2
+        assert np.max(np.abs(P[i] - ref)) <= 1e-10 * np.max(ref)
+
+
+def test_parseval():
+    rng = np.random.default_rng(2)
+    fr = rng.normal(size=(16, 400))
+    P = O.power_spectrum(fr)
+    w = O.hamming_window()
+    lhs = np.sum((fr * w) ** 2, axis=1)
+    rhs = (P[:, 0] + 2 * P[:, 1:200].sum(axis=1) + P[:, 200]) / 400
+    assert np.allclose(lhs, rhs, rtol=1e-13, atol=0)
+
+
+@pytest.mark.parametrize("k0", [1, 5, 25, 75, 150, 199])
+def test_pure_tone(k0):
+    """A sin(2 pi (40 k0) n / 16000) -> bin k0 with power
+    (A/2)^2 |sum w - What(2 k0)|^2, What the window's DFT written as a sum;
+    for k0 away from the ends that is (A sum w / 2)^2 to within 2e-3."""
+    A = 0.3
+    n = np.arange(400)
+    x = A * np.sin(2 * np.pi * 40 * k0 * n / 16000)
+    P = O.power_spectrum(x[None, :])[0]
+    w = np.array([0.54 - 0.46 * math.cos(2 * math.pi * m / 399) for m in range(400)])
+    What = np.sum(w * np.exp(-2j * np.pi * (2 * k0) * n / 400))
+    exact = (A / 2) ** 2 * abs(w.sum() - What) ** 2
+    assert P[k0] == pytest.approx(exact, rel=1e-12)
+    assert int(np.argmax(P)) == k0
+    if 2 <= k0 <= 198:
+        assert P[k0] == pytest.approx((A * 215.54 / 2) ** 2, rel=2e-3)
+
+
+# ----------------------------------------------------------------- mel pins
+
+def test_mel_scale_values():
+    assert O.hz_to_mel(0.0) == 0.0
+    assert O.hz_to_mel(8000.0) == pytest.approx(2595 * math.log10(1 + 8000 / 700), rel=1e-15)
+    assert O.hz_to_mel(8000.0) == pytest.approx(2840.023046708319, rel=1e-14)
+    # natural-log form 1127 ln(1 + f/700) agrees to the constant's precision
+    for f in (100.0, 1000.0, 4000.0):
+        assert O.hz_to_mel(f) == pytest.approx(2595 / math.log(10) * math.log(1 + f / 700), rel=1e-15)
+    for f in (1.0, 440.0, 7999.0):
+        assert O.mel_to_hz(O.hz_to_mel(f)) == pytest.approx(f, rel=1e-12)
+
+
+def test_mel_vertices():
+    f = O.mel_vertices_hz()
+    assert f.size == 130
+    assert f[0] == 0.0 and f[-1] == 8000.0           # pinned exactly
+    m = O.hz_to_mel(f)
+    step = 2595 * math.log10(1 + 8000 / 700) / 129
+    assert np.allclose(np.diff(m), step, rtol=0, atol=1e-9)   # even in mel
+    assert np.all(np.diff(f) > 0) and np.all(np.diff(np.diff(f)) > 0)  # dense low
+
+
+def _interp_weight(m, phi, f):
+    """Triangle m as a piecewise-linear interpolation through its vertices."""
+    return np.interp(phi, [f[m - 1], f[m], f[m + 1]], [0.0, 1.0, 0.0],
+                     left=0.0, right=0.0)
+
+
+def test_filterbank_vs_interpolation():
+    W = O.mel_filterbank()
+    f = O.mel_vertices_hz()
+    phi = 40.0 * np.arange(201)
+    for m in range(1, 129):
+        assert np.allclose(W[m - 1], _interp_weight(m, phi, f), atol=1e-14, rtol=0)
+
+
+def test_filterbank_invariants():
+    W = O.mel_filterbank()
+    f = O.mel_vertices_hz()
+    assert W.shape == (128, 201)
+    assert W.min() >= 0.0 and W.max() <= 1.0
+    # bins 0 and 200 sit on the pinned end vertices: exactly zero weight
+    assert np.all(W[:, 0] == 0.0) and np.all(W[:, 200] == 0.0)
+    # each bin lies in at most two triangles
+    assert ((W > 0).sum(axis=0)).max() == 2
+    # partition of unity between the first and last peaks
+    phi = 40.0 * np.arange(201)
+    inner = (phi >= f[1]) & (phi <= f[128])
+    assert np.allclose(W[:, inner].sum(axis=0), 1.0, atol=1e-13, rtol=0)
+    # a filter is empty exactly when no bin falls strictly inside its support
+    brute_empty = [m for m in range(1, 129)
+                   if not np.any((phi > f[m - 1]) & (phi < f[m + 1]))]
+    assert brute_empty == [1, 4, 7, 14]
+    assert [m for m in range(1, 129) if not np.any(W[m - 1] > 0)] == brute_empty
+    assert int((W > 0).sum()) == 394
+    # no area normalisation: each non-empty filter's largest weight is the
+    # interpolation at the bin nearest its peak, and the top one is < 1
+    assert W.max() == pytest.approx(0.9972954518776668, abs=1e-12)
+
+
+def test_whole_chain_brute_force():
+    """Full chain on tiny inputs from independent pieces: the window written
+    out, the DFT as a double sum, each triangle as a piecewise-linear
+    interpolation through its vertices (vertices from the mel formula
+    evaluated with math.log10), and ln(max(E, 1e-10))."""
+    a = 2595.0 * math.log10(1.0 + 8000.0 / 700.0)
+    f = [700.0 * (10.0 ** (a * i / 129 / 2595.0) - 1.0) for i in range(130)]
+    f[0], f[129] = 0.0, 8000.0
+    w = np.array([0.54 - 0.46 * math.cos(2 * math.pi * n / 399) for n in range(400)])
+    rng = np.random.default_rng(8)
+    n = np.arange(400)
+    frames = [rng.uniform(-1, 1, 400),
+              0.3 * np.sin(2 * np.pi * 200 * n / 16000),
+              1e-4 * rng.normal(size=400)]
+    for x in frames:
+        X = _brute_dft(x * w)
+        P = np.abs(X[:201]) ** 2
+        phi = 40.0 * np.arange(201)
+        E = np.array([np.sum(_interp_weight(m, phi, np.array(f)) * P)
+                      for m in range(1, 129)])
+        ref = np.log(np.maximum(E, 1e-10))
+        L, Eo = O.logmel_frames(x[None, :])
+        # fp64 rounding is relative to the frame's largest energy
+        assert np.allclose(Eo[0], E, rtol=1e-9, atol=1e-13 * E.max())
+        ok = E > 1e-6 * E.max()
+        assert np.allclose(L[0][ok], ref[ok], rtol=0, atol=1e-9)
+        assert np.array_equal(L[0][E == 0], ref[E == 0])
+
+
+def test_white_noise_mel_expectation():
+    """E[E_m] = sigma^2 * sum w^2 * sum_k W[m,k] for white noise."""
+    rng = np.random.default_rng(3)
+    sigma = 0.01
+    x = rng.normal(0, sigma, 160 * 20000 + 240)
+    L, E = O.logmel_clip(x)
+    W = O.mel_filterbank()
+    w2 = 0.54 ** 2 * 400 - 2 * 0.54 * 0.46 + 0.46 ** 2 * 200.5
+    expect = sigma ** 2 * w2 * W.sum(axis=1)
+    nz = expect > 0
+    # bins 1..199 only: no DC / Nyquist weight, so no factor-2 bins involved
+    assert np.allclose(E.mean(axis=0)[nz], expect[nz], rtol=0.05)
+
+
+# ----------------------------------------------------------------- log pins
+
+def test_silence():
+    L, E = O.logmel_clip(np.zeros(16000))
+    assert L.shape == (98, 128)
+    assert np.all(E == 0.0)
+    assert np.all(L == math.log(1e-10))
+    assert L[0, 0] == -23.025850929940457
+
+
+def test_empty_filters_floor():
+    x = np.random.default_rng(4).uniform(-1, 1, 4000)
+    L, E = O.logmel_clip(x)
+    for m in (1, 4, 7, 14):
+        assert np.all(L[:, m - 1] == math.log(1e-10))
+
+
+def test_scale_invariance():
+    rng = np.random.default_rng(5)
+    x = rng.uniform(-0.5, 0.5, 4000)
+    L1, E1 = O.logmel_clip(x)
+    for c in (0.25, -3.0):
+        L2, E2 = O.logmel_clip(c * x)
+        ok = (E1 >= 1e-10) & (E2 >= 1e-10)
+        assert np.allclose(L2[ok], L1[ok] + 2 * math.log(abs(c)), atol=1e-12)
+
+
+def test_natural_log_not_log10():
+    x = np.zeros(400)
+    x[200] = 1.0                 # impulse: P[k] = w[200]^2 for every bin
+    L, E = O.logmel_clip(x)
+    W = O.mel_filterbank()
+    w200 = 0.54 - 0.46 * math.cos(2 * math.pi * 200 / 399)
+    m = 60
+    assert L[0, m] == pytest.approx(math.log(w200 ** 2 * W[m].sum()), rel=1e-13)
+
+
+def test_nan_propagates():
+    x = np.zeros(400)
+    x[10] = np.nan
+    L, _ = O.logmel_clip(x)
+    assert np.isnan(L[0, 60])
+
+
+# ------------------------------------------------------- framing invariants
+
+def test_shift_by_hop():
+    rng = np.random.default_rng(6)
+    x = rng.uniform(-1, 1, 5000)
+    L1, _ = O.logmel_clip(x)
+    L2, _ = O.logmel_clip(x[160:])
+    assert np.array_equal(L1[1:], L2)
+
+
+def test_periodic_signal_identical_frames():
+    """200/1000/3000 Hz tones have a common period of 80 samples; the hop is
+    160, so every frame of the noiseless signal is the same frame."""
+    n = np.arange(16000)
+    x = sum(0.3 * np.sin(2 * np.pi * f * n / 16000) for f in (200, 1000, 3000))
+    L, E = O.logmel_clip(x)
+    assert L.shape == (98, 128)
+    # identical up to fp64 rounding, which is relative to the loudest band
+    assert np.max(np.abs(E - E[0])) < 1e-12 * E.max()
+    loud = E[0] > 1e-6 * E.max()
+    assert np.max(np.abs(L[:, loud] - L[0, loud])) < 1e-9
+
+
+def test_packed_equals_per_clip():
+    rng = np.random.default_rng(7)
+    lens = [0, 399, 400, 1000, 37, 2000]
+    so = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    s = rng.uniform(-1, 1, so[-1])
+    L, E, fo = O.logmel_packed(s, so)
+    for i, n in enumerate(lens):
+        Li, _ = O.logmel_clip(s[so[i]:so[i + 1]])
+        assert np.array_equal(L[fo[i]:fo[i + 1]], Li)
+    rows = np.arange(fo[-1])
+    Ls, _ = O.logmel_selected(s, so, rows)
+    assert np.allclose(Ls, L, atol=1e-12, rtol=0)
