@@ -1,0 +1,274 @@
+#!/usr/bin/env python3
+"""Throughput of the 128-bin log-mel front end on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c4|c3|c1]
+
+Prints one JSON line. A step is one logmel_compute over one batch of
+synthetic input already resident in HBM: framing, window, rFFT, power, mel
+and log for every frame of the batch (frame offsets are computed once, on
+the host, before the timed region). The default workload is the offline
+batch of 64 speech-like 30 s clips (64 x 480000 fp32 samples); the timed
+loop rotates over 5 copies of input and output buffers (1.1 GB) so that
+successive steps do not hit in the 256 MB Infinity Cache.
+
+``value`` is audio-seconds per second (sum of samples / 16000 per step,
+divided by the wall time per step, measured between device synchronisations
+around exactly K steps). ``roofline.achieved`` is the kernel's algorithmic
+HBM bytes (4 B per input sample + 512 B per output frame + the offsets)
+divided by the kernel's average duration from HIP events recorded around
+each launch on the stream it runs on. ``cpu_baseline`` times the fp64 oracle
+on the host cores over the same clips (a bounded sample: repeated passes for
+about --cpu-seconds seconds).
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+FS = 16000
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("logmel_kernels.hip", "logmel_frame.h", "gen_tables.py"):
+        with open(os.path.join(ROOT, "log_mel_spectrogram_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"logmel_tiles_{workload}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    rec = None
+    for line in open(path):
+        if line.startswith("TRAFFIC_JSON "):
+            rec = json.loads(line[len("TRAFFIC_JSON "):])
+    if not rec or rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+# ------------------------------------------------------------ CPU baseline
+
+def _oracle_worker(args):
+    import numpy as np
+    x, reps = args
+    from oracle import logmel_clip
+    for _ in range(reps):
+        logmel_clip(x)
+    return 0
+
+
+def cpu_baseline(clips, seconds):
+    """fp64 oracle over the given clips (list of numpy fp32 arrays) on a
+    process pool of the host's cores (at most 16), one BLAS thread each."""
+    import multiprocessing as mp
+    for v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[v] = "1"
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    ctx = mp.get_context("spawn")
+    audio_per_pass = sum(c.size for c in clips) / FS
+    with ctx.Pool(cores) as pool:
+        pool.map(_oracle_worker, [(clips[i % len(clips)], 1) for i in range(cores)])  # warm
+        t0 = time.perf_counter()
+        pool.map(_oracle_worker, [(c, 1) for c in clips])
+        one = time.perf_counter() - t0
+        reps = max(1, int(seconds / max(one, 1e-3)))
+        t0 = time.perf_counter()
+        pool.map(_oracle_worker, [(c, reps) for c in clips])
+        dt = time.perf_counter() - t0
+    return {
+        "value": audio_per_pass * reps / dt,
+        "unit": "audio-seconds/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"{len(clips)} clips of the workload ({audio_per_pass:.0f} audio-s), "
+                  f"{reps} passes, {dt:.1f} s wall",
+    }
+
+
+# ---------------------------------------------------------------- workloads
+
+def make_workload(name, device):
+    import logmel_synth as S
+    if name == "c2":
+        x, so = S.config2(device=device)
+        desc = "offline batch: 64 speech-like clips x 30 s (480000 fp32 samples each), packed"
+    elif name == "c1":
+        x, so = S.config1(device=device)
+        desc = "1 speech-like clip, 30 s (480000 fp32 samples)"
+    elif name == "c4":
+        x, so = S.config4(device=device)
+        desc = ("ragged long batch: 200 speech-like clips, log-uniform 0.5 s..87 min, "
+                "packed with int64 offsets")
+    else:
+        raise ValueError(name)
+    return x, so, desc
+
+
+def bench_offline(args, lm, plan, torch):
+    dev = torch.device("cuda", 0)
+    x, so, desc = make_workload(args.workload, dev)
+    fo = lm.logmel_frame_offsets(so)
+    total = int(fo[-1])
+    n_samples = int(so[-1])
+    so_d = torch.from_numpy(so).to(dev)
+    fo_d = torch.from_numpy(fo).to(dev)
+    set_bytes = 4 * n_samples + 512 * total
+    n_sets = max(1, min(5, int(math.ceil(1.1e9 / set_bytes)))) if args.workload != "c4" else 1
+    xs = [x] + [x.clone() for _ in range(n_sets - 1)]
+    outs = [torch.empty((total, 128), dtype=torch.float32, device=dev) for _ in range(n_sets)]
+    stream = torch.cuda.current_stream(dev)
+    for i in range(args.warmup):
+        k = i % n_sets
+        lm.logmel_compute(plan, xs[k], so_d, fo_d, total, out=outs[k], stream=stream)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        k = i % n_sets
+        starts[i].record(stream)
+        lm.logmel_compute(plan, xs[k], so_d, fo_d, total, out=outs[k], stream=stream)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    kern_avg_s = sum(kern_ms) / len(kern_ms) / 1e3
+    algo_bytes = set_bytes + 8 * 2 * (len(so))
+    ms_per_step = wall / args.steps * 1e3
+    audio_s = n_samples / FS
+    achieved = algo_bytes / kern_avg_s / 1e9
+    traffic = measured_traffic(args.workload)
+    rec = {
+        "metric": "audio-seconds/sec of 128-bin log-mel on 1 MI355X + % of HBM roofline",
+        "value": audio_s / (ms_per_step / 1e3),
+        "unit": "audio-seconds/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": desc, "clips": len(so) - 1, "samples": n_samples,
+                   "frames": total, "buffer_sets": n_sets},
+        "frames_per_s": total / (ms_per_step / 1e3),
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic, "kernel": "logmel_tiles_kernel",
+                     "kernel_avg_us": kern_avg_s * 1e6,
+                     "algorithmic_bytes_per_launch": algo_bytes},
+    }
+    clips_host = None
+    if not args.no_cpu_baseline:
+        xh = x.cpu().numpy()
+        nclip = min(len(so) - 1, 64)
+        if args.workload == "c4":
+            # the shortest clips of the ragged batch would skew nothing; take
+            # a contiguous 60 s slice of each of the first clips instead
+            clips_host = [xh[so[i]:min(so[i + 1], so[i] + 960000)] for i in range(16)]
+        else:
+            clips_host = [xh[so[i]:so[i + 1]] for i in range(nclip)]
+    return rec, clips_host
+
+
+def bench_stream(args, lm, plan, torch):
+    """One step = 375 pushes of 1280 samples to 512 streams (30 s each)."""
+    import logmel_synth as S
+    import numpy as np
+    dev = torch.device("cuda", 0)
+    n, pushes, P = 512, 375, 1280
+    streams = S.config3_streams(device=dev)
+    chunks = [streams[:, c * P:(c + 1) * P].contiguous().reshape(-1) for c in range(pushes)]
+    s = lm.logmel_stream_create(plan, n, P)
+    pl = np.full(n, P, dtype=np.int64)
+    out = torch.empty((n * 8, 128), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def one_pass():
+        lm.logmel_stream_reset(s)
+        for c in range(pushes):
+            fo = lm.logmel_stream_frames_for_push(s, pl)
+            lm.logmel_stream_push(s, chunks[c], pl, out=out[:int(fo[-1])], stream=stream)
+
+    for _ in range(args.warmup):
+        one_pass()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        one_pass()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / args.steps * 1e3
+    audio_s = n * pushes * P / FS
+    frames = n * 2998
+    rec = {
+        "metric": "audio-seconds/sec of 128-bin log-mel on 1 MI355X + % of HBM roofline",
+        "value": audio_s / (ms_per_step / 1e3),
+        "unit": "audio-seconds/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "streaming: 512 streams x 375 pushes of 1280 samples (80 ms)",
+                   "streams": n, "pushes": pushes, "push_samples": P},
+        "frames_per_s": frames / (ms_per_step / 1e3),
+        "push_latency_us": ms_per_step * 1e3 / pushes,
+    }
+    s.close()
+    return rec, None
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="c2", choices=["c2", "c1", "c4", "c3"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(frames are independent, so several GPUs would each run this same kernel "
+              "on their own share of the batch)", file=sys.stderr)
+        sys.exit(2)
+    defaults = {"c2": (200, 20), "c1": (500, 50), "c4": (5, 2), "c3": (3, 1)}
+    if args.steps is None:
+        args.steps = defaults[args.workload][0]
+    if args.warmup is None:
+        args.warmup = defaults[args.workload][1]
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    import log_mel_spectrogram_amd as lm
+    plan = lm.logmel_plan_create(0)
+    if args.workload == "c3":
+        rec, clips = bench_stream(args, lm, plan, torch)
+    else:
+        rec, clips = bench_offline(args, lm, plan, torch)
+    if clips is not None:
+        rec["cpu_baseline"] = cpu_baseline(clips, args.cpu_seconds)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,170 @@
+/* logmel.h -- C ABI of the MI355X (gfx950) 128-bin log-mel front end.
+ *
+ * What is computed (page "从零理解 ASR：音频基础、Qwen3-ASR 架构，以及离线 vs
+ * 流式推理原理", marsggbo blog, §2.3 "Log-Mel Spectrogram 提取流水线",
+ * steps 1-5, and the preprocessor-config list after them): 16 kHz mono fp32
+ * PCM is cut into 400-sample frames every 160 samples with no centring or
+ * padding, floor((N - 400) / 160) + 1 frames for N >= 400 and none below;
+ * each frame is multiplied by the symmetric Hamming window
+ * 0.54 - 0.46 cos(2 pi n / 399), transformed by a 400-point real FFT to 201
+ * bins, squared in magnitude, projected onto 128 triangular filters evenly
+ * spaced on mel = 2595 log10(1 + f/700) over 0..8000 Hz (peak 1, no
+ * normalisation; end vertices exactly 0 and 8000 Hz; triangles linear in
+ * Hz), and compressed by ln(max(E, 1e-10)). The output is frame-major
+ * [frames][128] fp32 (the page's shape table after step 5).
+ *
+ * Conventions of every call:
+ *  - Return value: LOGMEL_OK (0) or a negative LOGMEL_ERR_* code. Arguments
+ *    are checked on the host before anything is launched, so an error means
+ *    nothing was written. logmel_status_string() names a code.
+ *  - "d_" pointers are device pointers on the plan's device; "_host" pointers
+ *    are host memory. The caller owns every buffer it passes; the library
+ *    never keeps a pointer past the call. The plan owns nothing on the
+ *    device; a stream object owns its workspace.
+ *  - hip_stream is a hipStream_t (NULL = the null stream). Compute calls are
+ *    asynchronous on it: no host synchronisation, no read-back.
+ *  - Input values are not checked or clamped; [-1, 1] is the expected range
+ *    (page 1, §2.1). A NaN in a frame gives NaN in its outputs.
+ *  - Over-long input is an error (LOGMEL_ERR_INPUT_TOO_LONG), never a silent
+ *    truncation (the transcribe.cpp Qwen3-ASR page, §四, states the same
+ *    convention for its length limit).
+ */
+#ifndef LOGMEL_H_
+#define LOGMEL_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  LOGMEL_OK = 0,
+  LOGMEL_ERR_INVALID_ARGUMENT = -1, /* null pointer, negative size, bad offsets */
+  LOGMEL_ERR_UNSUPPORTED = -2,      /* a configuration other than the one below */
+  LOGMEL_ERR_OUT_OF_MEMORY = -3,    /* device or pinned host allocation failed */
+  LOGMEL_ERR_DEVICE = -4,           /* a HIP runtime call failed */
+  LOGMEL_ERR_INPUT_TOO_LONG = -5    /* sizes beyond int64 indexing or a stream's push limit */
+};
+
+/* The front-end configuration. Only the values of page 1 (§2.3 and the
+ * preprocessor-config list) are supported: sample_rate 16000, n_fft 400,
+ * hop 160, n_mels 128, f_min 0, f_max 8000, log_floor 1e-10. Any other value
+ * gives LOGMEL_ERR_UNSUPPORTED (a sample rate other than 16 kHz is rejected,
+ * as the page's processor call requires 16 kHz input). */
+typedef struct logmel_config {
+  int32_t sample_rate;
+  int32_t n_fft;
+  int32_t hop;
+  int32_t n_mels;
+  double f_min;
+  double f_max;
+  double log_floor;
+  int32_t device; /* HIP device ordinal */
+} logmel_config;
+
+/* Fills *cfg with the supported configuration on device 0. */
+void logmel_default_config(logmel_config* cfg);
+
+typedef struct logmel_plan logmel_plan;     /* immutable, shareable across threads */
+typedef struct logmel_stream logmel_stream; /* state of n streams; not thread-safe */
+
+/* Validates cfg and creates a plan for cfg->device. */
+int logmel_plan_create(const logmel_config* cfg, logmel_plan** out);
+void logmel_plan_destroy(logmel_plan* plan);
+
+/* Frames of an n_samples clip (page 1, §2.3 step 1): 0 if n_samples < 400,
+ * else floor((n_samples - 400) / 160) + 1. Negative n gives 0. */
+int64_t logmel_num_frames(int64_t n_samples);
+
+/* Host helper. Clip i holds samples [sample_offsets_host[i],
+ * sample_offsets_host[i+1]) of a packed buffer (n_clips + 1 non-decreasing
+ * int64, first 0). Writes frame_offsets_host[0..n_clips] = exclusive prefix
+ * sum of the clips' frame counts: clip i's frames are output rows
+ * [frame_offsets[i], frame_offsets[i+1]). Errors: INVALID_ARGUMENT for null
+ * pointers, n_clips < 0, a non-zero first offset or decreasing offsets. */
+int logmel_frame_offsets(const int64_t* sample_offsets_host, int64_t n_clips,
+                         int64_t* frame_offsets_host);
+
+/* Offline log-mel of a packed ragged batch (page 1, §2.3 steps 1-5).
+ *   d_samples          fp32, clip i = d_samples[d_sample_offsets[i] ..
+ *                      d_sample_offsets[i+1]), packed with no padding
+ *   d_sample_offsets   int64[n_clips + 1], as for logmel_frame_offsets
+ *   d_frame_offsets    int64[n_clips + 1], what logmel_frame_offsets returns
+ *                      for those sample offsets
+ *   total_frames       d_frame_offsets[n_clips]
+ *   d_out              fp32 [total_frames][128], row-major; row
+ *                      d_frame_offsets[i] + f is frame f of clip i
+ * The offsets are a precondition the device does not read back: a frame
+ * whose 400 samples do not lie inside its clip is written as a row of NaN
+ * rather than read out of bounds. With the environment variable
+ * LOGMEL_VALIDATE=1 the call copies the offsets to the host first (one
+ * synchronisation) and returns INVALID_ARGUMENT if they disagree.
+ * n_clips == 0 or total_frames == 0 is a valid empty call.
+ * INPUT_TOO_LONG if total_frames * 128 overflows int64. */
+int logmel_compute(const logmel_plan* plan, const float* d_samples,
+                   const int64_t* d_sample_offsets, const int64_t* d_frame_offsets,
+                   int64_t n_clips, int64_t total_frames, float* d_out,
+                   void* hip_stream);
+
+/* Streaming (the 80 ms audio clock of the Audio8-ASR-Infinite page gives the
+ * 1280-sample push). A stream object holds n_streams independent streams.
+ * Each push appends new samples to every stream and emits every frame that
+ * is now complete on the offline grid of that stream: the frames emitted
+ * over all pushes are exactly logmel_compute's frames of the concatenated
+ * stream, bit for bit. Between pushes a stream keeps only its carry: the
+ * samples from the start of its next frame on, at most 399 (240 plus the
+ * stream length minus 400, modulo 160, once 400 samples have arrived).
+ *
+ * logmel_stream_create allocates, on the plan's device, a workspace of
+ * n_streams rows of (400 + max_push) fp32 and a small pinned host staging
+ * area; pushes allocate nothing. max_push >= 1 is the most new samples one
+ * stream may receive in one push. */
+int logmel_stream_create(const logmel_plan* plan, int64_t n_streams, int64_t max_push,
+                         logmel_stream** out);
+void logmel_stream_destroy(logmel_stream* s);
+
+/* Forgets every stream's history (carry and counters). Host-side only. */
+int logmel_stream_reset(logmel_stream* s);
+
+/* Frames each stream will emit if push_len_host[j] new samples are pushed
+ * to stream j: writes out_frame_offsets_host[0..n_streams] (exclusive
+ * prefix sum). Does not change the state. */
+int logmel_stream_frames_for_push(const logmel_stream* s, const int64_t* push_len_host,
+                                  int64_t* out_frame_offsets_host);
+
+/* Pushes push_len_host[j] (0..max_push) new samples to every stream j.
+ *   d_new   fp32, the new samples packed stream by stream, stream j's at
+ *           offset sum_{i<j} push_len_host[i]
+ *   d_out   fp32 [total][128]: stream j's new frames are rows
+ *           [fo[j], fo[j+1]) with fo = logmel_stream_frames_for_push()
+ *   out_frame_offsets_host  optional (may be NULL): receives fo
+ * Two kernel launches on hip_stream; the per-push offsets go up through the
+ * stream object's pinned staging area. INPUT_TOO_LONG if a push_len exceeds
+ * max_push. The new samples are copied before the call returns its work to
+ * the queue, so d_new may be reused once hip_stream has passed this call. */
+int logmel_stream_push(logmel_stream* s, const float* d_new, const int64_t* push_len_host,
+                       float* d_out, int64_t* out_frame_offsets_host, void* hip_stream);
+
+/* Total samples pushed and frames emitted so far for stream j. */
+int logmel_stream_counters(const logmel_stream* s, int64_t j, int64_t* samples_seen,
+                           int64_t* frames_emitted);
+
+/* Snapshot / restore of all streams. State blob layout (int64 and fp32 words,
+ * size from logmel_stream_state_bytes): per stream, int64 samples_seen,
+ * int64 frames_emitted, int64 carry_len, then 400 fp32 carry samples (the
+ * first carry_len used). get_state synchronises hip_stream. */
+int64_t logmel_stream_state_bytes(const logmel_stream* s);
+int logmel_stream_get_state(logmel_stream* s, void* state_host, void* hip_stream);
+int logmel_stream_set_state(logmel_stream* s, const void* state_host, void* hip_stream);
+
+const char* logmel_status_string(int status);
+
+/* Version of this ABI, for binding checks. */
+int logmel_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOGMEL_H_ */

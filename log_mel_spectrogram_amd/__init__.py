@@ -1,0 +1,316 @@
+"""Python binding of liblogmel.so, the MI355X (gfx950) 128-bin log-mel front end.
+
+Argument marshalling only: every step of the front end runs in the HIP
+kernels behind the C ABI declared in include/logmel.h. Functions carry the C
+names. Device buffers are torch tensors on a ROCm device (torch provides the
+memory and the stream); the library is loaded from this directory and there
+is no fallback: without the built library, importing this package raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblogmel.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run `python -m log_mel_spectrogram_amd.build` "
+        "(hipcc for gfx950). There is no CPU fallback.")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+LOGMEL_OK = 0
+LOGMEL_ERR_INVALID_ARGUMENT = -1
+LOGMEL_ERR_UNSUPPORTED = -2
+LOGMEL_ERR_OUT_OF_MEMORY = -3
+LOGMEL_ERR_DEVICE = -4
+LOGMEL_ERR_INPUT_TOO_LONG = -5
+
+N_MELS = 128
+N_FFT = 400
+HOP = 160
+SAMPLE_RATE = 16000
+
+_i64 = ctypes.c_int64
+_p = ctypes.c_void_p
+_i64p = ctypes.POINTER(ctypes.c_int64)
+
+
+class logmel_config(ctypes.Structure):
+    _fields_ = [("sample_rate", ctypes.c_int32), ("n_fft", ctypes.c_int32),
+                ("hop", ctypes.c_int32), ("n_mels", ctypes.c_int32),
+                ("f_min", ctypes.c_double), ("f_max", ctypes.c_double),
+                ("log_floor", ctypes.c_double), ("device", ctypes.c_int32)]
+
+
+def _sig(name, res, *args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = list(args)
+    return f
+
+
+_default_config = _sig("logmel_default_config", None, ctypes.POINTER(logmel_config))
+_abi_version = _sig("logmel_abi_version", ctypes.c_int)
+_status_string = _sig("logmel_status_string", ctypes.c_char_p, ctypes.c_int)
+_plan_create = _sig("logmel_plan_create", ctypes.c_int, ctypes.POINTER(logmel_config),
+                    ctypes.POINTER(_p))
+_plan_destroy = _sig("logmel_plan_destroy", None, _p)
+_num_frames = _sig("logmel_num_frames", _i64, _i64)
+_frame_offsets = _sig("logmel_frame_offsets", ctypes.c_int, _i64p, _i64, _i64p)
+_compute = _sig("logmel_compute", ctypes.c_int, _p, _p, _p, _p, _i64, _i64, _p, _p)
+_stream_create = _sig("logmel_stream_create", ctypes.c_int, _p, _i64, _i64, ctypes.POINTER(_p))
+_stream_destroy = _sig("logmel_stream_destroy", None, _p)
+_stream_reset = _sig("logmel_stream_reset", ctypes.c_int, _p)
+_stream_frames_for_push = _sig("logmel_stream_frames_for_push", ctypes.c_int, _p, _i64p, _i64p)
+_stream_push = _sig("logmel_stream_push", ctypes.c_int, _p, _p, _i64p, _p, _i64p, _p)
+_stream_counters = _sig("logmel_stream_counters", ctypes.c_int, _p, _i64, _i64p, _i64p)
+_stream_state_bytes = _sig("logmel_stream_state_bytes", _i64, _p)
+_stream_get_state = _sig("logmel_stream_get_state", ctypes.c_int, _p, _p, _p)
+_stream_set_state = _sig("logmel_stream_set_state", ctypes.c_int, _p, _p, _p)
+
+EXPORTED = [
+    "logmel_default_config", "logmel_abi_version", "logmel_status_string",
+    "logmel_plan_create", "logmel_plan_destroy", "logmel_num_frames",
+    "logmel_frame_offsets", "logmel_compute", "logmel_stream_create",
+    "logmel_stream_destroy", "logmel_stream_reset", "logmel_stream_frames_for_push",
+    "logmel_stream_push", "logmel_stream_counters", "logmel_stream_state_bytes",
+    "logmel_stream_get_state", "logmel_stream_set_state",
+]
+
+
+class LogmelError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {logmel_status_string(status)} ({status})")
+
+
+def _check(status: int, what: str):
+    if status != LOGMEL_OK:
+        raise LogmelError(status, what)
+
+
+def _i64_array(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int64).reshape(-1))
+
+
+def _ptr64(a: np.ndarray):
+    return a.ctypes.data_as(_i64p)
+
+
+# ------------------------------------------------------------------ basics
+
+def logmel_abi_version() -> int:
+    return int(_abi_version())
+
+
+def logmel_status_string(status: int) -> str:
+    return _status_string(int(status)).decode()
+
+
+def logmel_default_config(device: int = 0) -> logmel_config:
+    cfg = logmel_config()
+    _default_config(ctypes.byref(cfg))
+    cfg.device = int(device)
+    return cfg
+
+
+def logmel_num_frames(n_samples: int) -> int:
+    return int(_num_frames(int(n_samples)))
+
+
+def logmel_frame_offsets(sample_offsets) -> np.ndarray:
+    so = _i64_array(sample_offsets)
+    if so.size < 1:
+        raise LogmelError(LOGMEL_ERR_INVALID_ARGUMENT, "logmel_frame_offsets")
+    fo = np.zeros(so.size, dtype=np.int64)
+    _check(_frame_offsets(_ptr64(so), so.size - 1, _ptr64(fo)), "logmel_frame_offsets")
+    return fo
+
+
+class Plan:
+    """Owns a logmel_plan handle."""
+
+    def __init__(self, cfg: logmel_config):
+        h = _p()
+        _check(_plan_create(ctypes.byref(cfg), ctypes.byref(h)), "logmel_plan_create")
+        self.handle = h
+        self.device = int(cfg.device)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            _plan_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        self.close()
+
+
+def logmel_plan_create(device: int = 0, cfg: logmel_config | None = None) -> Plan:
+    return Plan(cfg if cfg is not None else logmel_default_config(device))
+
+
+def logmel_plan_destroy(plan: Plan):
+    plan.close()
+
+
+# ----------------------------------------------------------- device glue
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dev_ptr(t, dtype, what):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{what} must be a torch tensor on a ROCm device")
+    if t.dtype != dtype:
+        raise TypeError(f"{what} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(stream, device):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def logmel_compute(plan: Plan, samples, sample_offsets, frame_offsets, total_frames: int,
+                   out=None, stream=None):
+    """Offline log-mel of a packed ragged batch; returns out [total_frames, 128].
+
+    samples fp32, sample_offsets / frame_offsets int64 [n_clips + 1], all on
+    the plan's device; the call is asynchronous on ``stream`` (default: the
+    current torch stream)."""
+    torch = _torch()
+    n_clips = int(sample_offsets.numel()) - 1
+    if out is None:
+        out = torch.empty((int(total_frames), N_MELS), dtype=torch.float32,
+                          device=samples.device)
+    if tuple(out.shape) != (int(total_frames), N_MELS):
+        raise ValueError(f"out must be [{total_frames}, {N_MELS}]")
+    if frame_offsets.numel() != n_clips + 1:
+        raise ValueError("frame_offsets must have n_clips + 1 entries")
+    st = _stream_handle(stream, samples.device)
+    _check(_compute(plan.handle, _dev_ptr(samples, torch.float32, "samples"),
+                    _dev_ptr(sample_offsets, torch.int64, "sample_offsets"),
+                    _dev_ptr(frame_offsets, torch.int64, "frame_offsets"),
+                    n_clips, int(total_frames), _dev_ptr(out, torch.float32, "out"), st),
+           "logmel_compute")
+    return out
+
+
+def log_mel(plan: Plan, samples, sample_offsets_host, stream=None):
+    """Convenience: host int64 sample offsets in, [frames, 128] out.
+
+    Computes the frame offsets with the C helper and uploads both offset
+    arrays with torch."""
+    torch = _torch()
+    so = _i64_array(sample_offsets_host)
+    fo = logmel_frame_offsets(so)
+    dev = samples.device
+    so_d = torch.from_numpy(so).to(dev)
+    fo_d = torch.from_numpy(fo).to(dev)
+    return logmel_compute(plan, samples, so_d, fo_d, int(fo[-1]), stream=stream), fo
+
+
+# --------------------------------------------------------------- streaming
+
+class Stream:
+    """Owns a logmel_stream handle (n_streams independent streams)."""
+
+    def __init__(self, plan: Plan, n_streams: int, max_push: int):
+        h = _p()
+        _check(_stream_create(plan.handle, int(n_streams), int(max_push), ctypes.byref(h)),
+               "logmel_stream_create")
+        self.handle = h
+        self.plan = plan
+        self.n_streams = int(n_streams)
+        self.max_push = int(max_push)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            _stream_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        self.close()
+
+
+def logmel_stream_create(plan: Plan, n_streams: int, max_push: int) -> Stream:
+    return Stream(plan, n_streams, max_push)
+
+
+def logmel_stream_destroy(s: Stream):
+    s.close()
+
+
+def logmel_stream_reset(s: Stream):
+    _check(_stream_reset(s.handle), "logmel_stream_reset")
+
+
+def logmel_stream_frames_for_push(s: Stream, push_len) -> np.ndarray:
+    pl = _i64_array(push_len)
+    if pl.size != s.n_streams:
+        raise ValueError("push_len must have n_streams entries")
+    fo = np.zeros(s.n_streams + 1, dtype=np.int64)
+    _check(_stream_frames_for_push(s.handle, _ptr64(pl), _ptr64(fo)),
+           "logmel_stream_frames_for_push")
+    return fo
+
+
+def logmel_stream_push(s: Stream, new_samples, push_len, out=None, stream=None):
+    """Pushes packed new samples; returns (out [frames, 128], frame offsets)."""
+    torch = _torch()
+    pl = _i64_array(push_len)
+    if pl.size != s.n_streams:
+        raise ValueError("push_len must have n_streams entries")
+    if int(pl.sum()) != int(new_samples.numel()):
+        raise ValueError("new_samples must hold sum(push_len) samples")
+    fo = logmel_stream_frames_for_push(s, pl)
+    total = int(fo[-1])
+    if out is None:
+        out = torch.empty((total, N_MELS), dtype=torch.float32, device=new_samples.device)
+    if tuple(out.shape) != (total, N_MELS):
+        raise ValueError(f"out must be [{total}, {N_MELS}]")
+    st = _stream_handle(stream, new_samples.device)
+    fo2 = np.zeros(s.n_streams + 1, dtype=np.int64)
+    _check(_stream_push(s.handle, _dev_ptr(new_samples, torch.float32, "new_samples"),
+                        _ptr64(pl), _dev_ptr(out, torch.float32, "out"), _ptr64(fo2), st),
+           "logmel_stream_push")
+    return out, fo2
+
+
+def logmel_stream_counters(s: Stream, j: int):
+    a, b = _i64(), _i64()
+    _check(_stream_counters(s.handle, int(j), ctypes.byref(a), ctypes.byref(b)),
+           "logmel_stream_counters")
+    return int(a.value), int(b.value)
+
+
+def logmel_stream_state_bytes(s: Stream) -> int:
+    return int(_stream_state_bytes(s.handle))
+
+
+def logmel_stream_get_state(s: Stream, stream=None) -> bytes:
+    buf = ctypes.create_string_buffer(logmel_stream_state_bytes(s))
+    st = _stream_handle(stream, None)
+    _check(_stream_get_state(s.handle, ctypes.cast(buf, _p), st), "logmel_stream_get_state")
+    return buf.raw
+
+
+def logmel_stream_set_state(s: Stream, state: bytes, stream=None):
+    if len(state) != logmel_stream_state_bytes(s):
+        raise ValueError("state blob has the wrong size")
+    buf = ctypes.create_string_buffer(state, len(state))
+    st = _stream_handle(stream, None)
+    _check(_stream_set_state(s.handle, ctypes.cast(buf, _p), st), "logmel_stream_set_state")

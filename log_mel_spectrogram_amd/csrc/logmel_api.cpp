@@ -1,0 +1,356 @@
+// C-ABI layer of the log-mel library: argument checks, integer frame
+// arithmetic, the stream objects' host shadow state, and kernel launches.
+// The declarations and their contracts are in include/logmel.h.
+#include "logmel.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "logmel_launch.h"
+
+namespace {
+
+constexpr int kNFFT = 400;
+constexpr int kHop = 160;
+constexpr int kMels = 128;
+constexpr int kRing = 400;  // carry capacity in front of each workspace row
+
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = true;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) { ok = false; return; }
+    if (prev != dev && hipSetDevice(dev) != hipSuccess) ok = false;
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+bool env_validate() {
+  const char* v = std::getenv("LOGMEL_VALIDATE");
+  return v && v[0] && v[0] != '0';
+}
+
+int64_t frames_of(int64_t n) { return n < kNFFT ? 0 : (n - kNFFT) / kHop + 1; }
+
+}  // namespace
+
+struct logmel_plan {
+  logmel_config cfg;
+};
+
+struct logmel_stream {
+  const logmel_plan* plan;
+  int64_t n;
+  int64_t max_push;
+  int64_t stride;              // floats per workspace row
+  float* ws = nullptr;         // device [n][stride]
+  int64_t* meta_dev = nullptr; // device [7n + 1]
+  // pinned staging ring for the per-push metadata
+  static constexpr int kSlots = 4;
+  int64_t* meta_host[kSlots] = {nullptr, nullptr, nullptr, nullptr};
+  hipEvent_t slot_done[kSlots] = {nullptr, nullptr, nullptr, nullptr};
+  int slot = 0;
+  // host shadow, per stream
+  std::vector<int64_t> seen, emitted, carry_len, carry_src;
+};
+
+extern "C" {
+
+void logmel_default_config(logmel_config* cfg) {
+  if (!cfg) return;
+  cfg->sample_rate = 16000;
+  cfg->n_fft = kNFFT;
+  cfg->hop = kHop;
+  cfg->n_mels = kMels;
+  cfg->f_min = 0.0;
+  cfg->f_max = 8000.0;
+  cfg->log_floor = 1e-10;
+  cfg->device = 0;
+}
+
+int logmel_abi_version(void) { return 1; }
+
+const char* logmel_status_string(int status) {
+  switch (status) {
+    case LOGMEL_OK: return "ok";
+    case LOGMEL_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case LOGMEL_ERR_UNSUPPORTED: return "unsupported configuration";
+    case LOGMEL_ERR_OUT_OF_MEMORY: return "out of memory";
+    case LOGMEL_ERR_DEVICE: return "HIP runtime error";
+    case LOGMEL_ERR_INPUT_TOO_LONG: return "input too long";
+    default: return "unknown status";
+  }
+}
+
+int logmel_plan_create(const logmel_config* cfg, logmel_plan** out) {
+  if (!cfg || !out) return LOGMEL_ERR_INVALID_ARGUMENT;
+  *out = nullptr;
+  if (cfg->sample_rate != 16000 || cfg->n_fft != kNFFT || cfg->hop != kHop ||
+      cfg->n_mels != kMels || cfg->f_min != 0.0 || cfg->f_max != 8000.0 ||
+      cfg->log_floor != 1e-10)
+    return LOGMEL_ERR_UNSUPPORTED;
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess) return LOGMEL_ERR_DEVICE;
+  if (cfg->device < 0 || cfg->device >= ndev) return LOGMEL_ERR_INVALID_ARGUMENT;
+  logmel_plan* p = new (std::nothrow) logmel_plan;
+  if (!p) return LOGMEL_ERR_OUT_OF_MEMORY;
+  p->cfg = *cfg;
+  *out = p;
+  return LOGMEL_OK;
+}
+
+void logmel_plan_destroy(logmel_plan* plan) { delete plan; }
+
+int64_t logmel_num_frames(int64_t n_samples) { return frames_of(n_samples); }
+
+int logmel_frame_offsets(const int64_t* so, int64_t n_clips, int64_t* fo) {
+  if (!so || !fo || n_clips < 0) return LOGMEL_ERR_INVALID_ARGUMENT;
+  if (so[0] != 0) return LOGMEL_ERR_INVALID_ARGUMENT;
+  for (int64_t i = 0; i < n_clips; ++i)
+    if (so[i + 1] < so[i]) return LOGMEL_ERR_INVALID_ARGUMENT;
+  int64_t acc = 0;
+  fo[0] = 0;
+  for (int64_t i = 0; i < n_clips; ++i) {
+    acc += frames_of(so[i + 1] - so[i]);
+    fo[i + 1] = acc;
+  }
+  return LOGMEL_OK;
+}
+
+int logmel_compute(const logmel_plan* plan, const float* d_samples,
+                   const int64_t* d_sample_offsets, const int64_t* d_frame_offsets,
+                   int64_t n_clips, int64_t total_frames, float* d_out, void* hip_stream) {
+  if (!plan || n_clips < 0 || total_frames < 0) return LOGMEL_ERR_INVALID_ARGUMENT;
+  if (total_frames > INT64_MAX / kMels) return LOGMEL_ERR_INPUT_TOO_LONG;
+  if (n_clips == 0 || total_frames == 0) return LOGMEL_OK;
+  if (!d_samples || !d_sample_offsets || !d_frame_offsets || !d_out)
+    return LOGMEL_ERR_INVALID_ARGUMENT;
+  DeviceGuard g(plan->cfg.device);
+  if (!g.ok) return LOGMEL_ERR_DEVICE;
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  if (env_validate()) {
+    std::vector<int64_t> so(n_clips + 1), fo(n_clips + 1), ref(n_clips + 1);
+    if (hipMemcpyAsync(so.data(), d_sample_offsets, (n_clips + 1) * 8, hipMemcpyDeviceToHost, st) !=
+            hipSuccess ||
+        hipMemcpyAsync(fo.data(), d_frame_offsets, (n_clips + 1) * 8, hipMemcpyDeviceToHost, st) !=
+            hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess)
+      return LOGMEL_ERR_DEVICE;
+    if (logmel_frame_offsets(so.data(), n_clips, ref.data()) != LOGMEL_OK)
+      return LOGMEL_ERR_INVALID_ARGUMENT;
+    if (ref != fo || fo[n_clips] != total_frames) return LOGMEL_ERR_INVALID_ARGUMENT;
+  }
+  const hipError_t e = logmel_launch_tiles(d_samples, d_sample_offsets, d_sample_offsets + 1,
+                                           d_frame_offsets, n_clips, total_frames, d_out, st);
+  return e == hipSuccess ? LOGMEL_OK : LOGMEL_ERR_DEVICE;
+}
+
+// ---------------------------------------------------------------- streaming
+
+int logmel_stream_create(const logmel_plan* plan, int64_t n_streams, int64_t max_push,
+                         logmel_stream** out) {
+  if (!plan || !out || n_streams < 1 || max_push < 1) return LOGMEL_ERR_INVALID_ARGUMENT;
+  *out = nullptr;
+  if (n_streams > (1LL << 31) - 1) return LOGMEL_ERR_INPUT_TOO_LONG;
+  int64_t stride = kRing + max_push;
+  stride = (stride + 63) / 64 * 64;  // 256-byte aligned rows
+  if (stride > INT64_MAX / n_streams / 4) return LOGMEL_ERR_INPUT_TOO_LONG;
+  DeviceGuard g(plan->cfg.device);
+  if (!g.ok) return LOGMEL_ERR_DEVICE;
+  logmel_stream* s = new (std::nothrow) logmel_stream;
+  if (!s) return LOGMEL_ERR_OUT_OF_MEMORY;
+  s->plan = plan;
+  s->n = n_streams;
+  s->max_push = max_push;
+  s->stride = stride;
+  const size_t meta_words = 7 * (size_t)n_streams + 1;
+  bool ok = hipMalloc(&s->ws, (size_t)n_streams * stride * sizeof(float)) == hipSuccess &&
+            hipMalloc(&s->meta_dev, meta_words * 8) == hipSuccess;
+  for (int i = 0; ok && i < logmel_stream::kSlots; ++i)
+    ok = hipHostMalloc(&s->meta_host[i], meta_words * 8, hipHostMallocDefault) == hipSuccess &&
+         hipEventCreateWithFlags(&s->slot_done[i], hipEventDisableTiming) == hipSuccess;
+  if (!ok) {
+    logmel_stream_destroy(s);
+    return LOGMEL_ERR_OUT_OF_MEMORY;
+  }
+  s->seen.assign(n_streams, 0);
+  s->emitted.assign(n_streams, 0);
+  s->carry_len.assign(n_streams, 0);
+  s->carry_src.assign(n_streams, 0);
+  for (int64_t j = 0; j < n_streams; ++j) s->carry_src[j] = j * stride + kRing;
+  *out = s;
+  return LOGMEL_OK;
+}
+
+void logmel_stream_destroy(logmel_stream* s) {
+  if (!s) return;
+  DeviceGuard g(s->plan->cfg.device);
+  for (int i = 0; i < logmel_stream::kSlots; ++i) {
+    if (s->slot_done[i]) {
+      (void)hipEventSynchronize(s->slot_done[i]);
+      (void)hipEventDestroy(s->slot_done[i]);
+    }
+    if (s->meta_host[i]) (void)hipHostFree(s->meta_host[i]);
+  }
+  if (s->ws) (void)hipFree(s->ws);
+  if (s->meta_dev) (void)hipFree(s->meta_dev);
+  delete s;
+}
+
+int logmel_stream_reset(logmel_stream* s) {
+  if (!s) return LOGMEL_ERR_INVALID_ARGUMENT;
+  for (int64_t j = 0; j < s->n; ++j) {
+    s->seen[j] = 0;
+    s->emitted[j] = 0;
+    s->carry_len[j] = 0;
+    s->carry_src[j] = j * s->stride + kRing;
+  }
+  return LOGMEL_OK;
+}
+
+int logmel_stream_frames_for_push(const logmel_stream* s, const int64_t* push_len,
+                                  int64_t* fo) {
+  if (!s || !push_len || !fo) return LOGMEL_ERR_INVALID_ARGUMENT;
+  fo[0] = 0;
+  for (int64_t j = 0; j < s->n; ++j) {
+    if (push_len[j] < 0) return LOGMEL_ERR_INVALID_ARGUMENT;
+    fo[j + 1] = fo[j] + frames_of(s->carry_len[j] + push_len[j]);
+  }
+  return LOGMEL_OK;
+}
+
+int logmel_stream_push(logmel_stream* s, const float* d_new, const int64_t* push_len,
+                       float* d_out, int64_t* fo_out, void* hip_stream) {
+  if (!s || !push_len) return LOGMEL_ERR_INVALID_ARGUMENT;
+  const int64_t n = s->n;
+  int64_t total_new = 0;
+  for (int64_t j = 0; j < n; ++j) {
+    if (push_len[j] < 0) return LOGMEL_ERR_INVALID_ARGUMENT;
+    if (push_len[j] > s->max_push) return LOGMEL_ERR_INPUT_TOO_LONG;
+    total_new += push_len[j];
+  }
+  if (total_new > 0 && !d_new) return LOGMEL_ERR_INVALID_ARGUMENT;
+  DeviceGuard g(s->plan->cfg.device);
+  if (!g.ok) return LOGMEL_ERR_DEVICE;
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+
+  // Fill the next staging slot once the push that last used it has gone up.
+  const int slot = s->slot;
+  if (hipEventSynchronize(s->slot_done[slot]) != hipSuccess) return LOGMEL_ERR_DEVICE;
+  int64_t* m = s->meta_host[slot];
+  int64_t off = 0;
+  int64_t* fo = m + 6 * n;
+  fo[0] = 0;
+  for (int64_t j = 0; j < n; ++j) {
+    const int64_t c = s->carry_len[j];
+    const int64_t p = push_len[j];
+    const int64_t base = j * s->stride;
+    m[j] = s->carry_src[j];
+    m[n + j] = c;
+    m[2 * n + j] = off;
+    m[3 * n + j] = p;
+    m[4 * n + j] = base + kRing - c;
+    m[5 * n + j] = base + kRing + p;
+    fo[j + 1] = fo[j] + frames_of(c + p);
+    off += p;
+  }
+  const int64_t total_frames = fo[n];
+  if (total_frames > INT64_MAX / kMels) return LOGMEL_ERR_INPUT_TOO_LONG;
+  if (total_frames > 0 && !d_out) return LOGMEL_ERR_INVALID_ARGUMENT;
+  const size_t meta_bytes = (7 * (size_t)n + 1) * 8;
+  if (hipMemcpyAsync(s->meta_dev, m, meta_bytes, hipMemcpyHostToDevice, st) != hipSuccess ||
+      hipEventRecord(s->slot_done[slot], st) != hipSuccess)
+    return LOGMEL_ERR_DEVICE;
+  s->slot = (slot + 1) % logmel_stream::kSlots;
+  if (logmel_launch_stream_prep(s->ws, s->stride, d_new, s->meta_dev, n, st) != hipSuccess)
+    return LOGMEL_ERR_DEVICE;
+  if (logmel_launch_tiles(s->ws, s->meta_dev + 4 * n, s->meta_dev + 5 * n, s->meta_dev + 6 * n,
+                          n, total_frames, d_out, st) != hipSuccess)
+    return LOGMEL_ERR_DEVICE;
+  // Advance the host shadow.
+  for (int64_t j = 0; j < n; ++j) {
+    const int64_t c = s->carry_len[j], p = push_len[j];
+    const int64_t F = frames_of(c + p);
+    const int64_t seg0 = j * s->stride + kRing - c;
+    s->carry_src[j] = seg0 + kHop * F;
+    s->carry_len[j] = c + p - kHop * F;
+    s->seen[j] += p;
+    s->emitted[j] += F;
+  }
+  if (fo_out) std::memcpy(fo_out, fo, (n + 1) * sizeof(int64_t));
+  return LOGMEL_OK;
+}
+
+int logmel_stream_counters(const logmel_stream* s, int64_t j, int64_t* seen, int64_t* emitted) {
+  if (!s || j < 0 || j >= s->n) return LOGMEL_ERR_INVALID_ARGUMENT;
+  if (seen) *seen = s->seen[j];
+  if (emitted) *emitted = s->emitted[j];
+  return LOGMEL_OK;
+}
+
+static constexpr int64_t kStateWords = 3 * 2 + kRing;  // 3 int64 + 400 fp32, in 4-byte words
+
+int64_t logmel_stream_state_bytes(const logmel_stream* s) {
+  return s ? s->n * kStateWords * 4 : 0;
+}
+
+int logmel_stream_get_state(logmel_stream* s, void* state_host, void* hip_stream) {
+  if (!s || !state_host) return LOGMEL_ERR_INVALID_ARGUMENT;
+  DeviceGuard g(s->plan->cfg.device);
+  if (!g.ok) return LOGMEL_ERR_DEVICE;
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  char* b = static_cast<char*>(state_host);
+  for (int64_t j = 0; j < s->n; ++j) {
+    char* r = b + j * kStateWords * 4;
+    int64_t hdr[3] = {s->seen[j], s->emitted[j], s->carry_len[j]};
+    std::memcpy(r, hdr, sizeof(hdr));
+    std::memset(r + 24, 0, kRing * 4);
+    if (s->carry_len[j] > 0 &&
+        hipMemcpyAsync(r + 24, s->ws + s->carry_src[j], s->carry_len[j] * 4,
+                       hipMemcpyDeviceToHost, st) != hipSuccess)
+      return LOGMEL_ERR_DEVICE;
+  }
+  return hipStreamSynchronize(st) == hipSuccess ? LOGMEL_OK : LOGMEL_ERR_DEVICE;
+}
+
+int logmel_stream_set_state(logmel_stream* s, const void* state_host, void* hip_stream) {
+  if (!s || !state_host) return LOGMEL_ERR_INVALID_ARGUMENT;
+  const char* b = static_cast<const char*>(state_host);
+  for (int64_t j = 0; j < s->n; ++j) {
+    int64_t hdr[3];
+    std::memcpy(hdr, b + j * kStateWords * 4, sizeof(hdr));
+    const int64_t seen = hdr[0], emitted = hdr[1], c = hdr[2];
+    // The state must be one a stream can reach: carry and counters agree.
+    const int64_t expect_c = seen < kNFFT ? seen : seen - kHop * frames_of(seen);
+    if (seen < 0 || emitted != frames_of(seen) || c != expect_c || c < 0 || c >= kRing)
+      return LOGMEL_ERR_INVALID_ARGUMENT;
+  }
+  DeviceGuard g(s->plan->cfg.device);
+  if (!g.ok) return LOGMEL_ERR_DEVICE;
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  for (int64_t j = 0; j < s->n; ++j) {
+    const char* r = b + j * kStateWords * 4;
+    int64_t hdr[3];
+    std::memcpy(hdr, r, sizeof(hdr));
+    const int64_t c = hdr[2];
+    const int64_t dst = j * s->stride + kRing - c;
+    if (c > 0 && hipMemcpyAsync(s->ws + dst, r + 24, c * 4, hipMemcpyHostToDevice, st) !=
+                     hipSuccess)
+      return LOGMEL_ERR_DEVICE;
+    s->seen[j] = hdr[0];
+    s->emitted[j] = hdr[1];
+    s->carry_len[j] = c;
+    s->carry_src[j] = dst;
+  }
+  // The host buffer is the caller's: finish the copies before returning.
+  return hipStreamSynchronize(st) == hipSuccess ? LOGMEL_OK : LOGMEL_ERR_DEVICE;
+}
+
+}  // extern "C"

@@ -1,0 +1,170 @@
+"""Streaming push: frames emitted over all pushes equal the offline frames of
+the concatenated stream, bit for bit; snapshot and restore; counters."""
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle as O
+import logmel_synth as S
+from tests.parity import assert_parity
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from tests.libload import load_binding
+    lm = load_binding()
+    plan = lm.logmel_plan_create(0)
+    return lm, plan, torch
+
+
+def offline(env, streams):
+    """Offline frames of each row of streams [n, N] (torch, cuda)."""
+    lm, plan, torch = env
+    n, N = streams.shape
+    so = np.arange(n + 1, dtype=np.int64) * N
+    out, fo = lm.log_mel(plan, streams.reshape(-1).contiguous(), so)
+    return out, fo
+
+
+def run_pushes(env, s, streams, schedule, collect):
+    """schedule: list of push-length arrays; collect[j] gets stream j's rows."""
+    lm, plan, torch = env
+    n = streams.shape[0]
+    pos = np.zeros(n, dtype=np.int64)
+    for pl in schedule:
+        pl = np.asarray(pl, dtype=np.int64)
+        chunks = [streams[j, pos[j]:pos[j] + pl[j]] for j in range(n)]
+        new = torch.cat(chunks).contiguous()
+        out, fo = lm.logmel_stream_push(s, new, pl)
+        for j in range(n):
+            if fo[j + 1] > fo[j]:
+                collect[j].append(out[fo[j]:fo[j + 1]])
+        pos += pl
+    return pos
+
+
+def test_config3_stream_equals_offline(env):
+    """512 streams, 375 pushes of 1280 samples (80 ms): 6 frames on the
+    first push, then 8; 2998 per stream; bitwise equal to offline."""
+    lm, plan, torch = env
+    say("config3 generate")
+    streams = S.config3_streams(device="cuda")
+    n = streams.shape[0]
+    s = lm.logmel_stream_create(plan, n, 1280)
+    first = lm.logmel_stream_frames_for_push(s, np.full(n, 1280))
+    assert np.all(np.diff(first) == 6)
+    say("config3 pushes")
+    collect = [[] for _ in range(n)]
+    new_all = streams.reshape(n, 375, 1280)
+    fo_seen = []
+    for c in range(375):
+        new = new_all[:, c, :].contiguous().reshape(-1)
+        out, fo = lm.logmel_stream_push(s, new, np.full(n, 1280))
+        fo_seen.append(int(fo[1] - fo[0]))
+        for j in range(n):
+            collect[j].append(out[fo[j]:fo[j + 1]])
+    assert fo_seen[0] == 6 and all(v == 8 for v in fo_seen[1:])
+    streamed = torch.stack([torch.cat(collect[j]) for j in range(n)])
+    torch.cuda.synchronize()
+    assert streamed.shape == (n, 2998, 128)
+    say("config3 offline")
+    ref, fo = offline(env, streams)
+    assert torch.equal(streamed.reshape(-1, 128), ref), "stream != offline"
+    for j in (0, 511):
+        assert lm.logmel_stream_counters(s, j) == (480000, 2998)
+    # and the offline frames against the oracle on two streams
+    x = streams[[0, 511]].cpu().numpy()
+    for k, j in enumerate((0, 511)):
+        L, E = O.logmel_clip(x[k])
+        assert_parity(streamed[j].cpu().numpy(), L, E, f"config3 stream {j}")
+    s.close()
+
+
+def test_random_push_lengths(env):
+    lm, plan, torch = env
+    say("random push lengths")
+    rng = np.random.default_rng(31)
+    n, N = 13, 20000
+    streams = torch.from_numpy(rng.uniform(-1, 1, (n, N)).astype(np.float32)).cuda()
+    s = lm.logmel_stream_create(plan, n, 3000)
+    collect = [[] for _ in range(n)]
+    pos = np.zeros(n, dtype=np.int64)
+    while np.any(pos < N):
+        pl = np.minimum(rng.choice([0, 1, 7, 159, 160, 161, 399, 400, 1280, 3000], n), N - pos)
+        chunks = [streams[j, pos[j]:pos[j] + pl[j]] for j in range(n)]
+        out, fo = lm.logmel_stream_push(s, torch.cat(chunks).contiguous(), pl)
+        for j in range(n):
+            if fo[j + 1] > fo[j]:
+                collect[j].append(out[fo[j]:fo[j + 1]])
+        pos += pl
+    ref, fo = offline(env, streams)
+    got = torch.cat([torch.cat(c) for c in collect])
+    assert torch.equal(got, ref)
+    s.close()
+
+
+def test_push_too_long_is_an_error(env):
+    lm, plan, torch = env
+    say("push too long")
+    s = lm.logmel_stream_create(plan, 2, 100)
+    new = torch.zeros(202, dtype=torch.float32, device="cuda")
+    with pytest.raises(lm.LogmelError) as e:
+        lm.logmel_stream_push(s, new, [101, 101])
+    assert e.value.status == lm.LOGMEL_ERR_INPUT_TOO_LONG
+    assert lm.logmel_stream_counters(s, 0) == (0, 0)
+    s.close()
+
+
+def test_snapshot_restore(env):
+    """Snapshot after some pushes, destroy, restore into a new object and
+    continue: identical to an uninterrupted run."""
+    lm, plan, torch = env
+    say("snapshot restore")
+    rng = np.random.default_rng(32)
+    n, N, P = 5, 16000, 1000
+    streams = torch.from_numpy(rng.uniform(-1, 1, (n, N)).astype(np.float32)).cuda()
+    sched = [np.full(n, P)] * (N // P)
+    a = lm.logmel_stream_create(plan, n, P)
+    ca = [[] for _ in range(n)]
+    run_pushes(env, a, streams, sched, ca)
+    b = lm.logmel_stream_create(plan, n, P)
+    cb = [[] for _ in range(n)]
+    half = len(sched) // 2 + 1
+    run_pushes(env, b, streams[:, :half * P], sched[:half], cb)
+    state = lm.logmel_stream_get_state(b)
+    b.close()
+    c = lm.logmel_stream_create(plan, n, P)
+    lm.logmel_stream_set_state(c, state)
+    assert lm.logmel_stream_counters(c, 0) == (half * P, O.num_frames(half * P))
+    rest = streams[:, half * P:].contiguous()
+    run_pushes(env, c, rest, sched[half:], cb)
+    for j in range(n):
+        assert torch.equal(torch.cat(ca[j]), torch.cat(cb[j]))
+    a.close()
+    c.close()
+
+
+def test_reset(env):
+    lm, plan, torch = env
+    say("reset")
+    n = 3
+    rng = np.random.default_rng(33)
+    x = torch.from_numpy(rng.uniform(-1, 1, (n, 4000)).astype(np.float32)).cuda()
+    s = lm.logmel_stream_create(plan, n, 4000)
+    o1, _ = lm.logmel_stream_push(s, x.reshape(-1).contiguous(), [4000] * n)
+    lm.logmel_stream_reset(s)
+    o2, _ = lm.logmel_stream_push(s, x.reshape(-1).contiguous(), [4000] * n)
+    assert torch.equal(o1, o2)
+    s.close()
