@@ -41,8 +41,17 @@ int64_t frames_of(int64_t n) { return n < kNFFT ? 0 : (n - kNFFT) / kHop + 1; }
 
 }  // namespace
 
+// fp64 tables, computed by gen_tables.py from the definitions.
+static const double kHostWindow[400] = {
+#include "logmel_window.inc"
+};
+static const double kHostRot800[202] = {
+#include "logmel_rot800.inc"
+};
+
 struct logmel_plan {
   logmel_config cfg;
+  double* tables = nullptr;  // device, kTabDoubles
 };
 
 struct logmel_stream {
@@ -102,11 +111,35 @@ int logmel_plan_create(const logmel_config* cfg, logmel_plan** out) {
   logmel_plan* p = new (std::nothrow) logmel_plan;
   if (!p) return LOGMEL_ERR_OUT_OF_MEMORY;
   p->cfg = *cfg;
+  DeviceGuard g(cfg->device);
+  if (!g.ok) {
+    delete p;
+    return LOGMEL_ERR_DEVICE;
+  }
+  double host[kTabDoubles];
+  std::memcpy(host + kTabWindow, kHostWindow, sizeof(kHostWindow));
+  std::memcpy(host + kTabRot800, kHostRot800, sizeof(kHostRot800));
+  if (hipMalloc(&p->tables, sizeof(host)) != hipSuccess) {
+    delete p;
+    return LOGMEL_ERR_OUT_OF_MEMORY;
+  }
+  if (hipMemcpy(p->tables, host, sizeof(host), hipMemcpyHostToDevice) != hipSuccess) {
+    (void)hipFree(p->tables);
+    delete p;
+    return LOGMEL_ERR_DEVICE;
+  }
   *out = p;
   return LOGMEL_OK;
 }
 
-void logmel_plan_destroy(logmel_plan* plan) { delete plan; }
+void logmel_plan_destroy(logmel_plan* plan) {
+  if (!plan) return;
+  if (plan->tables) {
+    DeviceGuard g(plan->cfg.device);
+    (void)hipFree(plan->tables);
+  }
+  delete plan;
+}
 
 int64_t logmel_num_frames(int64_t n_samples) { return frames_of(n_samples); }
 
@@ -147,7 +180,8 @@ int logmel_compute(const logmel_plan* plan, const float* d_samples,
       return LOGMEL_ERR_INVALID_ARGUMENT;
     if (ref != fo || fo[n_clips] != total_frames) return LOGMEL_ERR_INVALID_ARGUMENT;
   }
-  const hipError_t e = logmel_launch_tiles(d_samples, d_sample_offsets, d_sample_offsets + 1,
+  const hipError_t e = logmel_launch_tiles(plan->tables, d_samples, d_sample_offsets,
+                                           d_sample_offsets + 1,
                                            d_frame_offsets, n_clips, total_frames, d_out, st);
   return e == hipSuccess ? LOGMEL_OK : LOGMEL_ERR_DEVICE;
 }
@@ -271,8 +305,8 @@ int logmel_stream_push(logmel_stream* s, const float* d_new, const int64_t* push
   s->slot = (slot + 1) % logmel_stream::kSlots;
   if (logmel_launch_stream_prep(s->ws, s->stride, d_new, s->meta_dev, n, st) != hipSuccess)
     return LOGMEL_ERR_DEVICE;
-  if (logmel_launch_tiles(s->ws, s->meta_dev + 4 * n, s->meta_dev + 5 * n, s->meta_dev + 6 * n,
-                          n, total_frames, d_out, st) != hipSuccess)
+  if (logmel_launch_tiles(s->plan->tables, s->ws, s->meta_dev + 4 * n, s->meta_dev + 5 * n,
+                          s->meta_dev + 6 * n, n, total_frames, d_out, st) != hipSuccess)
     return LOGMEL_ERR_DEVICE;
   // Advance the host shadow.
   for (int64_t j = 0; j < n; ++j) {

@@ -1,20 +1,34 @@
-// Per-frame log-mel routine for gfx950: one 400-sample frame per lane.
+// Per-frame log-mel routine for gfx950: one 400-sample frame per lane pair.
 //
 // The steps follow the five-step recipe of the page "从零理解 ASR：音频基础、
 // Qwen3-ASR 架构，以及离线 vs 流式推理原理" (§2.3): symmetric Hamming window,
 // 400-point real FFT to 201 bins, power |X|^2, 128 triangular mel filters
 // (mel = 2595 log10(1 + f/700), 0..8000 Hz), ln(max(E, 1e-10)).
 //
-// Layout of the work: every lane owns one whole frame and keeps it in
-// registers. The 400-point transform is a prime-factor (Good-Thomas) 16 x 25
-// decomposition, so there are no twiddles between the two stages:
-//   n = (25 n1 + 16 n2) mod 400,  k = (225 k1 + 176 k2) mod 400,
-//   X[k] = sum_n1 W16^(n1 k1) sum_n2 W25^(n2 k2) y[n].
-// Stage 1 runs 16 real 25-point DFTs (two at a time as one complex DFT,
-// 5 x 5 Cooley-Tukey), stage 2 runs 13 16-point DFTs (4 x 4 Cooley-Tukey)
-// for k2 = 0..12, which by Hermitian symmetry covers every bin 0..200 once.
-// All twiddles, window values and filter weights are compile-time literals,
-// the same for every lane, so no lane-varying constant is ever loaded.
+// Precision. The result must hold to 1e-3 in the log wherever a band's
+// energy is at least 1e-7, also in loud frames whose quietest bands sit
+// 90 dB or more below their loudest. An fp32 transform leaves a rounding
+// floor about 1e-7 of the frame's amplitude in every bin, which is above
+// such bands, so the window and the whole transform run in fp64 (full rate
+// on CDNA). Power, filterbank and log run in fp32: a bin's power is formed
+// in fp64 and rounded once.
+//
+// Work split. fp64 doubles the registers a frame needs, so a frame takes two
+// adjacent lanes (a "pair"): role 0 transforms the even samples, role 1 the
+// odd ones (decimation in time). Each role runs the same code:
+//   * a 200-point real DFT as a prime-factor (Good-Thomas) 8 x 25 transform,
+//       m = (25 n1 + 8 n2) mod 200,  k = (25 k1 + 176 k2) mod 200,
+//     with 8 real 25-point DFTs (two at a time as one complex 5 x 5 DFT)
+//     and 13 8-point DFTs for k2 = 0..12, which cover k = 0..100;
+//   * the radix-2 combine X[k] = E[k] + W400^k O[k] in the symmetric form
+//       |X[k]|       = |W800^-k E[k] + W800^k O[k]|,
+//       |X[200 - k]| = |W800^-k E[k] - W800^k O[k]|,
+//     each role rotating its own spectrum by W800^(-/+k), swapping it with
+//     its partner (DPP), and forming both powers. Both lanes then hold the
+//     same 201 powers and run the same filterbank; each logs and stores one
+//     half of the 128 bands.
+// Window values differ between the roles (w[2m] against w[2m+1]) and come
+// from LDS; every other constant is the same for all lanes.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -23,26 +37,34 @@
 
 namespace logmel {
 
-struct cf {
-  float re, im;
+struct cd {
+  double re, im;
 };
 
-__device__ __forceinline__ cf c_add(cf a, cf b) { return {a.re + b.re, a.im + b.im}; }
-__device__ __forceinline__ cf c_sub(cf a, cf b) { return {a.re - b.re, a.im - b.im}; }
-// a * conj-free twiddle exp(-2 pi i j / n) = (c, -s)
-__device__ __forceinline__ cf c_twiddle(cf a, float c, float s) {
+__device__ __forceinline__ cd c_add(cd a, cd b) { return {a.re + b.re, a.im + b.im}; }
+__device__ __forceinline__ cd c_sub(cd a, cd b) { return {a.re - b.re, a.im - b.im}; }
+// a * exp(-2 pi i j / n) = a * (c - i s)
+__device__ __forceinline__ cd c_twiddle(cd a, double c, double s) {
   return {a.re * c + a.im * s, a.im * c - a.re * s};
 }
 
-// Forward 5-point DFT, Winograd-style grouping of conjugate pairs.
-__device__ __forceinline__ void dft5(cf& x0, cf& x1, cf& x2, cf& x3, cf& x4) {
-  const cf t1 = c_add(x1, x4), t2 = c_add(x2, x3);
-  const cf t3 = c_sub(x1, x4), t4 = c_sub(x2, x3);
-  const cf y0 = {x0.re + t1.re + t2.re, x0.im + t1.im + t2.im};
-  const cf a1 = {x0.re + kC51 * t1.re + kC52 * t2.re, x0.im + kC51 * t1.im + kC52 * t2.im};
-  const cf a2 = {x0.re + kC52 * t1.re + kC51 * t2.re, x0.im + kC52 * t1.im + kC51 * t2.im};
-  const cf b1 = {kS51 * t3.re + kS52 * t4.re, kS51 * t3.im + kS52 * t4.im};
-  const cf b2 = {kS52 * t3.re - kS51 * t4.re, kS52 * t3.im - kS51 * t4.im};
+// Compiler ordering fence: an empty volatile asm that "rewrites" v in VGPRs.
+// Volatile asm statements keep their program order, so fencing a phase's
+// inputs after the previous phase's outputs keeps independent phases from
+// being interleaved, which would raise register pressure. No instruction.
+__device__ __forceinline__ void fence(float& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void fence(double& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void fence(cd& v) { fence(v.re); fence(v.im); }
+
+// Forward 5-point DFT, conjugate pairs grouped.
+__device__ __forceinline__ void dft5(cd& x0, cd& x1, cd& x2, cd& x3, cd& x4) {
+  const cd t1 = c_add(x1, x4), t2 = c_add(x2, x3);
+  const cd t3 = c_sub(x1, x4), t4 = c_sub(x2, x3);
+  const cd y0 = {x0.re + t1.re + t2.re, x0.im + t1.im + t2.im};
+  const cd a1 = {x0.re + kDC51 * t1.re + kDC52 * t2.re, x0.im + kDC51 * t1.im + kDC52 * t2.im};
+  const cd a2 = {x0.re + kDC52 * t1.re + kDC51 * t2.re, x0.im + kDC52 * t1.im + kDC51 * t2.im};
+  const cd b1 = {kDS51 * t3.re + kDS52 * t4.re, kDS51 * t3.im + kDS52 * t4.im};
+  const cd b2 = {kDS52 * t3.re - kDS51 * t4.re, kDS52 * t3.im - kDS51 * t4.im};
   x0 = y0;
   x1 = {a1.re + b1.im, a1.im - b1.re};  // a1 - i b1
   x4 = {a1.re - b1.im, a1.im + b1.re};  // a1 + i b1
@@ -51,22 +73,37 @@ __device__ __forceinline__ void dft5(cf& x0, cf& x1, cf& x2, cf& x3, cf& x4) {
 }
 
 // Forward 4-point DFT.
-__device__ __forceinline__ void dft4(cf& x0, cf& x1, cf& x2, cf& x3) {
-  const cf s02 = c_add(x0, x2), d02 = c_sub(x0, x2);
-  const cf s13 = c_add(x1, x3), d13 = c_sub(x1, x3);
+__device__ __forceinline__ void dft4(cd& x0, cd& x1, cd& x2, cd& x3) {
+  const cd s02 = c_add(x0, x2), d02 = c_sub(x0, x2);
+  const cd s13 = c_add(x1, x3), d13 = c_sub(x1, x3);
   x0 = c_add(s02, s13);
   x2 = c_sub(s02, s13);
   x1 = {d02.re + d13.im, d02.im - d13.re};  // d02 - i d13
   x3 = {d02.re - d13.im, d02.im + d13.re};  // d02 + i d13
 }
 
+// In-place forward 8-point DFT: even/odd 4-point DFTs and one radix-2 step.
+__device__ __forceinline__ void dft8(cd (&v)[8]) {
+  cd e0 = v[0], e1 = v[2], e2 = v[4], e3 = v[6];
+  cd o0 = v[1], o1 = v[3], o2 = v[5], o3 = v[7];
+  dft4(e0, e1, e2, e3);
+  dft4(o0, o1, o2, o3);
+  // W8^1 = (1 - i)/sqrt2, W8^2 = -i, W8^3 = -(1 + i)/sqrt2
+  const cd t1 = {(o1.re + o1.im) * kDRootHalf, (o1.im - o1.re) * kDRootHalf};
+  const cd t2 = {o2.im, -o2.re};
+  const cd t3 = {(o3.im - o3.re) * kDRootHalf, -(o3.re + o3.im) * kDRootHalf};
+  v[0] = c_add(e0, o0); v[4] = c_sub(e0, o0);
+  v[1] = c_add(e1, t1); v[5] = c_sub(e1, t1);
+  v[2] = c_add(e2, t2); v[6] = c_sub(e2, t2);
+  v[3] = c_add(e3, t3); v[7] = c_sub(e3, t3);
+}
+
 // In-place forward 25-point DFT, 5 x 5: n = na + 5 nb, k = 5 ka + kb.
-// Input z[n] in natural order; output Z[k] in natural order.
-__device__ __forceinline__ void dft25(cf (&z)[25]) {
-  cf t[5][5];
+__device__ __forceinline__ void dft25(cd (&z)[25]) {
+  cd t[5][5];
 #pragma unroll
   for (int na = 0; na < 5; ++na) {
-    cf a = z[na], b = z[na + 5], c = z[na + 10], d = z[na + 15], e = z[na + 20];
+    cd a = z[na], b = z[na + 5], c = z[na + 10], d = z[na + 15], e = z[na + 20];
     dft5(a, b, c, d, e);
     t[na][0] = a; t[na][1] = b; t[na][2] = c; t[na][3] = d; t[na][4] = e;
   }
@@ -74,80 +111,63 @@ __device__ __forceinline__ void dft25(cf (&z)[25]) {
   for (int na = 1; na < 5; ++na)
 #pragma unroll
     for (int kb = 1; kb < 5; ++kb)
-      t[na][kb] = c_twiddle(t[na][kb], kCos25[na * kb], kSin25[na * kb]);
+      t[na][kb] = c_twiddle(t[na][kb], kDCos25[na * kb], kDSin25[na * kb]);
 #pragma unroll
   for (int kb = 0; kb < 5; ++kb) {
-    cf a = t[0][kb], b = t[1][kb], c = t[2][kb], d = t[3][kb], e = t[4][kb];
+    cd a = t[0][kb], b = t[1][kb], c = t[2][kb], d = t[3][kb], e = t[4][kb];
     dft5(a, b, c, d, e);
     z[kb] = a; z[5 + kb] = b; z[10 + kb] = c; z[15 + kb] = d; z[20 + kb] = e;
   }
 }
 
-// In-place forward 16-point DFT, 4 x 4: n = na + 4 nb, k = 4 ka + kb.
-__device__ __forceinline__ void dft16(cf (&v)[16]) {
-  cf t[4][4];
-#pragma unroll
-  for (int na = 0; na < 4; ++na) {
-    cf a = v[na], b = v[na + 4], c = v[na + 8], d = v[na + 12];
-    dft4(a, b, c, d);
-    t[na][0] = a; t[na][1] = b; t[na][2] = c; t[na][3] = d;
-  }
-#pragma unroll
-  for (int na = 1; na < 4; ++na)
-#pragma unroll
-    for (int kb = 1; kb < 4; ++kb)
-      t[na][kb] = c_twiddle(t[na][kb], kCos16[na * kb], kSin16[na * kb]);
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    cf a = t[0][kb], b = t[1][kb], c = t[2][kb], d = t[3][kb];
-    dft4(a, b, c, d);
-    v[kb] = a; v[4 + kb] = b; v[8 + kb] = c; v[12 + kb] = d;
-  }
+__host__ __device__ constexpr int pfa_m(int n1, int n2) { return (25 * n1 + 8 * n2) % 200; }
+__host__ __device__ constexpr int pfa_k(int k1, int k2) { return (25 * k1 + 176 * k2) % 200; }
+
+// Swap a double with the pair partner (lanes 2f <-> 2f+1): DPP quad_perm [1,0,3,2].
+__device__ __forceinline__ double pair_swap(double v) {
+  const long long b = __builtin_bit_cast(long long, v);
+  // quad_perm reads a lane of the same quad for every lane, so no lane keeps
+  // an old value (bound_ctrl is irrelevant and set).
+  const int lo = __builtin_amdgcn_mov_dpp((int)b, 0xB1, 0xf, 0xf, true);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(b >> 32), 0xB1, 0xf, 0xf, true);
+  return __builtin_bit_cast(double, ((long long)hi << 32) | (unsigned int)lo);
 }
 
-// Compiler ordering fence for a value: an empty volatile asm that "rewrites"
-// v in a VGPR. Volatile asm statements keep their program order, so fencing a
-// phase's inputs after the previous phase's outputs stops the scheduler from
-// interleaving independent phases (which would raise register pressure far
-// beyond the ~430 values one frame needs). It emits no instruction.
-__device__ __forceinline__ void fence(float& v) { asm volatile("" : "+v"(v)); }
-__device__ __forceinline__ void fence(cf& v) { fence(v.re); fence(v.im); }
-
-__host__ __device__ constexpr int pfa_in(int n1, int n2) { return (25 * n1 + 16 * n2) % 400; }
-__host__ __device__ constexpr int pfa_out(int k1, int k2) { return (225 * k1 + 176 * k2) % 400; }
-__host__ __device__ constexpr int bin_of(int k1, int k2) {
-  return pfa_out(k1, k2) <= 200 ? pfa_out(k1, k2) : 400 - pfa_out(k1, k2);
-}
-
-// One frame: x[400] raw samples -> out[128] log-mel.
+// One frame on a lane pair.
+//   v[200]   this lane's samples: x[2m + role], m = 0..199 (fp32)
+//   win      this role's 200-double window table in LDS (kDWinPairs layout)
+//   rot      cos, sin of 2 pi k / 800 for k = 0..100, interleaved (uniform)
+//   sgn      +1.0 for role 0, -1.0 for role 1 (direction of the W800 rotation)
+//   role     0 or 1
+//   out[64]  log-mel of bands 64*role .. 64*role + 63
 // Bins that are not multiples of 25 come out of the transform at twice their
-// amplitude (the factor 1/2 of the two-real-sequences split is not applied);
-// their filter weights carry the compensating 1/4.
-__device__ __forceinline__ void logmel_frame(const float (&x)[400], float (&out)[128]) {
-  // Stage 1: 16 real 25-point DFTs over n2, two per complex DFT.
-  // A[n1][k2] for k2 = 0..12 (k2 = 0 is real: its .im is an exact 0).
-  cf A[16][13];
+// amplitude (the 1/2 of the two-real-sequences split is not applied); their
+// filter weights carry the compensating 1/4.
+__device__ __forceinline__ void logmel_pair_frame(const float (&v)[200], const double* win,
+                                                  const double* __restrict__ rot, double sgn,
+                                                  int role, float (&out)[64]) {
+  // Stage 1: 8 real 25-point DFTs over n2, two per complex DFT.
+  // A[n1][k2], k2 = 0..12 (k2 = 0 is real: its .im is an exact 0).
+  cd A[8][13];
 #pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    cf z[25];
+  for (int p = 0; p < 4; ++p) {
+    cd z[25];
 #pragma unroll
     for (int n2 = 0; n2 < 25; ++n2) {
-      const int ia = pfa_in(2 * p, n2), ib = pfa_in(2 * p + 1, n2);
-      float xa = x[ia], xb = x[ib];
+      float xa = v[pfa_m(2 * p, n2)], xb = v[pfa_m(2 * p + 1, n2)];
       fence(xa);
       fence(xb);
-      z[n2] = {kWin[ia] * xa, kWin[ib] * xb};
+      const double2 w = *reinterpret_cast<const double2*>(win + 50 * p + 2 * n2);
+      z[n2] = {w.x * (double)xa, w.y * (double)xb};
     }
     dft25(z);
-    A[2 * p][0] = {z[0].re, 0.0f};
-    A[2 * p + 1][0] = {z[0].im, 0.0f};
+    A[2 * p][0] = {z[0].re, 0.0};
+    A[2 * p + 1][0] = {z[0].im, 0.0};
 #pragma unroll
     for (int k = 1; k <= 12; ++k) {
-      const cf zk = z[k], zc = z[25 - k];
-      // 2 * DFT of the real part:  zk + conj(zc)
-      A[2 * p][k] = {zk.re + zc.re, zk.im - zc.im};
-      // 2 * DFT of the imaginary part: -i (zk - conj(zc))
-      A[2 * p + 1][k] = {zk.im + zc.im, zc.re - zk.re};
+      const cd zk = z[k], zc = z[25 - k];
+      A[2 * p][k] = {zk.re + zc.re, zk.im - zc.im};      // 2 x DFT of the first sequence
+      A[2 * p + 1][k] = {zk.im + zc.im, zc.re - zk.re};  // 2 x DFT of the second
     }
 #pragma unroll
     for (int k = 0; k <= 12; ++k) {
@@ -160,40 +180,62 @@ __device__ __forceinline__ void logmel_frame(const float (&x)[400], float (&out)
     }
   }
 
-  // Stage 2: for each k2, a 16-point DFT over n1, then power.
+  // Stage 2 and the combine: for each k2, an 8-point DFT over n1 gives this
+  // role's spectrum R at k = pfa_k(k1, k2) (k > 100 through conjugation);
+  // rotate, swap with the partner, and form the powers of bins k and 200 - k.
   float P[201];
 #pragma unroll
   for (int k2 = 0; k2 <= 12; ++k2) {
-    cf v[16];
+    cd q[8];
 #pragma unroll
-    for (int n1 = 0; n1 < 16; ++n1) {
-      v[n1] = A[n1][k2];
-      fence(v[n1].re);
-      if (k2 > 0) fence(v[n1].im);
+    for (int n1 = 0; n1 < 8; ++n1) {
+      q[n1] = A[n1][k2];
+      fence(q[n1].re);
+      if (k2 > 0) fence(q[n1].im);
     }
-    dft16(v);
+    dft8(q);
 #pragma unroll
-    for (int k1 = 0; k1 < 16; ++k1) {
-      if (k2 == 0 && k1 > 8) continue;  // conjugates of k1 = 1..7
-      P[bin_of(k1, k2)] = v[k1].re * v[k1].re + v[k1].im * v[k1].im;
-      fence(P[bin_of(k1, k2)]);
+    for (int k1 = 0; k1 < 8; ++k1) {
+      if (k2 == 0 && k1 > 4) continue;          // conjugates of k1 = 1..3
+      const int k = pfa_k(k1, k2);
+      const int kap = k <= 100 ? k : 200 - k;
+      if (kap == 0) continue;                   // bins 0 and 200 carry no weight
+      const cd r = k <= 100 ? q[k1] : cd{q[k1].re, -q[k1].im};
+      const double c = rot[2 * kap], s = sgn * rot[2 * kap + 1];
+      // role 0: r * exp(+2 pi i kap / 800); role 1: r * exp(-2 pi i kap / 800)
+      const cd u = {r.re * c - r.im * s, r.re * s + r.im * c};
+      const cd w = {pair_swap(u.re), pair_swap(u.im)};
+      const cd a = c_add(u, w), b = c_sub(u, w);
+      P[kap] = (float)(a.re * a.re + a.im * a.im);
+      fence(P[kap]);
+      if (kap != 100) {
+        P[200 - kap] = (float)(b.re * b.re + b.im * b.im);
+        fence(P[200 - kap]);
+      }
     }
   }
 
-  // Band-sparse mel projection and log with the 1e-10 floor. The floor test
+  // Band-sparse mel projection (both lanes, all bands), then this lane's
+  // half of the bands through the log with the 1e-10 floor. The floor test
   // is written so that a NaN energy stays NaN.
+  float E[128];
 #pragma unroll
   for (int m = 0; m < 128; ++m) {
     if (kMelCount[m] == 0) {
-      out[m] = kLnFloor;
+      E[m] = 0.0f;
       continue;
     }
     float e = kMelW[m][0] * P[kMelStart[m]];
 #pragma unroll
     for (int j = 1; j < kMelMaxBins; ++j)
       if (j < kMelCount[m]) e += kMelW[m][j] * P[kMelStart[m] + j];
+    E[m] = e;
+  }
+#pragma unroll
+  for (int i = 0; i < 64; ++i) {
+    float e = role ? E[64 + i] : E[i];
     e = (e < kLogFloor) ? kLogFloor : e;
-    out[m] = __builtin_amdgcn_logf(e) * kLn2;
+    out[i] = __builtin_amdgcn_logf(e) * kLn2;
   }
 }
 

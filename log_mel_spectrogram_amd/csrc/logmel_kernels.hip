@@ -1,16 +1,15 @@
 // HIP kernels of the log-mel front end for gfx950 (MI355X).
 //
 // logmel_tiles_kernel: the offline hot path over a packed ragged batch.
-//   The flattened frame space [0, total_frames) is cut into tiles of 64
-//   consecutive frames, one wavefront per tile, one frame per lane. A tile may
-//   straddle clips. Each lane finds its clip from the int64 frame offsets,
-//   loads only the first 160 samples of its frame from HBM and takes the
-//   remaining 240 (the overlap of the 400/160 framing) from its two right
-//   neighbours with wavefront-shift DPP moves, so every sample is read from
-//   HBM once. Lanes whose neighbours are not their next frames (clip ends,
-//   the tile's last two lanes) read those 240 samples themselves. Then the
-//   per-frame routine of logmel_frame.h runs in registers and the lane writes
-//   its 512-byte output row once.
+//   The flattened frame space [0, total_frames) is cut into tiles of 32
+//   consecutive frames, one wavefront per tile, one frame per lane pair
+//   (role 0: even samples, role 1: odd samples; see logmel_frame.h). A tile
+//   may straddle clips: each pair finds its clip from the int64 frame
+//   offsets. Each lane reads its frame's 400 samples with 16-byte loads
+//   (starting at the frame's first sample, or one sample later for role 1)
+//   and keeps its 200; neighbouring frames share 240 samples, which the L1
+//   and L2 caches serve, so HBM sees each sample about once. The pair's
+//   transform runs in registers and each lane writes its 64 bands once.
 //
 // logmel_stream_prep_kernel: the streaming push, step 1. Moves each stream's
 //   carry (the samples of its next, not yet complete frame) to sit right
@@ -22,18 +21,18 @@
 #include <stdint.h>
 
 #include "logmel_frame.h"
+#include "logmel_launch.h"
 
 namespace logmel {
 
-static constexpr int kTile = 64;
+static constexpr int kTile = 32;          // frames per wavefront
+static constexpr int kWaveLanes = 64;
 
-__device__ __forceinline__ float shl1(float v) {
-  // wave_shl:1 -- lane i receives lane i+1's value (lane 63 keeps its own,
-  // which is never used: the tile's last lanes always reload).
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v),
-                                         0x130, 0xf, 0xf, false));
-}
+// 16 bytes from a 4-byte aligned address (global memory allows this on the
+// HSA target).
+struct __attribute__((packed, aligned(4))) f4u {
+  float x, y, z, w;
+};
 
 // First index in a[0, n) whose value is > v (a non-decreasing).
 __device__ __forceinline__ int64_t upper_bound_i64(const int64_t* __restrict__ a, int64_t n,
@@ -46,23 +45,6 @@ __device__ __forceinline__ int64_t upper_bound_i64(const int64_t* __restrict__ a
   return lo;
 }
 
-// dst[0..N) = p[0..N). 16-byte loads when p is 16-byte aligned, else 4-byte
-// loads (a clip may start at any sample; all frames of one clip share the
-// alignment because the hop, 160 samples, is a multiple of 4).
-template <int N>
-__device__ __forceinline__ void load_run(const float* __restrict__ p, float* dst, bool al16) {
-  if (al16) {
-#pragma unroll
-    for (int i = 0; i < N / 4; ++i) {
-      const float4 v = *reinterpret_cast<const float4*>(p + 4 * i);
-      dst[4 * i] = v.x; dst[4 * i + 1] = v.y; dst[4 * i + 2] = v.z; dst[4 * i + 3] = v.w;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < N; ++i) dst[i] = p[i];
-  }
-}
-
 extern "C" __global__ void __attribute__((amdgpu_flat_work_group_size(64, 64),
                                           amdgpu_waves_per_eu(1, 1)))
 logmel_tiles_kernel(const float* __restrict__ samples,
@@ -71,15 +53,22 @@ logmel_tiles_kernel(const float* __restrict__ samples,
                     const int64_t* __restrict__ frame_off,   // [n_clips + 1]
                     int64_t n_clips, int64_t total_frames,
                     float* __restrict__ out,                 // [total_frames][128]
-                    int64_t first_tile)                      // tile index of blockIdx.x == 0
+                    int64_t first_tile,                      // tile index of blockIdx.x == 0
+                    const double* __restrict__ tables)       // plan tables: window, rotation
 {
+  __shared__ double win_lds[400];
   const int lane = threadIdx.x;
+  const int role = lane & 1;
+  for (int i = lane; i < 400; i += kWaveLanes) win_lds[i] = tables[kTabWindow + i];
+
   const int64_t g0 = (first_tile + (int64_t)blockIdx.x) * kTile;
-  const int64_t g = g0 + lane;
+  const int64_t g = g0 + (lane >> 1);
   const bool in_range = g < total_frames;
   const int64_t gq = in_range ? g : total_frames - 1;   // lookup key for idle lanes
 
-  // Clip of the tile's first frame (wave-uniform), then of every lane.
+  // Clip of the tile's first frame (wave-uniform), then of every pair: lane j
+  // holds the j-th clip boundary after it, and each lane counts the
+  // boundaries at or below its frame.
   int64_t c0 = upper_bound_i64(frame_off, n_clips + 1, g0) - 1;
   c0 = c0 < 0 ? 0 : c0;
   const int64_t bidx = c0 + 1 + lane;
@@ -87,7 +76,7 @@ logmel_tiles_kernel(const float* __restrict__ samples,
   const int64_t B63 = __shfl(B, 63);
   int64_t c;
   if (B63 <= gq) {
-    // 64 or more clip boundaries inside this tile (many empty clips).
+    // 64 or more clip boundaries inside this tile (runs of empty clips).
     c = upper_bound_i64(frame_off, n_clips + 1, gq) - 1;
   } else {
     int cnt = 0;
@@ -101,43 +90,43 @@ logmel_tiles_kernel(const float* __restrict__ samples,
   const int64_t s = seg_start[c] + 160 * f;
   // A frame is only computed if all its 400 samples lie inside its clip.
   const bool valid = in_range && f >= 0 && (s + 400 <= seg_end[c]);
-  // Wave-uniform: may every lane use 16-byte loads?
-  const bool al16 = __all(!valid || (s & 3) == 0);
 
-  float x[400];
+  // This lane's 200 samples x[s + 2m + role]: components 0 and 2 of 16-byte
+  // loads at s + role + 4q; the last pair as two 4-byte loads so that no
+  // load reaches past the frame.
+  float v[200];
   if (valid) {
-    load_run<160>(samples + s, x, al16);
+    const float* p = samples + s + role;
+#pragma unroll
+    for (int q = 0; q < 99; ++q) {
+      const f4u t = *reinterpret_cast<const f4u*>(p + 4 * q);
+      v[2 * q] = t.x;
+      v[2 * q + 1] = t.z;
+    }
+    v[198] = p[396];
+    v[199] = p[398];
   } else {
 #pragma unroll
-    for (int i = 0; i < 160; ++i) x[i] = 0.0f;
+    for (int i = 0; i < 200; ++i) v[i] = 0.0f;
   }
 #pragma unroll
-  for (int i = 0; i < 160; ++i) x[160 + i] = shl1(x[i]);
-#pragma unroll
-  for (int i = 0; i < 80; ++i) x[320 + i] = shl1(x[160 + i]);
+  for (int i = 0; i < 200; ++i) fence(v[i]);
+  __syncthreads();   // window table in LDS
 
-  // Is lane+2 this clip's frame f+2 (then lane+1 is frame f+1)?
-  const int64_t c2 = __shfl_down(c, 2);
-  const bool v2 = __shfl_down((int)valid, 2) != 0;
-  const bool have_next = (lane < kTile - 2) && v2 && (c2 == c);
-  if (valid && !have_next) load_run<240>(samples + s + 160, x + 160, al16);
-#pragma unroll
-  for (int i = 0; i < 400; ++i) fence(x[i]);
-
-  float o[128];
-  logmel_frame(x, o);
+  float o[64];
+  logmel_pair_frame(v, win_lds + 200 * role, tables + kTabRot800, role ? -1.0 : 1.0, role, o);
 
   if (in_range) {
-    float4* dst = reinterpret_cast<float4*>(out + g * 128);
+    float4* dst = reinterpret_cast<float4*>(out + g * 128 + 64 * role);
     if (valid) {
 #pragma unroll
-      for (int i = 0; i < 32; ++i) dst[i] = make_float4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+      for (int i = 0; i < 16; ++i) dst[i] = make_float4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
     } else {
       // Offsets that promise a frame the clip cannot hold: a loud row, not a
       // silent truncation.
       const float qnan = __builtin_nanf("");
 #pragma unroll
-      for (int i = 0; i < 32; ++i) dst[i] = make_float4(qnan, qnan, qnan, qnan);
+      for (int i = 0; i < 16; ++i) dst[i] = make_float4(qnan, qnan, qnan, qnan);
     }
   }
 }
@@ -180,21 +169,19 @@ logmel_stream_prep_kernel(float* __restrict__ ws, int64_t row_stride,
 // ---------------------------------------------------------------------------
 // Host-side launchers, called by the C-ABI layer.
 // ---------------------------------------------------------------------------
-#include "logmel_launch.h"
-
-hipError_t logmel_launch_tiles(const float* samples, const int64_t* seg_start,
-                               const int64_t* seg_end, const int64_t* frame_off,
-                               int64_t n_clips, int64_t total_frames, float* out,
-                               hipStream_t stream) {
+hipError_t logmel_launch_tiles(const double* tables, const float* samples,
+                               const int64_t* seg_start, const int64_t* seg_end,
+                               const int64_t* frame_off, int64_t n_clips, int64_t total_frames,
+                               float* out, hipStream_t stream) {
   if (total_frames <= 0) return hipSuccess;
   const int64_t tiles = (total_frames + logmel::kTile - 1) / logmel::kTile;
   // A launch covers at most 2^25 workgroups (2^31 work-items).
   const int64_t chunk = (int64_t)1 << 25;
   for (int64_t t0 = 0; t0 < tiles; t0 += chunk) {
     const int64_t n = tiles - t0 < chunk ? tiles - t0 : chunk;
-    hipLaunchKernelGGL(logmel::logmel_tiles_kernel, dim3((unsigned)n), dim3(logmel::kTile), 0,
+    hipLaunchKernelGGL(logmel::logmel_tiles_kernel, dim3((unsigned)n), dim3(logmel::kWaveLanes), 0,
                        stream, samples, seg_start, seg_end, frame_off, n_clips, total_frames,
-                       out, t0);
+                       out, t0, tables);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

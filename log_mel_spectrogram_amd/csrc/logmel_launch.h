@@ -4,10 +4,16 @@
 #include <stdint.h>
 
 
-hipError_t logmel_launch_tiles(const float* samples, const int64_t* seg_start,
-                               const int64_t* seg_end, const int64_t* frame_off,
-                               int64_t n_clips, int64_t total_frames, float* out,
-                               hipStream_t stream);
+// Device constant tables owned by a plan (fp64): the window in the order the
+// even/odd lanes consume it, then cos/sin of 2 pi k / 800 interleaved.
+static constexpr int kTabWindow = 0;
+static constexpr int kTabRot800 = 400;
+static constexpr int kTabDoubles = 602;
+
+hipError_t logmel_launch_tiles(const double* tables, const float* samples,
+                               const int64_t* seg_start, const int64_t* seg_end,
+                               const int64_t* frame_off, int64_t n_clips, int64_t total_frames,
+                               float* out, hipStream_t stream);
 
 hipError_t logmel_launch_stream_prep(float* ws, int64_t row_stride, const float* fresh,
                                      const int64_t* meta, int64_t n_streams,
