@@ -75,7 +75,9 @@ logmel_tiles_kernel(const float* __restrict__ samples,
   const int64_t B = bidx <= n_clips ? frame_off[bidx] : INT64_MAX;
   const int64_t B63 = __shfl(B, 63);
   int64_t c;
-  if (B63 <= gq) {
+  // The cross-lane search below needs every lane (__shfl reads inactive
+  // lanes as garbage), so the choice is made for the whole wavefront.
+  if (__any(B63 <= gq)) {
     // 64 or more clip boundaries inside this tile (runs of empty clips).
     c = upper_bound_i64(frame_off, n_clips + 1, gq) - 1;
   } else {
