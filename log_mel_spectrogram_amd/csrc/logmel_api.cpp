@@ -45,7 +45,7 @@ int64_t frames_of(int64_t n) { return n < kNFFT ? 0 : (n - kNFFT) / kHop + 1; }
 static const double kHostWindow[400] = {
 #include "logmel_window.inc"
 };
-static const double kHostRot800[202] = {
+static const double kHostRot800[208] = {
 #include "logmel_rot800.inc"
 };
 

@@ -136,7 +136,7 @@ __device__ __forceinline__ double pair_swap(double v) {
 // One frame on a lane pair.
 //   v[200]   this lane's samples: x[2m + role], m = 0..199 (fp32)
 //   win      this role's 200-double window table in LDS (kDWinPairs layout)
-//   rot      cos, sin of 2 pi k / 800 for k = 0..100, interleaved (uniform)
+//   rot      cos, sin of 2 pi kap / 800 for the bins in [k2][k1] order (uniform)
 //   sgn      +1.0 for role 0, -1.0 for role 1 (direction of the W800 rotation)
 //   role     0 or 1
 //   out[64]  log-mel of bands 64*role .. 64*role + 63
@@ -152,13 +152,21 @@ __device__ __forceinline__ void logmel_pair_frame(const float (&v)[200], const d
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     cd z[25];
+    float xa[25], xb[25];
 #pragma unroll
     for (int n2 = 0; n2 < 25; ++n2) {
-      float xa = v[pfa_m(2 * p, n2)], xb = v[pfa_m(2 * p + 1, n2)];
-      fence(xa);
-      fence(xb);
+      xa[n2] = v[pfa_m(2 * p, n2)];
+      xb[n2] = v[pfa_m(2 * p + 1, n2)];
+    }
+#pragma unroll
+    for (int n2 = 0; n2 < 25; ++n2) {
+      fence(xa[n2]);
+      fence(xb[n2]);
+    }
+#pragma unroll
+    for (int n2 = 0; n2 < 25; ++n2) {
       const double2 w = *reinterpret_cast<const double2*>(win + 50 * p + 2 * n2);
-      z[n2] = {w.x * (double)xa, w.y * (double)xb};
+      z[n2] = {w.x * (double)xa[n2], w.y * (double)xb[n2]};
     }
     dft25(z);
     A[2 * p][0] = {z[0].re, 0.0};
@@ -193,6 +201,14 @@ __device__ __forceinline__ void logmel_pair_frame(const float (&v)[200], const d
       fence(q[n1].re);
       if (k2 > 0) fence(q[n1].im);
     }
+    // This column's rotations, loaded ahead of the 8-point DFT so that the
+    // scalar loads overlap it.
+    double rc[8], rs[8];
+#pragma unroll
+    for (int k1 = 0; k1 < 8; ++k1) {
+      rc[k1] = rot[16 * k2 + 2 * k1];
+      rs[k1] = rot[16 * k2 + 2 * k1 + 1];
+    }
     dft8(q);
 #pragma unroll
     for (int k1 = 0; k1 < 8; ++k1) {
@@ -201,17 +217,25 @@ __device__ __forceinline__ void logmel_pair_frame(const float (&v)[200], const d
       const int kap = k <= 100 ? k : 200 - k;
       if (kap == 0) continue;                   // bins 0 and 200 carry no weight
       const cd r = k <= 100 ? q[k1] : cd{q[k1].re, -q[k1].im};
-      const double c = rot[2 * kap], s = sgn * rot[2 * kap + 1];
+      const double c = rc[k1], s = sgn * rs[k1];
       // role 0: r * exp(+2 pi i kap / 800); role 1: r * exp(-2 pi i kap / 800)
       const cd u = {r.re * c - r.im * s, r.re * s + r.im * c};
       const cd w = {pair_swap(u.re), pair_swap(u.im)};
       const cd a = c_add(u, w), b = c_sub(u, w);
       P[kap] = (float)(a.re * a.re + a.im * a.im);
-      fence(P[kap]);
       if (kap != 100) {
         P[200 - kap] = (float)(b.re * b.re + b.im * b.im);
-        fence(P[200 - kap]);
       }
+    }
+    // one scheduling region per column
+#pragma unroll
+    for (int k1 = 0; k1 < 8; ++k1) {
+      if (k2 == 0 && k1 > 4) continue;
+      const int k = pfa_k(k1, k2);
+      const int kap = k <= 100 ? k : 200 - k;
+      if (kap == 0) continue;
+      fence(P[kap]);
+      if (kap != 100) fence(P[200 - kap]);
     }
   }
 

@@ -5,10 +5,11 @@
 
 
 // Device constant tables owned by a plan (fp64): the window in the order the
-// even/odd lanes consume it, then cos/sin of 2 pi k / 800 interleaved.
+// even/odd lanes consume it, then cos/sin of 2 pi k / 800 interleaved, in the
+// order the transform's 8-point DFTs produce bins ([k2][k1], 13 x 8 pairs).
 static constexpr int kTabWindow = 0;
 static constexpr int kTabRot800 = 400;
-static constexpr int kTabDoubles = 602;
+static constexpr int kTabDoubles = 608;
 
 hipError_t logmel_launch_tiles(const double* tables, const float* samples,
                                const int64_t* seg_start, const int64_t* seg_end,
