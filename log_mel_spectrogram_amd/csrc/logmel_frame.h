@@ -18,7 +18,7 @@
 // odd ones (decimation in time). Each role runs the same code:
 //   * a 200-point real DFT as a prime-factor (Good-Thomas) 8 x 25 transform,
 //       m = (25 n1 + 8 n2) mod 200,  k = (25 k1 + 176 k2) mod 200,
-//     with 8 real 25-point DFTs (two at a time as one complex 5 x 5 DFT)
+//     with 8 real-input 25-point DFTs (5 x 5, conjugate halves skipped)
 //     and 13 8-point DFTs for k2 = 0..12, which cover k = 0..100;
 //   * the radix-2 combine X[k] = E[k] + W400^k O[k] in the symmetric form
 //       |X[k]|       = |W800^-k E[k] + W800^k O[k]|,
@@ -120,6 +120,50 @@ __device__ __forceinline__ void dft25(cd (&z)[25]) {
   }
 }
 
+// Forward 5-point DFT of real input: y0 real, y1 and y2 (y3 = conj y2 and
+// y4 = conj y1 are not formed).
+__device__ __forceinline__ void dft5_real(double x0, double x1, double x2, double x3, double x4,
+                                          double& y0, cd& y1, cd& y2) {
+  const double t1 = x1 + x4, t2 = x2 + x3, t3 = x1 - x4, t4 = x2 - x3;
+  y0 = x0 + t1 + t2;
+  const double a1 = x0 + kDC51 * t1 + kDC52 * t2, a2 = x0 + kDC52 * t1 + kDC51 * t2;
+  const double b1 = kDS51 * t3 + kDS52 * t4, b2 = kDS52 * t3 - kDS51 * t4;
+  y1 = {a1, -b1};
+  y2 = {a2, -b2};
+}
+
+// Forward 25-point DFT of real input y[25] (5 x 5, n = na + 5 nb,
+// k = 5 ka + kb), giving Z[0..12] (Z[0] real; the rest by Hermitian symmetry).
+// Only kb = 0, 1, 2 of the first stage are formed: kb = 3, 4 are conjugates.
+__device__ __forceinline__ void dft25_real(const double (&y)[25], cd (&Z)[13]) {
+  double r0[5];
+  cd r1[5], r2[5];
+#pragma unroll
+  for (int na = 0; na < 5; ++na)
+    dft5_real(y[na], y[na + 5], y[na + 10], y[na + 15], y[na + 20], r0[na], r1[na], r2[na]);
+#pragma unroll
+  for (int na = 1; na < 5; ++na) {
+    r1[na] = c_twiddle(r1[na], kDCos25[na], kDSin25[na]);
+    r2[na] = c_twiddle(r2[na], kDCos25[2 * na], kDSin25[2 * na]);
+  }
+  // kb = 0: real input again.
+  double z0;
+  cd z5, z10;
+  dft5_real(r0[0], r0[1], r0[2], r0[3], r0[4], z0, z5, z10);
+  // kb = 1 and kb = 2: complex.
+  dft5(r1[0], r1[1], r1[2], r1[3], r1[4]);   // Z[1], Z[6], Z[11], Z[16], Z[21]
+  dft5(r2[0], r2[1], r2[2], r2[3], r2[4]);   // Z[2], Z[7], Z[12], Z[17], Z[22]
+  Z[0] = {z0, 0.0};
+  Z[5] = z5;
+  Z[10] = z10;
+  Z[1] = r1[0]; Z[6] = r1[1]; Z[11] = r1[2];
+  Z[2] = r2[0]; Z[7] = r2[1]; Z[12] = r2[2];
+  Z[3] = {r2[4].re, -r2[4].im};    // conj Z[22]
+  Z[4] = {r1[4].re, -r1[4].im};    // conj Z[21]
+  Z[8] = {r2[3].re, -r2[3].im};    // conj Z[17]
+  Z[9] = {r1[3].re, -r1[3].im};    // conj Z[16]
+}
+
 __host__ __device__ constexpr int pfa_m(int n1, int n2) { return (25 * n1 + 8 * n2) % 200; }
 __host__ __device__ constexpr int pfa_k(int k1, int k2) { return (25 * k1 + 176 * k2) % 200; }
 
@@ -135,57 +179,48 @@ __device__ __forceinline__ double pair_swap(double v) {
 
 // One frame on a lane pair.
 //   v[200]   this lane's samples: x[2m + role], m = 0..199 (fp32)
-//   win      this role's 200-double window table in LDS (kDWinPairs layout)
+//   win      this role's 200-double window table in LDS, in the order
+//            [n1][n2] of sample m = (25 n1 + 8 n2) mod 200
 //   rot      cos, sin of 2 pi kap / 800 for the bins in [k2][k1] order (uniform)
 //   sgn      +1.0 for role 0, -1.0 for role 1 (direction of the W800 rotation)
 //   role     0 or 1
 //   out[64]  log-mel of bands 64*role .. 64*role + 63
-// Bins that are not multiples of 25 come out of the transform at twice their
-// amplitude (the 1/2 of the two-real-sequences split is not applied); their
-// filter weights carry the compensating 1/4.
 __device__ __forceinline__ void logmel_pair_frame(const float (&v)[200], const double* win,
                                                   const double* __restrict__ rot, double sgn,
                                                   int role, float (&out)[64]) {
-  // Stage 1: 8 real 25-point DFTs over n2, two per complex DFT.
+  // Stage 1: 8 real 25-point DFTs over n2, two rows n1 per scheduling region
+  // (two independent transforms give the scheduler work to overlap).
   // A[n1][k2], k2 = 0..12 (k2 = 0 is real: its .im is an exact 0).
   cd A[8][13];
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    cd z[25];
-    float xa[25], xb[25];
+    float xr[2][25];
 #pragma unroll
-    for (int n2 = 0; n2 < 25; ++n2) {
-      xa[n2] = v[pfa_m(2 * p, n2)];
-      xb[n2] = v[pfa_m(2 * p + 1, n2)];
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int n2 = 0; n2 < 25; ++n2) xr[h][n2] = v[pfa_m(2 * p + h, n2)];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int n2 = 0; n2 < 25; ++n2) fence(xr[h][n2]);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int n1 = 2 * p + h;
+      double y[25];
+#pragma unroll
+      for (int n2 = 0; n2 < 25; ++n2) y[n2] = win[25 * n1 + n2] * (double)xr[h][n2];
+      cd Z[13];
+      dft25_real(y, Z);
+#pragma unroll
+      for (int k = 0; k <= 12; ++k) A[n1][k] = Z[k];
     }
 #pragma unroll
-    for (int n2 = 0; n2 < 25; ++n2) {
-      fence(xa[n2]);
-      fence(xb[n2]);
-    }
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int n2 = 0; n2 < 25; ++n2) {
-      const double2 w = *reinterpret_cast<const double2*>(win + 50 * p + 2 * n2);
-      z[n2] = {w.x * (double)xa[n2], w.y * (double)xb[n2]};
-    }
-    dft25(z);
-    A[2 * p][0] = {z[0].re, 0.0};
-    A[2 * p + 1][0] = {z[0].im, 0.0};
-#pragma unroll
-    for (int k = 1; k <= 12; ++k) {
-      const cd zk = z[k], zc = z[25 - k];
-      A[2 * p][k] = {zk.re + zc.re, zk.im - zc.im};      // 2 x DFT of the first sequence
-      A[2 * p + 1][k] = {zk.im + zc.im, zc.re - zk.re};  // 2 x DFT of the second
-    }
-#pragma unroll
-    for (int k = 0; k <= 12; ++k) {
-      fence(A[2 * p][k].re);
-      fence(A[2 * p + 1][k].re);
-      if (k > 0) {
-        fence(A[2 * p][k].im);
-        fence(A[2 * p + 1][k].im);
+      for (int k = 0; k <= 12; ++k) {
+        fence(A[2 * p + h][k].re);
+        if (k > 0) fence(A[2 * p + h][k].im);
       }
-    }
   }
 
   // Stage 2 and the combine: for each k2, an 8-point DFT over n1 gives this
