@@ -24,9 +24,9 @@
 //       |X[k]|       = |W800^-k E[k] + W800^k O[k]|,
 //       |X[200 - k]| = |W800^-k E[k] - W800^k O[k]|,
 //     each role rotating its own spectrum by W800^(-/+k), swapping it with
-//     its partner (DPP), and forming both powers. Both lanes then hold the
-//     same 201 powers and run the same filterbank; each logs and stores one
-//     half of the 128 bands.
+//     its partner (DPP), and forming one of the two powers; a second DPP
+//     broadcast gives both lanes the same 201 powers, and both run the same
+//     filterbank; each logs and stores one half of the 128 bands.
 // Window values differ between the roles (w[2m] against w[2m+1]) and come
 // from LDS; every other constant is the same for all lanes.
 #pragma once
@@ -177,6 +177,13 @@ __device__ __forceinline__ double pair_swap(double v) {
   return __builtin_bit_cast(double, ((long long)hi << 32) | (unsigned int)lo);
 }
 
+// The value of the pair's lane `src` (0 = even, 1 = odd) in both lanes.
+__device__ __forceinline__ float pair_from(float v, int src) {
+  const int b = __builtin_bit_cast(int, v);
+  return __builtin_bit_cast(float, src == 0 ? __builtin_amdgcn_mov_dpp(b, 0xA0, 0xf, 0xf, true)
+                                            : __builtin_amdgcn_mov_dpp(b, 0xF5, 0xf, 0xf, true));
+}
+
 // One frame on a lane pair.
 //   v[200]   this lane's samples: x[2m + role], m = 0..199 (fp32)
 //   win      this role's 200-double window table in LDS, in the order
@@ -256,11 +263,13 @@ __device__ __forceinline__ void logmel_pair_frame(const float (&v)[200], const d
       // role 0: r * exp(+2 pi i kap / 800); role 1: r * exp(-2 pi i kap / 800)
       const cd u = {r.re * c - r.im * s, r.re * s + r.im * c};
       const cd w = {pair_swap(u.re), pair_swap(u.im)};
-      const cd a = c_add(u, w), b = c_sub(u, w);
-      P[kap] = (float)(a.re * a.re + a.im * a.im);
-      if (kap != 100) {
-        P[200 - kap] = (float)(b.re * b.re + b.im * b.im);
-      }
+      // role 0: |u + w|^2 = bin kap; role 1: |u - w|^2 = bin 200 - kap
+      const double are = w.re * sgn + u.re, aim = w.im * sgn + u.im;
+      const float own = (float)(are * are + aim * aim);
+      // Both lanes take bin kap from the even lane and bin 200 - kap from the
+      // odd one (DPP quad_perm [0,0,2,2] and [1,1,3,3]).
+      P[kap] = pair_from(own, 0);
+      if (kap != 100) P[200 - kap] = pair_from(own, 1);
     }
     // one scheduling region per column
 #pragma unroll

@@ -5,10 +5,9 @@
 //   consecutive frames, one wavefront per tile, one frame per lane pair
 //   (role 0: even samples, role 1: odd samples; see logmel_frame.h). A tile
 //   may straddle clips: each pair finds its clip from the int64 frame
-//   offsets. Each lane reads its frame's 400 samples with 16-byte loads
-//   (starting at the frame's first sample, or one sample later for role 1)
-//   and keeps its 200; neighbouring frames share 240 samples, which the L1
-//   and L2 caches serve, so HBM sees each sample about once. The pair's
+//   offsets. A tile inside one clip reads its 5360-sample span once,
+//   coalesced, and shares it through LDS; a tile across clips lets each lane
+//   gather its own 200 samples (the caches serve the overlap). The pair's
 //   transform runs in registers and each lane writes its 64 bands once.
 //
 // logmel_stream_prep_kernel: the streaming push, step 1. Moves each stream's
@@ -27,6 +26,16 @@ namespace logmel {
 
 static constexpr int kTile = 32;          // frames per wavefront
 static constexpr int kWaveLanes = 64;
+
+// A tile of 32 frames of one clip spans 31 * 160 + 400 = 5360 samples
+// (1340 16-byte groups). It is staged in LDS split by parity: element e of
+// the even (odd) sequence is sample 2e (2e + 1) of the span and sits at
+// e + 4 floor(e / 80), so that frame f's 200 values start at 84 f: the
+// 16-byte reads of the 32 frames then fall on distinct bank groups.
+static constexpr int kSpan = (kTile - 1) * 160 + 400;
+static constexpr int kSpanGroups = kSpan / 4;
+static constexpr int kParityLen = 2812;   // last element 2679 sits at 2811
+static constexpr int kOddBase = 2832;     // odd sequence after the even one
 
 // 16 bytes from a 4-byte aligned address (global memory allows this on the
 // HSA target).
@@ -57,7 +66,9 @@ logmel_tiles_kernel(const float* __restrict__ samples,
                     const double* __restrict__ tables)       // plan tables: window, rotation
 {
   __shared__ double win_lds[400];
+  __shared__ float4 span_lds[(kOddBase + kParityLen + 3) / 4];
   const int lane = threadIdx.x;
+  __builtin_assume(lane < kWaveLanes);
   const int role = lane & 1;
   for (int i = lane; i < 400; i += kWaveLanes) win_lds[i] = tables[kTabWindow + i];
 
@@ -93,11 +104,40 @@ logmel_tiles_kernel(const float* __restrict__ samples,
   // A frame is only computed if all its 400 samples lie inside its clip.
   const bool valid = in_range && f >= 0 && (s + 400 <= seg_end[c]);
 
-  // This lane's 200 samples x[s + 2m + role]: components 0 and 2 of 16-byte
-  // loads at s + role + 4q; the last pair as two 4-byte loads so that no
-  // load reaches past the frame.
+  // This lane's 200 samples x[s + 2m + role].
   float v[200];
-  if (valid) {
+  const bool same_clip = c == __shfl(c, 0);
+  if (__all(valid && same_clip)) {
+    // All 32 frames lie in one clip: the wavefront reads the tile's sample
+    // span once with coalesced 16-byte loads, splits it by parity into LDS,
+    // and each lane reads its frame's 200 values back from there.
+    const float* src = samples + __shfl(s, 0);
+    float* lds = reinterpret_cast<float*>(span_lds);
+#pragma unroll
+    for (int i = 0; i < (kSpanGroups + kWaveLanes - 1) / kWaveLanes; ++i) {
+      // Lanes past the span's end repeat its last group (same data, same
+      // place), so every load is issued without a branch.
+      const int j = min(lane + kWaveLanes * i, kSpanGroups - 1);
+      const f4u t = *reinterpret_cast<const f4u*>(src + 4 * j);
+      const int e = 2 * j + 4 * (j / 40);
+      *reinterpret_cast<float2*>(lds + e) = make_float2(t.x, t.z);
+      *reinterpret_cast<float2*>(lds + kOddBase + e) = make_float2(t.y, t.w);
+    }
+    __syncthreads();
+    const float4* a = reinterpret_cast<const float4*>(lds + role * kOddBase + 84 * (lane >> 1));
+#pragma unroll
+    for (int q = 0; q < 50; ++q) {
+      const float4 t = a[q + q / 20];
+      v[4 * q] = t.x;
+      v[4 * q + 1] = t.y;
+      v[4 * q + 2] = t.z;
+      v[4 * q + 3] = t.w;
+    }
+  } else if (valid) {
+    // Frames of several clips (or the batch's last, partial tile): each lane
+    // gathers its own samples, components 0 and 2 of 16-byte loads at
+    // s + role + 4q, the last pair as two 4-byte loads so that no load
+    // reaches past the frame.
     const float* p = samples + s + role;
 #pragma unroll
     for (int q = 0; q < 99; ++q) {
