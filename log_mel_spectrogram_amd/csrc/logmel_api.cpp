@@ -42,7 +42,7 @@ int64_t frames_of(int64_t n) { return n < kNFFT ? 0 : (n - kNFFT) / kHop + 1; }
 }  // namespace
 
 // fp64 tables, computed by gen_tables.py from the definitions.
-static const double kHostWindow[400] = {
+static const double kHostWindow[200] = {
 #include "logmel_window.inc"
 };
 static const double kHostRot800[208] = {

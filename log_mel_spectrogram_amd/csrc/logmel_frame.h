@@ -14,21 +14,24 @@
 // in fp64 and rounded once.
 //
 // Work split. fp64 doubles the registers a frame needs, so a frame takes two
-// adjacent lanes (a "pair"): role 0 transforms the even samples, role 1 the
-// odd ones (decimation in time). Each role runs the same code:
+// adjacent lanes (a "pair"): role 0 transforms the even samples in order,
+// e[m] = x[2m], role 1 the odd samples in reverse order, o[m] = x[399 - 2m]
+// (decimation in time). The window is symmetric, w[399 - 2m] = w[2m], so
+// both roles apply the same window values, and every constant of the
+// routine is the same for all lanes. Each role runs the same code:
 //   * a 200-point real DFT as a prime-factor (Good-Thomas) 8 x 25 transform,
 //       m = (25 n1 + 8 n2) mod 200,  k = (25 k1 + 176 k2) mod 200,
 //     with 8 real-input 25-point DFTs (5 x 5, conjugate halves skipped)
 //     and 13 8-point DFTs for k2 = 0..12, which cover k = 0..100;
-//   * the radix-2 combine X[k] = E[k] + W400^k O[k] in the symmetric form
-//       |X[k]|       = |W800^-k E[k] + W800^k O[k]|,
-//       |X[200 - k]| = |W800^-k E[k] - W800^k O[k]|,
-//     each role rotating its own spectrum by W800^(-/+k), swapping it with
-//     its partner (DPP), and forming one of the two powers; a second DPP
+//   * the radix-2 combine. With E and R the two roles' spectra, the odd
+//     samples' spectrum is W200^-k conj(R[k]), and multiplying X[k] by
+//     W800^k (a unit phase) gives, with u = W800^k E[k], v = W800^k R[k],
+//       |X[k]|       = |u + conj(v)|,
+//       |X[200 - k]| = |u - conj(v)|.
+//     Each role forms its own rotation (the same W800^k for both), swaps it
+//     with its partner (DPP) and forms one of the two powers; a second DPP
 //     broadcast gives both lanes the same 201 powers, and both run the same
 //     filterbank; each logs and stores one half of the 128 bands.
-// Window values differ between the roles (w[2m] against w[2m+1]) and come
-// from LDS; every other constant is the same for all lanes.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -185,14 +188,15 @@ __device__ __forceinline__ float pair_from(float v, int src) {
 }
 
 // One frame on a lane pair.
-//   v[200]   this lane's samples: x[2m + role], m = 0..199 (fp32)
-//   win      this role's 200-double window table in LDS, in the order
-//            [n1][n2] of sample m = (25 n1 + 8 n2) mod 200
+//   v[200]   this lane's samples, m = 0..199 (fp32): x[2m] for role 0,
+//            x[399 - 2m] for role 1
+//   win      w[2m], m = (25 n1 + 8 n2) mod 200, in [n1][n2] order (uniform)
 //   rot      cos, sin of 2 pi kap / 800 for the bins in [k2][k1] order (uniform)
-//   sgn      +1.0 for role 0, -1.0 for role 1 (direction of the W800 rotation)
+//   sgn      +1.0 for role 0, -1.0 for role 1
 //   role     0 or 1
 //   out[64]  log-mel of bands 64*role .. 64*role + 63
-__device__ __forceinline__ void logmel_pair_frame(const float (&v)[200], const double* win,
+__device__ __forceinline__ void logmel_pair_frame(const float (&v)[200],
+                                                  const double* __restrict__ win,
                                                   const double* __restrict__ rot, double sgn,
                                                   int role, float (&out)[64]) {
   // Stage 1: 8 real 25-point DFTs over n2, two rows n1 per scheduling region
@@ -259,12 +263,11 @@ __device__ __forceinline__ void logmel_pair_frame(const float (&v)[200], const d
       const int kap = k <= 100 ? k : 200 - k;
       if (kap == 0) continue;                   // bins 0 and 200 carry no weight
       const cd r = k <= 100 ? q[k1] : cd{q[k1].re, -q[k1].im};
-      const double c = rc[k1], s = sgn * rs[k1];
-      // role 0: r * exp(+2 pi i kap / 800); role 1: r * exp(-2 pi i kap / 800)
-      const cd u = {r.re * c - r.im * s, r.re * s + r.im * c};
+      // r * W800^kap, the same rotation in both roles
+      const cd u = c_twiddle(r, rc[k1], rs[k1]);
       const cd w = {pair_swap(u.re), pair_swap(u.im)};
-      // role 0: |u + w|^2 = bin kap; role 1: |u - w|^2 = bin 200 - kap
-      const double are = w.re * sgn + u.re, aim = w.im * sgn + u.im;
+      // role 0: |u + conj(w)|^2 = bin kap; role 1: |u - conj(w)|^2 = bin 200 - kap
+      const double are = w.re * sgn + u.re, aim = u.im - w.im * sgn;
       const float own = (float)(are * are + aim * aim);
       // Both lanes take bin kap from the even lane and bin 200 - kap from the
       // odd one (DPP quad_perm [0,0,2,2] and [1,1,3,3]).

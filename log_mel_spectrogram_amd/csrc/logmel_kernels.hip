@@ -28,10 +28,14 @@ static constexpr int kTile = 32;          // frames per wavefront
 static constexpr int kWaveLanes = 64;
 
 // A tile of 32 frames of one clip spans 31 * 160 + 400 = 5360 samples
-// (1340 16-byte groups). It is staged in LDS split by parity: element e of
-// the even (odd) sequence is sample 2e (2e + 1) of the span and sits at
-// e + 4 floor(e / 80), so that frame f's 200 values start at 84 f: the
-// 16-byte reads of the 32 frames then fall on distinct bank groups.
+// (1340 16-byte groups). It is staged in LDS split by parity, each sequence
+// of 2680 values stored with 4 padding slots after every 80 (value i at
+// i + 4 floor(i / 80)), so that a frame's 200 values start at a multiple of
+// 84 and the 16-byte reads of the 32 frames fall on distinct bank groups.
+// The even sequence holds sample 2i of the span in order; the odd one holds
+// sample 2i + 1 in reverse order (value i is sample 5359 - 2i), which is the
+// order the odd lane of a pair consumes: frame f's even values start at
+// 84 f, its reversed odd values at 84 (31 - f).
 static constexpr int kSpan = (kTile - 1) * 160 + 400;
 static constexpr int kSpanGroups = kSpan / 4;
 static constexpr int kParityLen = 2812;   // last element 2679 sits at 2811
@@ -65,46 +69,67 @@ logmel_tiles_kernel(const float* __restrict__ samples,
                     int64_t first_tile,                      // tile index of blockIdx.x == 0
                     const double* __restrict__ tables)       // plan tables: window, rotation
 {
-  __shared__ double win_lds[400];
   __shared__ float4 span_lds[(kOddBase + kParityLen + 3) / 4];
   const int lane = threadIdx.x;
   __builtin_assume(lane < kWaveLanes);
   const int role = lane & 1;
-  for (int i = lane; i < 400; i += kWaveLanes) win_lds[i] = tables[kTabWindow + i];
 
   const int64_t g0 = (first_tile + (int64_t)blockIdx.x) * kTile;
   const int64_t g = g0 + (lane >> 1);
   const bool in_range = g < total_frames;
   const int64_t gq = in_range ? g : total_frames - 1;   // lookup key for idle lanes
 
-  // Clip of the tile's first frame (wave-uniform), then of every pair: lane j
-  // holds the j-th clip boundary after it, and each lane counts the
-  // boundaries at or below its frame.
-  int64_t c0 = upper_bound_i64(frame_off, n_clips + 1, g0) - 1;
-  c0 = c0 < 0 ? 0 : c0;
+  // Clip of the tile's first frame (wave-uniform): the last c with
+  // frame_off[c] <= g0, by a 64-ary search (one load per lane and one ballot
+  // per level; the entries <= g0 form a prefix).
+  int64_t c0 = 0;
+  for (int64_t len = n_clips + 1; len > 1;) {
+    const int64_t stride = (len + kWaveLanes - 1) / kWaveLanes;
+    const int64_t idx = c0 + lane * stride;
+    const bool le = idx < c0 + len && frame_off[idx] <= g0;
+    const int cnt = __popcll(__ballot(le));
+    if (cnt == 0) break;                       // frame_off[0] > g0: inconsistent offsets
+    const int64_t lo = c0 + (cnt - 1) * stride;
+    len = min(stride, c0 + len - lo);
+    c0 = lo;
+  }
+  c0 = max(min(c0, n_clips - 1), (int64_t)0);
+  // Then the clip of every pair: lane j holds the j-th clip boundary after
+  // c0 (and clip c0 + j's sample range), and each lane counts the boundaries
+  // at or below its frame.
   const int64_t bidx = c0 + 1 + lane;
   const int64_t B = bidx <= n_clips ? frame_off[bidx] : INT64_MAX;
+  const int64_t cl = min(c0 + lane, n_clips - 1);
+  const int64_t SS = seg_start[cl], SE = seg_end[cl];
   const int64_t B63 = __shfl(B, 63);
-  int64_t c;
+  int64_t c, fo_c, ss_c, se_c;
   // The cross-lane search below needs every lane (__shfl reads inactive
   // lanes as garbage), so the choice is made for the whole wavefront.
   if (__any(B63 <= gq)) {
     // 64 or more clip boundaries inside this tile (runs of empty clips).
     c = upper_bound_i64(frame_off, n_clips + 1, gq) - 1;
+    c = c < 0 ? 0 : (c >= n_clips ? n_clips - 1 : c);   // only inconsistent offsets need this
+    fo_c = frame_off[c];
+    ss_c = seg_start[c];
+    se_c = seg_end[c];
   } else {
     int cnt = 0;
 #pragma unroll
     for (int step = 32; step >= 1; step >>= 1)
       if (__shfl(B, cnt + step - 1) <= gq) cnt += step;
-    c = c0 + cnt;
+    c = min(c0 + cnt, n_clips - 1);            // only inconsistent offsets need the clamp
+    const int j = (int)(c - c0);
+    const int64_t fo_prev = __shfl(B, j > 0 ? j - 1 : 0);
+    fo_c = j > 0 ? fo_prev : frame_off[c0];
+    ss_c = __shfl(SS, j);
+    se_c = __shfl(SE, j);
   }
-  c = c < 0 ? 0 : (c >= n_clips ? n_clips - 1 : c);   // only inconsistent offsets need this
-  const int64_t f = gq - frame_off[c];
-  const int64_t s = seg_start[c] + 160 * f;
+  const int64_t f = gq - fo_c;
+  const int64_t s = ss_c + 160 * f;
   // A frame is only computed if all its 400 samples lie inside its clip.
-  const bool valid = in_range && f >= 0 && (s + 400 <= seg_end[c]);
+  const bool valid = in_range && f >= 0 && (s + 400 <= se_c);
 
-  // This lane's 200 samples x[s + 2m + role].
+  // This lane's 200 samples: x[s + 2m] for role 0, x[s + 399 - 2m] for role 1.
   float v[200];
   const bool same_clip = c == __shfl(c, 0);
   if (__all(valid && same_clip)) {
@@ -119,12 +144,17 @@ logmel_tiles_kernel(const float* __restrict__ samples,
       // place), so every load is issued without a branch.
       const int j = min(lane + kWaveLanes * i, kSpanGroups - 1);
       const f4u t = *reinterpret_cast<const f4u*>(src + 4 * j);
+      // even values 2j, 2j + 1; reversed odd values 2678 - 2j (sample
+      // 4j + 3) and 2679 - 2j (sample 4j + 1)
       const int e = 2 * j + 4 * (j / 40);
+      const int o = kOddBase + (kSpan / 2 - 2 - 2 * j) + 4 * ((kSpanGroups - 1 - j) / 40);
       *reinterpret_cast<float2*>(lds + e) = make_float2(t.x, t.z);
-      *reinterpret_cast<float2*>(lds + kOddBase + e) = make_float2(t.y, t.w);
+      *reinterpret_cast<float2*>(lds + o) = make_float2(t.w, t.y);
     }
     __syncthreads();
-    const float4* a = reinterpret_cast<const float4*>(lds + role * kOddBase + 84 * (lane >> 1));
+    const int fl = lane >> 1;
+    const float4* a = reinterpret_cast<const float4*>(lds + (role ? kOddBase + 84 * (kTile - 1 - fl)
+                                                                  : 84 * fl));
 #pragma unroll
     for (int q = 0; q < 50; ++q) {
       const float4 t = a[q + q / 20];
@@ -135,28 +165,23 @@ logmel_tiles_kernel(const float* __restrict__ samples,
     }
   } else if (valid) {
     // Frames of several clips (or the batch's last, partial tile): each lane
-    // gathers its own samples, components 0 and 2 of 16-byte loads at
-    // s + role + 4q, the last pair as two 4-byte loads so that no load
-    // reaches past the frame.
-    const float* p = samples + s + role;
+    // gathers its own 200 samples; the caches serve the overlap.
+    const float* p = samples + s + (role ? 399 : 0);
+    const int64_t step = role ? -2 : 2;
 #pragma unroll
-    for (int q = 0; q < 99; ++q) {
-      const f4u t = *reinterpret_cast<const f4u*>(p + 4 * q);
-      v[2 * q] = t.x;
-      v[2 * q + 1] = t.z;
+    for (int m = 0; m < 200; ++m) {
+      v[m] = *p;
+      p += step;
     }
-    v[198] = p[396];
-    v[199] = p[398];
   } else {
 #pragma unroll
     for (int i = 0; i < 200; ++i) v[i] = 0.0f;
   }
 #pragma unroll
   for (int i = 0; i < 200; ++i) fence(v[i]);
-  __syncthreads();   // window table in LDS
 
   float o[64];
-  logmel_pair_frame(v, win_lds + 200 * role, tables + kTabRot800, role ? -1.0 : 1.0, role, o);
+  logmel_pair_frame(v, tables + kTabWindow, tables + kTabRot800, role ? -1.0 : 1.0, role, o);
 
   if (in_range) {
     float4* dst = reinterpret_cast<float4*>(out + g * 128 + 64 * role);

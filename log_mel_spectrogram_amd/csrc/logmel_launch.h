@@ -4,12 +4,13 @@
 #include <stdint.h>
 
 
-// Device constant tables owned by a plan (fp64): the window in the order the
-// even/odd lanes consume it, then cos/sin of 2 pi k / 800 interleaved, in the
-// order the transform's 8-point DFTs produce bins ([k2][k1], 13 x 8 pairs).
+// Device constant tables owned by a plan (fp64): the window at the even
+// points in the order the transform consumes them (both lanes of a pair use
+// it), then cos/sin of 2 pi k / 800 interleaved, in the order the
+// transform's 8-point DFTs produce bins ([k2][k1], 13 x 8 pairs).
 static constexpr int kTabWindow = 0;
-static constexpr int kTabRot800 = 400;
-static constexpr int kTabDoubles = 608;
+static constexpr int kTabRot800 = 200;
+static constexpr int kTabDoubles = 408;
 
 hipError_t logmel_launch_tiles(const double* tables, const float* samples,
                                const int64_t* seg_start, const int64_t* seg_end,
