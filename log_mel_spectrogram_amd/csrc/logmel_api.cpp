@@ -51,7 +51,8 @@ static const double kHostRot800[208] = {
 
 struct logmel_plan {
   logmel_config cfg;
-  double* tables = nullptr;  // device, kTabDoubles
+  double* tables = nullptr;  // device, kTabBytes
+  int resident_waves = 0;    // wavefronts of the transform kernel resident at once: one per SIMD
 };
 
 struct logmel_stream {
@@ -116,14 +117,22 @@ int logmel_plan_create(const logmel_config* cfg, logmel_plan** out) {
     delete p;
     return LOGMEL_ERR_DEVICE;
   }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, cfg->device) !=
+          hipSuccess || cus <= 0) {
+    delete p;
+    return LOGMEL_ERR_DEVICE;
+  }
+  p->resident_waves = 4 * cus;   // 4 SIMDs per compute unit
   double host[kTabDoubles];
   std::memcpy(host + kTabWindow, kHostWindow, sizeof(kHostWindow));
   std::memcpy(host + kTabRot800, kHostRot800, sizeof(kHostRot800));
-  if (hipMalloc(&p->tables, sizeof(host)) != hipSuccess) {
+  if (hipMalloc(&p->tables, kTabBytes) != hipSuccess) {
     delete p;
     return LOGMEL_ERR_OUT_OF_MEMORY;
   }
-  if (hipMemcpy(p->tables, host, sizeof(host), hipMemcpyHostToDevice) != hipSuccess) {
+  if (hipMemset(p->tables, 0, kTabBytes) != hipSuccess ||
+      hipMemcpy(p->tables, host, sizeof(host), hipMemcpyHostToDevice) != hipSuccess) {
     (void)hipFree(p->tables);
     delete p;
     return LOGMEL_ERR_DEVICE;
@@ -182,7 +191,8 @@ int logmel_compute(const logmel_plan* plan, const float* d_samples,
   }
   const hipError_t e = logmel_launch_tiles(plan->tables, d_samples, d_sample_offsets,
                                            d_sample_offsets + 1,
-                                           d_frame_offsets, n_clips, total_frames, d_out, st);
+                                           d_frame_offsets, n_clips, total_frames, d_out,
+                                           plan->resident_waves, st);
   return e == hipSuccess ? LOGMEL_OK : LOGMEL_ERR_DEVICE;
 }
 
@@ -306,7 +316,8 @@ int logmel_stream_push(logmel_stream* s, const float* d_new, const int64_t* push
   if (logmel_launch_stream_prep(s->ws, s->stride, d_new, s->meta_dev, n, st) != hipSuccess)
     return LOGMEL_ERR_DEVICE;
   if (logmel_launch_tiles(s->plan->tables, s->ws, s->meta_dev + 4 * n, s->meta_dev + 5 * n,
-                          s->meta_dev + 6 * n, n, total_frames, d_out, st) != hipSuccess)
+                          s->meta_dev + 6 * n, n, total_frames, d_out,
+                          s->plan->resident_waves, st) != hipSuccess)
     return LOGMEL_ERR_DEVICE;
   // Advance the host shadow.
   for (int64_t j = 0; j < n; ++j) {

@@ -187,18 +187,16 @@ __device__ __forceinline__ float pair_from(float v, int src) {
                                             : __builtin_amdgcn_mov_dpp(b, 0xF5, 0xf, 0xf, true));
 }
 
-// One frame on a lane pair.
+// Power spectrum of one frame on a lane pair.
 //   v[200]   this lane's samples, m = 0..199 (fp32): x[2m] for role 0,
 //            x[399 - 2m] for role 1
 //   win      w[2m], m = (25 n1 + 8 n2) mod 200, in [n1][n2] order (uniform)
 //   rot      cos, sin of 2 pi kap / 800 for the bins in [k2][k1] order (uniform)
 //   sgn      +1.0 for role 0, -1.0 for role 1
-//   role     0 or 1
-//   out[64]  log-mel of bands 64*role .. 64*role + 63
-__device__ __forceinline__ void logmel_pair_frame(const float (&v)[200],
-                                                  const double* __restrict__ win,
-                                                  const double* __restrict__ rot, double sgn,
-                                                  int role, float (&out)[64]) {
+//   P[201]   the frame's power spectrum |X[k]|^2 (the same in both lanes)
+__device__ __forceinline__ void pair_power(const float (&v)[200], const double* __restrict__ win,
+                                           const double* __restrict__ rot, double sgn,
+                                           float (&P)[201]) {
   // Stage 1: 8 real 25-point DFTs over n2, two rows n1 per scheduling region
   // (two independent transforms give the scheduler work to overlap).
   // A[n1][k2], k2 = 0..12 (k2 = 0 is real: its .im is an exact 0).
@@ -237,7 +235,7 @@ __device__ __forceinline__ void logmel_pair_frame(const float (&v)[200],
   // Stage 2 and the combine: for each k2, an 8-point DFT over n1 gives this
   // role's spectrum R at k = pfa_k(k1, k2) (k > 100 through conjugation);
   // rotate, swap with the partner, and form the powers of bins k and 200 - k.
-  float P[201];
+  P[0] = P[200] = 0.0f;   // no filter reaches bins 0 and 200
 #pragma unroll
   for (int k2 = 0; k2 <= 12; ++k2) {
     cd q[8];
@@ -286,9 +284,13 @@ __device__ __forceinline__ void logmel_pair_frame(const float (&v)[200],
     }
   }
 
-  // Band-sparse mel projection (both lanes, all bands), then this lane's
-  // half of the bands through the log with the 1e-10 floor. The floor test
-  // is written so that a NaN energy stays NaN.
+}
+
+// Band-sparse mel projection of a power spectrum (both lanes, all bands),
+// then this lane's half of the bands, 64*role .. 64*role + 63, through the
+// log with the 1e-10 floor. The floor test is written so that a NaN energy
+// stays NaN.
+__device__ __forceinline__ void pair_logmel(const float (&P)[201], int role, float (&out)[64]) {
   float E[128];
 #pragma unroll
   for (int m = 0; m < 128; ++m) {

@@ -2,13 +2,15 @@
 //
 // logmel_tiles_kernel: the offline hot path over a packed ragged batch.
 //   The flattened frame space [0, total_frames) is cut into tiles of 32
-//   consecutive frames, one wavefront per tile, one frame per lane pair
-//   (role 0: even samples, role 1: odd samples; see logmel_frame.h). A tile
-//   may straddle clips: each pair finds its clip from the int64 frame
-//   offsets. A tile inside one clip reads its 5360-sample span once,
-//   coalesced, and shares it through LDS; a tile across clips lets each lane
-//   gather its own 200 samples (the caches serve the overlap). The pair's
-//   transform runs in registers and each lane writes its 64 bands once.
+//   consecutive frames, one frame per lane pair (role 0: even samples, role
+//   1: odd samples; see logmel_frame.h). A persistent grid of one wavefront
+//   per SIMD walks the tiles; a wavefront locates and loads its next tile
+//   while it finishes the current one. A tile may straddle clips: each pair
+//   finds its clip from the int64 frame offsets. A tile inside one clip reads
+//   its 5360-sample span once, coalesced, and shares it through LDS; a tile
+//   across clips lets each lane gather its own 200 samples (the caches serve
+//   the overlap). The pair's transform runs in registers and each lane
+//   writes its 64 bands once.
 //
 // logmel_stream_prep_kernel: the streaming push, step 1. Moves each stream's
 //   carry (the samples of its next, not yet complete frame) to sit right
@@ -40,6 +42,7 @@ static constexpr int kSpan = (kTile - 1) * 160 + 400;
 static constexpr int kSpanGroups = kSpan / 4;
 static constexpr int kParityLen = 2812;   // last element 2679 sits at 2811
 static constexpr int kOddBase = 2832;     // odd sequence after the even one
+static_assert(kTabPadFloats >= kSpan, "the plan's pad must cover a span");
 
 // 16 bytes from a 4-byte aligned address (global memory allows this on the
 // HSA target).
@@ -58,26 +61,25 @@ __device__ __forceinline__ int64_t upper_bound_i64(const int64_t* __restrict__ a
   return lo;
 }
 
-extern "C" __global__ void __attribute__((amdgpu_flat_work_group_size(64, 64),
-                                          amdgpu_waves_per_eu(1, 1)))
-logmel_tiles_kernel(const float* __restrict__ samples,
-                    const int64_t* __restrict__ seg_start,   // [n_clips] first sample of clip
-                    const int64_t* __restrict__ seg_end,     // [n_clips] one past its last
-                    const int64_t* __restrict__ frame_off,   // [n_clips + 1]
-                    int64_t n_clips, int64_t total_frames,
-                    float* __restrict__ out,                 // [total_frames][128]
-                    int64_t first_tile,                      // tile index of blockIdx.x == 0
-                    const double* __restrict__ tables)       // plan tables: window, rotation
-{
-  __shared__ float4 span_lds[(kOddBase + kParityLen + 3) / 4];
-  const int lane = threadIdx.x;
-  __builtin_assume(lane < kWaveLanes);
-  const int role = lane & 1;
+// Where a tile's frames come from. Per lane: the frame (g), whether it is
+// inside the batch (in_range) and computable (valid), its first sample (s).
+// Per wavefront: whether all 32 frames lie in one clip (fast), in which case
+// the tile's span starts at sample s0.
+struct TileSrc {
+  int64_t g, s, s0;
+  bool in_range, valid, fast;
+};
 
-  const int64_t g0 = (first_tile + (int64_t)blockIdx.x) * kTile;
-  const int64_t g = g0 + (lane >> 1);
-  const bool in_range = g < total_frames;
-  const int64_t gq = in_range ? g : total_frames - 1;   // lookup key for idle lanes
+__device__ __forceinline__ TileSrc locate_tile(int64_t tile, int lane,
+                                               const int64_t* __restrict__ seg_start,
+                                               const int64_t* __restrict__ seg_end,
+                                               const int64_t* __restrict__ frame_off,
+                                               int64_t n_clips, int64_t total_frames) {
+  TileSrc t;
+  const int64_t g0 = tile * kTile;
+  t.g = g0 + (lane >> 1);
+  t.in_range = t.g < total_frames;
+  const int64_t gq = t.in_range ? t.g : total_frames - 1;   // lookup key for idle lanes
 
   // Clip of the tile's first frame (wave-uniform): the last c with
   // frame_off[c] <= g0, by a 64-ary search (one load per lane and one ballot
@@ -125,76 +127,138 @@ logmel_tiles_kernel(const float* __restrict__ samples,
     se_c = __shfl(SE, j);
   }
   const int64_t f = gq - fo_c;
-  const int64_t s = ss_c + 160 * f;
+  t.s = ss_c + 160 * f;
   // A frame is only computed if all its 400 samples lie inside its clip.
-  const bool valid = in_range && f >= 0 && (s + 400 <= se_c);
+  t.valid = t.in_range && f >= 0 && (t.s + 400 <= se_c);
+  t.fast = __all(t.valid && c == __shfl(c, 0));
+  t.s0 = __shfl(t.s, 0);
+  return t;
+}
 
-  // This lane's 200 samples: x[s + 2m] for role 0, x[s + 399 - 2m] for role 1.
-  float v[200];
-  const bool same_clip = c == __shfl(c, 0);
-  if (__all(valid && same_clip)) {
-    // All 32 frames lie in one clip: the wavefront reads the tile's sample
-    // span once with coalesced 16-byte loads, splits it by parity into LDS,
-    // and each lane reads its frame's 200 values back from there.
-    const float* src = samples + __shfl(s, 0);
-    float* lds = reinterpret_cast<float*>(span_lds);
+// The span of a tile inside one clip: 16-byte groups lane + 64 i; lanes past
+// the span's end repeat its last group, so every load is issued without a
+// branch.
+static constexpr int kSpanRegs = (kSpanGroups + kWaveLanes - 1) / kWaveLanes;
+
+__device__ __forceinline__ void load_span(const float* __restrict__ src, int lane,
+                                          f4u (&span)[kSpanRegs]) {
 #pragma unroll
-    for (int i = 0; i < (kSpanGroups + kWaveLanes - 1) / kWaveLanes; ++i) {
-      // Lanes past the span's end repeat its last group (same data, same
-      // place), so every load is issued without a branch.
-      const int j = min(lane + kWaveLanes * i, kSpanGroups - 1);
-      const f4u t = *reinterpret_cast<const f4u*>(src + 4 * j);
-      // even values 2j, 2j + 1; reversed odd values 2678 - 2j (sample
-      // 4j + 3) and 2679 - 2j (sample 4j + 1)
-      const int e = 2 * j + 4 * (j / 40);
-      const int o = kOddBase + (kSpan / 2 - 2 - 2 * j) + 4 * ((kSpanGroups - 1 - j) / 40);
-      *reinterpret_cast<float2*>(lds + e) = make_float2(t.x, t.z);
-      *reinterpret_cast<float2*>(lds + o) = make_float2(t.w, t.y);
-    }
-    __syncthreads();
-    const int fl = lane >> 1;
-    const float4* a = reinterpret_cast<const float4*>(lds + (role ? kOddBase + 84 * (kTile - 1 - fl)
-                                                                  : 84 * fl));
-#pragma unroll
-    for (int q = 0; q < 50; ++q) {
-      const float4 t = a[q + q / 20];
-      v[4 * q] = t.x;
-      v[4 * q + 1] = t.y;
-      v[4 * q + 2] = t.z;
-      v[4 * q + 3] = t.w;
-    }
-  } else if (valid) {
-    // Frames of several clips (or the batch's last, partial tile): each lane
-    // gathers its own 200 samples; the caches serve the overlap.
-    const float* p = samples + s + (role ? 399 : 0);
-    const int64_t step = role ? -2 : 2;
-#pragma unroll
-    for (int m = 0; m < 200; ++m) {
-      v[m] = *p;
-      p += step;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 200; ++i) v[i] = 0.0f;
+  for (int i = 0; i < kSpanRegs; ++i) {
+    const int j = min(lane + kWaveLanes * i, kSpanGroups - 1);
+    span[i] = *reinterpret_cast<const f4u*>(src + 4 * j);
   }
-#pragma unroll
-  for (int i = 0; i < 200; ++i) fence(v[i]);
+}
 
-  float o[64];
-  logmel_pair_frame(v, tables + kTabWindow, tables + kTabRot800, role ? -1.0 : 1.0, role, o);
+extern "C" __global__ void __attribute__((amdgpu_flat_work_group_size(64, 64),
+                                          amdgpu_waves_per_eu(1, 1)))
+logmel_tiles_kernel(const float* __restrict__ samples,
+                    const int64_t* __restrict__ seg_start,   // [n_clips] first sample of clip
+                    const int64_t* __restrict__ seg_end,     // [n_clips] one past its last
+                    const int64_t* __restrict__ frame_off,   // [n_clips + 1]
+                    int64_t n_clips, int64_t total_frames,
+                    float* __restrict__ out,                 // [total_frames][128]
+                    const double* __restrict__ tables)       // plan tables: window, rotation, pad
+{
+  const float* span_pad = reinterpret_cast<const float*>(tables + kTabDoubles);
+  __shared__ float4 span_lds[(kOddBase + kParityLen + 3) / 4];
+  float* lds = reinterpret_cast<float*>(span_lds);
+  const int lane = threadIdx.x;
+  __builtin_assume(lane < kWaveLanes);
+  const int role = lane & 1;
+  const int fl = lane >> 1;
+  const int64_t n_tiles = (total_frames + kTile - 1) / kTile;
 
-  if (in_range) {
-    float4* dst = reinterpret_cast<float4*>(out + g * 128 + 64 * role);
-    if (valid) {
+  // Each wavefront takes tiles blockIdx.x, + gridDim.x, ... While it computes
+  // one tile it locates the next and loads that tile's span into registers
+  // (between the transform and the filterbank, where the fewest registers
+  // are live), so the loads' latency hides behind the filterbank and the log.
+  int64_t tile = blockIdx.x;
+  if (tile >= n_tiles) return;
+  TileSrc cur = locate_tile(tile, lane, seg_start, seg_end, frame_off, n_clips, total_frames);
+  f4u span[kSpanRegs];
+  if (cur.fast) load_span(samples + cur.s0, lane, span);
+
+  while (true) {
+    // Lane-derived LDS addresses are formed inside the loop: hoisted out of
+    // it they would stay live across the transform.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    // This lane's 200 samples: x[s + 2m] for role 0, x[s + 399 - 2m] for role 1.
+    float v[200];
+    if (cur.fast) {
+      // Split the span by parity into LDS (layout above), then read back this
+      // lane's 200 values.
 #pragma unroll
-      for (int i = 0; i < 16; ++i) dst[i] = make_float4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+      for (int i = 0; i < kSpanRegs; ++i) {
+        const int j = min(ln + kWaveLanes * i, kSpanGroups - 1);
+        // even values 2j, 2j + 1; reversed odd values 2678 - 2j (sample
+        // 4j + 3) and 2679 - 2j (sample 4j + 1)
+        const int e = 2 * j + 4 * (j / 40);
+        const int o = kOddBase + (kSpan / 2 - 2 - 2 * j) + 4 * ((kSpanGroups - 1 - j) / 40);
+        *reinterpret_cast<float2*>(lds + e) = make_float2(span[i].x, span[i].z);
+        *reinterpret_cast<float2*>(lds + o) = make_float2(span[i].w, span[i].y);
+      }
+      __syncthreads();
+      const float4* a = reinterpret_cast<const float4*>(
+          lds + ((ln & 1) ? kOddBase + 84 * (kTile - 1 - (ln >> 1)) : 84 * (ln >> 1)));
+#pragma unroll
+      for (int q = 0; q < 50; ++q) {
+        const float4 t = a[q + q / 20];
+        v[4 * q] = t.x;
+        v[4 * q + 1] = t.y;
+        v[4 * q + 2] = t.z;
+        v[4 * q + 3] = t.w;
+      }
+    } else if (cur.valid) {
+      // Frames of several clips (or the batch's last, partial tile): each
+      // lane gathers its own 200 samples; the caches serve the overlap.
+      const float* p = samples + cur.s + (role ? 399 : 0);
+      const int64_t step = role ? -2 : 2;
+#pragma unroll
+      for (int m = 0; m < 200; ++m) {
+        v[m] = *p;
+        p += step;
+      }
     } else {
-      // Offsets that promise a frame the clip cannot hold: a loud row, not a
-      // silent truncation.
-      const float qnan = __builtin_nanf("");
 #pragma unroll
-      for (int i = 0; i < 16; ++i) dst[i] = make_float4(qnan, qnan, qnan, qnan);
+      for (int i = 0; i < 200; ++i) v[i] = 0.0f;
     }
+#pragma unroll
+    for (int i = 0; i < 200; ++i) fence(v[i]);
+    // Only a wave-wide mask crosses the transform (no per-lane registers).
+    const uint64_t valid_mask = __ballot(cur.valid);
+
+    float P[201];
+    pair_power(v, tables + kTabWindow, tables + kTabRot800, role ? -1.0 : 1.0, P);
+
+    const int64_t next = tile + gridDim.x;
+    const bool more = next < n_tiles;
+    TileSrc nxt = cur;
+    if (more) nxt = locate_tile(next, lane, seg_start, seg_end, frame_off, n_clips, total_frames);
+    // Loaded on every path (from the plan's zero pad when there is no span
+    // to fetch), so that no register merge waits for the loads here.
+    load_span(more && nxt.fast ? samples + nxt.s0 : span_pad, lane, span);
+
+    float o[64];
+    pair_logmel(P, role, o);
+    const int64_t g = tile * kTile + fl;
+    if (g < total_frames) {
+      float4* dst = reinterpret_cast<float4*>(out + g * 128 + 64 * role);
+      if ((valid_mask >> lane) & 1) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          dst[i] = make_float4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+      } else {
+        // Offsets that promise a frame the clip cannot hold: a loud row, not
+        // a silent truncation.
+        const float qnan = __builtin_nanf("");
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dst[i] = make_float4(qnan, qnan, qnan, qnan);
+      }
+    }
+    if (!more) break;
+    tile = next;
+    cur = nxt;
   }
 }
 
@@ -239,20 +303,16 @@ logmel_stream_prep_kernel(float* __restrict__ ws, int64_t row_stride,
 hipError_t logmel_launch_tiles(const double* tables, const float* samples,
                                const int64_t* seg_start, const int64_t* seg_end,
                                const int64_t* frame_off, int64_t n_clips, int64_t total_frames,
-                               float* out, hipStream_t stream) {
+                               float* out, int resident_waves, hipStream_t stream) {
   if (total_frames <= 0) return hipSuccess;
   const int64_t tiles = (total_frames + logmel::kTile - 1) / logmel::kTile;
-  // A launch covers at most 2^25 workgroups (2^31 work-items).
-  const int64_t chunk = (int64_t)1 << 25;
-  for (int64_t t0 = 0; t0 < tiles; t0 += chunk) {
-    const int64_t n = tiles - t0 < chunk ? tiles - t0 : chunk;
-    hipLaunchKernelGGL(logmel::logmel_tiles_kernel, dim3((unsigned)n), dim3(logmel::kWaveLanes), 0,
-                       stream, samples, seg_start, seg_end, frame_off, n_clips, total_frames,
-                       out, t0, tables);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
+  // One wavefront per SIMD is resident at a time; the grid is that many
+  // wavefronts (fewer for small batches) and each walks its share of tiles.
+  const int64_t grid = tiles < resident_waves ? tiles : resident_waves;
+  hipLaunchKernelGGL(logmel::logmel_tiles_kernel, dim3((unsigned)grid), dim3(logmel::kWaveLanes),
+                     0, stream, samples, seg_start, seg_end, frame_off, n_clips, total_frames, out,
+                     tables);
+  return hipGetLastError();
 }
 
 hipError_t logmel_launch_stream_prep(float* ws, int64_t row_stride, const float* fresh,

@@ -8,14 +8,18 @@
 // points in the order the transform consumes them (both lanes of a pair use
 // it), then cos/sin of 2 pi k / 800 interleaved, in the order the
 // transform's 8-point DFTs produce bins ([k2][k1], 13 x 8 pairs).
+// After the doubles, kTabPadFloats zero floats: a readable stand-in for a
+// tile's 5360-sample span.
 static constexpr int kTabWindow = 0;
 static constexpr int kTabRot800 = 200;
 static constexpr int kTabDoubles = 408;
+static constexpr int kTabPadFloats = 5360;
+static constexpr size_t kTabBytes = 8 * kTabDoubles + 4 * kTabPadFloats;
 
 hipError_t logmel_launch_tiles(const double* tables, const float* samples,
                                const int64_t* seg_start, const int64_t* seg_end,
                                const int64_t* frame_off, int64_t n_clips, int64_t total_frames,
-                               float* out, hipStream_t stream);
+                               float* out, int resident_waves, hipStream_t stream);
 
 hipError_t logmel_launch_stream_prep(float* ws, int64_t row_stride, const float* fresh,
                                      const int64_t* meta, int64_t n_streams,
