@@ -29,12 +29,13 @@
 //       |X[k]|       = |u + conj(v)|,
 //       |X[200 - k]| = |u - conj(v)|.
 //     Each role forms its own rotation (the same W800^k for both), swaps it
-//     with its partner (DPP) and forms one of the two powers; a second DPP
-//     broadcast gives both lanes the same 201 powers, and both run the same
-//     filterbank; each logs and stores one half of the 128 bands.
+//     with its partner (DPP) and forms one of the two powers, so each lane
+//     holds one half of the spectrum; the filterbank runs on the halves (see
+//     pair_logmel) and each lane logs and stores one half of the 128 bands.
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <utility>
 
 #include "logmel_tables.h"
 
@@ -135,15 +136,33 @@ __device__ __forceinline__ void dft5_real(double x0, double x1, double x2, doubl
   y2 = {a2, -b2};
 }
 
-// Forward 25-point DFT of real input y[25] (5 x 5, n = na + 5 nb,
-// k = 5 ka + kb), giving Z[0..12] (Z[0] real; the rest by Hermitian symmetry).
-// Only kb = 0, 1, 2 of the first stage are formed: kb = 3, 4 are conjugates.
-__device__ __forceinline__ void dft25_real(const double (&y)[25], cd (&Z)[13]) {
+// dft5_real of the windowed input w[i] * v[i], the window products folded
+// into the first sums and differences (x1 +- x4 = fma(w1, v1, +-w4 v4)).
+__device__ __forceinline__ void dft5_real_w(double w0, double v0, double w1, double v1, double w2,
+                                            double v2, double w3, double v3, double w4, double v4,
+                                            double& y0, cd& y1, cd& y2) {
+  const double x0 = w0 * v0, p4 = w4 * v4, p3 = w3 * v3;
+  const double t1 = __builtin_fma(w1, v1, p4), t3 = __builtin_fma(w1, v1, -p4);
+  const double t2 = __builtin_fma(w2, v2, p3), t4 = __builtin_fma(w2, v2, -p3);
+  y0 = x0 + t1 + t2;
+  const double a1 = x0 + kDC51 * t1 + kDC52 * t2, a2 = x0 + kDC52 * t1 + kDC51 * t2;
+  const double b1 = kDS51 * t3 + kDS52 * t4, b2 = kDS52 * t3 - kDS51 * t4;
+  y1 = {a1, -b1};
+  y2 = {a2, -b2};
+}
+
+// Forward 25-point DFT of the real windowed input w[n] * v[n] (5 x 5,
+// n = na + 5 nb, k = 5 ka + kb), giving Z[0..12] (Z[0] real; the rest by
+// Hermitian symmetry). Only kb = 0, 1, 2 of the first stage are formed:
+// kb = 3, 4 are conjugates.
+__device__ __forceinline__ void dft25_real(const double (&w)[25], const double (&v)[25],
+                                           cd (&Z)[13]) {
   double r0[5];
   cd r1[5], r2[5];
 #pragma unroll
   for (int na = 0; na < 5; ++na)
-    dft5_real(y[na], y[na + 5], y[na + 10], y[na + 15], y[na + 20], r0[na], r1[na], r2[na]);
+    dft5_real_w(w[na], v[na], w[na + 5], v[na + 5], w[na + 10], v[na + 10], w[na + 15],
+                v[na + 15], w[na + 20], v[na + 20], r0[na], r1[na], r2[na]);
 #pragma unroll
   for (int na = 1; na < 5; ++na) {
     r1[na] = c_twiddle(r1[na], kDCos25[na], kDSin25[na]);
@@ -193,10 +212,11 @@ __device__ __forceinline__ float pair_from(float v, int src) {
 //   win      w[2m], m = (25 n1 + 8 n2) mod 200, in [n1][n2] order (uniform)
 //   rot      cos, sin of 2 pi kap / 800 for the bins in [k2][k1] order (uniform)
 //   sgn      +1.0 for role 0, -1.0 for role 1
-//   P[201]   the frame's power spectrum |X[k]|^2 (the same in both lanes)
+//   own[101] this lane's half of the power spectrum: own[kap] = |X[kap]|^2
+//            for role 0 and |X[200 - kap]|^2 for role 1, kap = 1..100
 __device__ __forceinline__ void pair_power(const float (&v)[200], const double* __restrict__ win,
                                            const double* __restrict__ rot, double sgn,
-                                           float (&P)[201]) {
+                                           float (&P)[101]) {
   // Stage 1: 8 real 25-point DFTs over n2, two rows n1 per scheduling region
   // (two independent transforms give the scheduler work to overlap).
   // A[n1][k2], k2 = 0..12 (k2 = 0 is real: its .im is an exact 0).
@@ -215,11 +235,14 @@ __device__ __forceinline__ void pair_power(const float (&v)[200], const double* 
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int n1 = 2 * p + h;
-      double y[25];
+      double wv[25], y[25];
 #pragma unroll
-      for (int n2 = 0; n2 < 25; ++n2) y[n2] = win[25 * n1 + n2] * (double)xr[h][n2];
+      for (int n2 = 0; n2 < 25; ++n2) {
+        wv[n2] = win[25 * n1 + n2];
+        y[n2] = (double)xr[h][n2];
+      }
       cd Z[13];
-      dft25_real(y, Z);
+      dft25_real(wv, y, Z);
 #pragma unroll
       for (int k = 0; k <= 12; ++k) A[n1][k] = Z[k];
     }
@@ -234,8 +257,9 @@ __device__ __forceinline__ void pair_power(const float (&v)[200], const double* 
 
   // Stage 2 and the combine: for each k2, an 8-point DFT over n1 gives this
   // role's spectrum R at k = pfa_k(k1, k2) (k > 100 through conjugation);
-  // rotate, swap with the partner, and form the powers of bins k and 200 - k.
-  P[0] = P[200] = 0.0f;   // no filter reaches bins 0 and 200
+  // rotate, swap with the partner, and form this role's power of bin k or
+  // bin 200 - k.
+  P[0] = 0.0f;   // no filter reaches bins 0 and 200
 #pragma unroll
   for (int k2 = 0; k2 <= 12; ++k2) {
     cd q[8];
@@ -266,11 +290,7 @@ __device__ __forceinline__ void pair_power(const float (&v)[200], const double* 
       const cd w = {pair_swap(u.re), pair_swap(u.im)};
       // role 0: |u + conj(w)|^2 = bin kap; role 1: |u - conj(w)|^2 = bin 200 - kap
       const double are = w.re * sgn + u.re, aim = u.im - w.im * sgn;
-      const float own = (float)(are * are + aim * aim);
-      // Both lanes take bin kap from the even lane and bin 200 - kap from the
-      // odd one (DPP quad_perm [0,0,2,2] and [1,1,3,3]).
-      P[kap] = pair_from(own, 0);
-      if (kap != 100) P[200 - kap] = pair_from(own, 1);
+      P[kap] = (float)(are * are + aim * aim);
     }
     // one scheduling region per column
 #pragma unroll
@@ -280,30 +300,62 @@ __device__ __forceinline__ void pair_power(const float (&v)[200], const double* 
       const int kap = k <= 100 ? k : 200 - k;
       if (kap == 0) continue;
       fence(P[kap]);
-      if (kap != 100) fence(P[200 - kap]);
     }
   }
 
 }
 
-// Band-sparse mel projection of a power spectrum (both lanes, all bands),
-// then this lane's half of the bands, 64*role .. 64*role + 63, through the
-// log with the 1e-10 floor. The floor test is written so that a NaN energy
-// stays NaN.
-__device__ __forceinline__ void pair_logmel(const float (&P)[201], int role, float (&out)[64]) {
-  float E[128];
+// Band-sparse mel projection and log. Each lane holds only its own half of
+// the spectrum (own[kap]: bin kap in role 0, bin 200 - kap in role 1), and
+// both run the same code: a band whose bins all lie below 100 is summed over
+// own[bin] (right in role 0), a band whose bins all lie above 100 over
+// own[200 - bin] (right in role 1), and the bands around bin 100 as the two
+// partial sums. Role 0 logs bands 0..63, all below bin 100; role 1 logs bands
+// 64..127 and takes the energies that only role 0 holds from its partner
+// (DPP). The log has the 1e-10 floor; the floor test keeps a NaN energy NaN.
+__host__ __device__ constexpr int mel_side(int m) {   // 0: bins < 100, 1: bins > 100, 2: both
+  return kMelCount[m] == 0 ? 0
+       : (kMelStart[m] + kMelCount[m] - 1 < 100 ? 0 : (kMelStart[m] > 100 ? 1 : 2));
+}
+
+// Energy of band m from this lane's half spectrum (bins in order, one
+// instance per band so that every index and weight is a constant).
+template <int m>
+__device__ __forceinline__ float mel_band(const float (&own)[101]) {
+  constexpr int n = kMelCount[m], k0 = kMelStart[m], side = mel_side(m);
+  if constexpr (n == 0) {
+    return 0.0f;
+  } else {
+    float lo = 0.0f, hi = 0.0f;
 #pragma unroll
-  for (int m = 0; m < 128; ++m) {
-    if (kMelCount[m] == 0) {
-      E[m] = 0.0f;
-      continue;
+    for (int j = 0; j < n; ++j) {
+      const int bin = k0 + j;
+      if (bin <= 100) {
+        lo = (bin == k0) ? kMelW[m][j] * own[bin] : lo + kMelW[m][j] * own[bin];
+      } else {
+        hi = (bin == k0 || bin == 101) ? kMelW[m][j] * own[200 - bin]
+                                       : hi + kMelW[m][j] * own[200 - bin];
+      }
     }
-    float e = kMelW[m][0] * P[kMelStart[m]];
-#pragma unroll
-    for (int j = 1; j < kMelMaxBins; ++j)
-      if (j < kMelCount[m]) e += kMelW[m][j] * P[kMelStart[m] + j];
-    E[m] = e;
+    if constexpr (side == 0) {
+      return m < 64 ? lo : pair_from(lo, 0);
+    } else if constexpr (side == 1) {
+      return hi;
+    } else {
+      return pair_from(lo, 0) + hi;
+    }
   }
+}
+
+template <int... M>
+__device__ __forceinline__ void mel_bands(const float (&own)[101], float (&E)[128],
+                                          std::integer_sequence<int, M...>) {
+  ((E[M] = mel_band<M>(own)), ...);
+}
+
+__device__ __forceinline__ void pair_logmel(const float (&own)[101], int role, float (&out)[64]) {
+  float E[128];
+  mel_bands(own, E, std::make_integer_sequence<int, 128>{});
 #pragma unroll
   for (int i = 0; i < 64; ++i) {
     float e = role ? E[64 + i] : E[i];

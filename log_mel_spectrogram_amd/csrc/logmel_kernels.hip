@@ -228,7 +228,7 @@ logmel_tiles_kernel(const float* __restrict__ samples,
     // Only a wave-wide mask crosses the transform (no per-lane registers).
     const uint64_t valid_mask = __ballot(cur.valid);
 
-    float P[201];
+    float P[101];
     pair_power(v, tables + kTabWindow, tables + kTabRot800, role ? -1.0 : 1.0, P);
 
     const int64_t next = tile + gridDim.x;
