@@ -35,6 +35,16 @@ The output layout is frame-major [frames, 128] (page 1, the shape table after
 step 5). The streaming result is, by definition, this offline result on the
 concatenated stream.
 
+30-s chunks for the encoder (page 1, the preprocessor-config list after
+§2.3: chunk_length 30 s gives 3000 frames; page 1, §4 point 1: the encoder
+input has the fixed shape [B, 3000, 128], and point 4: every input is padded
+to 3000 frames; page 3, §二 stage 1: the front end cuts at 30 s). The pages do
+not say which frames fall into which chunk, nor the pad value. Reading: chunk
+j of a clip holds the clip's own frames 3000 j .. 3000 j + 2999 (the frames
+that start in seconds 30 j .. 30 j + 30), so chunking never changes a frame;
+the rows of the last chunk past the clip's last frame hold ln(1e-10), the
+value the recipe gives silence; a clip with no frame has no chunk.
+
 Everything here is fp64. The fp32 samples are upcast exactly.
 """
 
@@ -50,6 +60,7 @@ N_MELS = 128
 F_MIN = 0.0
 F_MAX = 8000.0
 LOG_FLOOR = 1e-10
+CHUNK_FRAMES = 3000   # page 1, preprocessor-config list: 30 s -> 3000 frames
 
 
 def num_frames(n_samples: int) -> int:
@@ -205,3 +216,46 @@ def logmel_selected(samples: np.ndarray, sample_offsets, rows):
     frames = np.stack([np.asarray(samples[s:s + N_FFT], dtype=np.float64)
                        for s in start]) if rows.size else np.zeros((0, N_FFT))
     return logmel_frames(frames)
+
+
+def num_chunks(n_frames: int) -> int:
+    """30-s chunks of a clip with ``n_frames`` frames: ceil(F / 3000) (see the
+    chunking reading in the module docstring)."""
+    return -(-int(n_frames) // CHUNK_FRAMES)
+
+
+def chunk_offsets(sample_offsets) -> np.ndarray:
+    """Exclusive prefix sum of per-clip chunk counts, int64, length n_clips+1."""
+    so = np.asarray(sample_offsets, dtype=np.int64).reshape(-1)
+    counts = [num_chunks(num_frames(int(so[i + 1] - so[i]))) for i in range(so.size - 1)]
+    return np.concatenate([[0], np.cumsum(np.asarray(counts, dtype=np.int64))]).astype(np.int64)
+
+
+def chunk_frames(sample_offsets) -> np.ndarray:
+    """Frames of the clip held by each chunk (the rest of its 3000 rows are
+    padding), int64, one entry per chunk in order."""
+    so = np.asarray(sample_offsets, dtype=np.int64).reshape(-1)
+    out = []
+    for i in range(so.size - 1):
+        F = num_frames(int(so[i + 1] - so[i]))
+        for j in range(num_chunks(F)):
+            out.append(min(CHUNK_FRAMES, F - CHUNK_FRAMES * j))
+    return np.asarray(out, dtype=np.int64)
+
+
+def logmel_chunked(samples: np.ndarray, sample_offsets):
+    """Encoder input [chunks, 3000, 128] fp64 of a packed batch: each clip's
+    frames in order, cut every 3000 frames, the last chunk padded with
+    ln(1e-10). Returns (chunks, chunk_offsets)."""
+    so = np.asarray(sample_offsets, dtype=np.int64).reshape(-1)
+    co = chunk_offsets(so)
+    out = np.full((int(co[-1]), CHUNK_FRAMES, N_MELS), np.log(LOG_FLOOR), dtype=np.float64)
+    for i in range(so.size - 1):
+        F = num_frames(int(so[i + 1] - so[i]))
+        if F == 0:
+            continue
+        Li, _ = logmel_clip(samples[so[i]:so[i + 1]])
+        for j in range(int(co[i + 1] - co[i])):
+            rows = Li[CHUNK_FRAMES * j:CHUNK_FRAMES * (j + 1)]
+            out[co[i] + j, :rows.shape[0]] = rows
+    return out, co

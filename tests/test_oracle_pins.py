@@ -344,3 +344,71 @@ def test_packed_equals_per_clip():
     rows = np.arange(fo[-1])
     Ls, _ = O.logmel_selected(s, so, rows)
     assert np.allclose(Ls, L, atol=1e-12, rtol=0)
+
+
+# ------------------------------------------------------------ 30-s chunks
+
+def _brute_chunk_count(F):
+    """Count chunk starts 0, 3000, 6000, ... that hold at least one frame."""
+    c, start = 0, 0
+    while start < F:
+        c += 1
+        start += 3000
+    return c
+
+
+def test_chunk_page_facts(golden_dir):
+    facts = json.load(open(os.path.join(golden_dir, "page_facts.json")))
+    ch = facts["chunk_30s"]
+    assert O.CHUNK_FRAMES == ch["frames"]
+    # 3000 frames at the 10 ms hop are exactly the 30 s of the chunk
+    assert O.CHUNK_FRAMES * O.HOP == ch["seconds"] * O.SAMPLE_RATE
+    shape = facts["encoder_input_shape"]["shape"]
+    assert shape[1:] == [O.CHUNK_FRAMES, O.N_MELS]
+
+
+def test_chunk_counts_brute():
+    for F in list(range(0, 7000)) + [521_998, 2_998_000]:
+        assert O.num_chunks(F) == _brute_chunk_count(F), F
+    # a 30 s clip has 2998 frames: one chunk, two rows of padding
+    assert O.num_chunks(O.num_frames(480000)) == 1
+    # 87 minutes (the longest input page 3 accepts) -> 174 chunks
+    assert O.num_chunks(O.num_frames(87 * 60 * 16000)) == 174
+
+
+def test_chunk_offsets_and_frames():
+    lens = [0, 399, 400, 480000, 480160, 960000, 480000 + 160 * 2, 16000]
+    so = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    co = O.chunk_offsets(so)
+    cf = O.chunk_frames(so)
+    assert co.dtype == np.int64 and co[0] == 0
+    F = [_brute_frame_count(n) for n in lens]
+    assert F == [0, 0, 1, 2998, 2999, 5998, 3000, 98]
+    assert list(np.diff(co)) == [_brute_chunk_count(f) for f in F]
+    assert list(cf) == [1, 2998, 2999, 3000, 2998, 3000, 98]
+    # the chunks of a clip hold its frames exactly once
+    for i, f in enumerate(F):
+        assert sum(cf[co[i]:co[i + 1]]) == f
+
+
+def test_chunked_layout():
+    rng = np.random.default_rng(5)
+    lens = [0, 3000 * 160 + 240, 399, 3000 * 160 + 400, 6000 * 160 + 240 + 37, 12345]
+    x = (0.3 * rng.standard_normal(sum(lens))).astype(np.float32)
+    so = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    chunks, co = O.logmel_chunked(x, so)
+    L, _, fo = O.logmel_packed(x, so)
+    floor = math.log(1e-10)
+    assert chunks.shape == (int(co[-1]), 3000, 128)
+    for i in range(len(lens)):
+        F = int(fo[i + 1] - fo[i])
+        for j in range(int(co[i + 1] - co[i])):
+            n = min(3000, F - 3000 * j)
+            # frame 3000 j + r of clip i sits in row r of its chunk j
+            np.testing.assert_array_equal(chunks[co[i] + j, :n], L[fo[i] + 3000 * j: fo[i] + 3000 * j + n])
+            assert np.all(chunks[co[i] + j, n:] == floor)
+    # a 3000-frame clip fills its chunk with no padding; one more frame opens
+    # a second chunk holding a single frame
+    assert [O.num_frames(n) for n in lens] == [0, 3000, 0, 3001, 6000, 75]
+    assert list(np.diff(co)) == [0, 1, 0, 2, 2, 1]
+    assert O.chunk_frames(so).tolist() == [3000, 3000, 1, 3000, 3000, 75]
