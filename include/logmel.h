@@ -107,6 +107,44 @@ int logmel_compute(const logmel_plan* plan, const float* d_samples,
                    int64_t n_clips, int64_t total_frames, float* d_out,
                    void* hip_stream);
 
+/* 30-s chunks for the encoder input [chunks][3000][128] (page 1: the
+ * preprocessor-config list after §2.3 gives chunk_length 30 s -> 3000
+ * frames, and §4 says the encoder takes a fixed [B, 3000, 128] with every
+ * input padded to 3000 frames; page 3, §二 stage 1: the front end cuts at
+ * 30 s). Chunk j of a clip holds the clip's frames 3000 j .. 3000 j + 2999
+ * (the frames that start in seconds 30 j .. 30 j + 30), so a chunked frame
+ * is the offline frame bit for bit; the rows of a clip's last chunk past its
+ * last frame hold ln(1e-10), bit for bit the value of a silent frame; a clip
+ * with no frame has no chunk. */
+#define LOGMEL_CHUNK_FRAMES 3000
+
+/* Host helper. Writes chunk_offsets_host[0..n_clips] = exclusive prefix sum
+ * of the clips' chunk counts ceil(F_i / 3000): clip i's chunks are
+ * [chunk_offsets[i], chunk_offsets[i+1]). Same errors as
+ * logmel_frame_offsets. */
+int logmel_chunk_offsets(const int64_t* sample_offsets_host, int64_t n_clips,
+                         int64_t* chunk_offsets_host);
+
+/* Host helper. Writes, for each of the total_chunks chunks in order, the
+ * number of frames it holds (1..3000; the rest of its rows are padding), for
+ * an encoder's attention mask or ragged-tail trimming. total_chunks must be
+ * what logmel_chunk_offsets gives (INVALID_ARGUMENT otherwise). */
+int logmel_chunk_frames(const int64_t* sample_offsets_host, int64_t n_clips,
+                        int64_t total_chunks, int64_t* chunk_frames_host);
+
+/* logmel_compute into the chunk layout.
+ *   d_chunk_offsets    int64[n_clips + 1], what logmel_chunk_offsets returns
+ *   total_chunks       d_chunk_offsets[n_clips]
+ *   d_out              fp32 [total_chunks][3000][128], row-major; frame f of
+ *                      clip i is row d_chunk_offsets[i] * 3000 + f
+ * Everything else as logmel_compute (LOGMEL_VALIDATE=1 also checks the chunk
+ * offsets). INPUT_TOO_LONG if total_chunks * 3000 * 128 overflows int64. */
+int logmel_compute_chunked(const logmel_plan* plan, const float* d_samples,
+                           const int64_t* d_sample_offsets, const int64_t* d_frame_offsets,
+                           const int64_t* d_chunk_offsets, int64_t n_clips,
+                           int64_t total_frames, int64_t total_chunks, float* d_out,
+                           void* hip_stream);
+
 /* Streaming (the 80 ms audio clock of the Audio8-ASR-Infinite page gives the
  * 1280-sample push). A stream object holds n_streams independent streams.
  * Each push appends new samples to every stream and emits every frame that

@@ -32,6 +32,7 @@ LOGMEL_ERR_DEVICE = -4
 LOGMEL_ERR_INPUT_TOO_LONG = -5
 
 N_MELS = 128
+CHUNK_FRAMES = 3000   # LOGMEL_CHUNK_FRAMES
 N_FFT = 400
 HOP = 160
 SAMPLE_RATE = 16000
@@ -64,6 +65,10 @@ _plan_destroy = _sig("logmel_plan_destroy", None, _p)
 _num_frames = _sig("logmel_num_frames", _i64, _i64)
 _frame_offsets = _sig("logmel_frame_offsets", ctypes.c_int, _i64p, _i64, _i64p)
 _compute = _sig("logmel_compute", ctypes.c_int, _p, _p, _p, _p, _i64, _i64, _p, _p)
+_chunk_offsets = _sig("logmel_chunk_offsets", ctypes.c_int, _i64p, _i64, _i64p)
+_chunk_frames = _sig("logmel_chunk_frames", ctypes.c_int, _i64p, _i64, _i64, _i64p)
+_compute_chunked = _sig("logmel_compute_chunked", ctypes.c_int, _p, _p, _p, _p, _p, _i64, _i64,
+                        _i64, _p, _p)
 _stream_create = _sig("logmel_stream_create", ctypes.c_int, _p, _i64, _i64, ctypes.POINTER(_p))
 _stream_destroy = _sig("logmel_stream_destroy", None, _p)
 _stream_reset = _sig("logmel_stream_reset", ctypes.c_int, _p)
@@ -77,7 +82,8 @@ _stream_set_state = _sig("logmel_stream_set_state", ctypes.c_int, _p, _p, _p)
 EXPORTED = [
     "logmel_default_config", "logmel_abi_version", "logmel_status_string",
     "logmel_plan_create", "logmel_plan_destroy", "logmel_num_frames",
-    "logmel_frame_offsets", "logmel_compute", "logmel_stream_create",
+    "logmel_frame_offsets", "logmel_compute", "logmel_chunk_offsets", "logmel_chunk_frames",
+    "logmel_compute_chunked", "logmel_stream_create",
     "logmel_stream_destroy", "logmel_stream_reset", "logmel_stream_frames_for_push",
     "logmel_stream_push", "logmel_stream_counters", "logmel_stream_state_bytes",
     "logmel_stream_get_state", "logmel_stream_set_state",
@@ -131,6 +137,27 @@ def logmel_frame_offsets(sample_offsets) -> np.ndarray:
     fo = np.zeros(so.size, dtype=np.int64)
     _check(_frame_offsets(_ptr64(so), so.size - 1, _ptr64(fo)), "logmel_frame_offsets")
     return fo
+
+
+def logmel_chunk_offsets(sample_offsets) -> np.ndarray:
+    """Exclusive prefix sum of the clips' 30-s chunk counts (int64, n_clips + 1)."""
+    so = _i64_array(sample_offsets)
+    if so.size < 1:
+        raise LogmelError(LOGMEL_ERR_INVALID_ARGUMENT, "logmel_chunk_offsets")
+    co = np.zeros(so.size, dtype=np.int64)
+    _check(_chunk_offsets(_ptr64(so), so.size - 1, _ptr64(co)), "logmel_chunk_offsets")
+    return co
+
+
+def logmel_chunk_frames(sample_offsets, total_chunks: int) -> np.ndarray:
+    """Frames held by each 30-s chunk (int64, total_chunks)."""
+    so = _i64_array(sample_offsets)
+    if so.size < 1:
+        raise LogmelError(LOGMEL_ERR_INVALID_ARGUMENT, "logmel_chunk_frames")
+    cf = np.zeros(max(int(total_chunks), 1), dtype=np.int64)
+    _check(_chunk_frames(_ptr64(so), so.size - 1, int(total_chunks), _ptr64(cf)),
+           "logmel_chunk_frames")
+    return cf[:int(total_chunks)]
 
 
 class Plan:
@@ -206,6 +233,31 @@ def logmel_compute(plan: Plan, samples, sample_offsets, frame_offsets, total_fra
                     _dev_ptr(frame_offsets, torch.int64, "frame_offsets"),
                     n_clips, int(total_frames), _dev_ptr(out, torch.float32, "out"), st),
            "logmel_compute")
+    return out
+
+
+def logmel_compute_chunked(plan: Plan, samples, sample_offsets, frame_offsets, chunk_offsets,
+                           total_frames: int, total_chunks: int, out=None, stream=None):
+    """logmel_compute into the 30-s chunk layout; returns out
+    [total_chunks, 3000, 128] (frame f of clip i at flat row
+    chunk_offsets[i] * 3000 + f, the rest of a clip's last chunk ln(1e-10))."""
+    torch = _torch()
+    n_clips = int(sample_offsets.numel()) - 1
+    if out is None:
+        out = torch.empty((int(total_chunks), CHUNK_FRAMES, N_MELS), dtype=torch.float32,
+                          device=samples.device)
+    if tuple(out.shape) != (int(total_chunks), CHUNK_FRAMES, N_MELS):
+        raise ValueError(f"out must be [{total_chunks}, {CHUNK_FRAMES}, {N_MELS}]")
+    if frame_offsets.numel() != n_clips + 1 or chunk_offsets.numel() != n_clips + 1:
+        raise ValueError("frame_offsets and chunk_offsets must have n_clips + 1 entries")
+    st = _stream_handle(stream, samples.device)
+    _check(_compute_chunked(plan.handle, _dev_ptr(samples, torch.float32, "samples"),
+                            _dev_ptr(sample_offsets, torch.int64, "sample_offsets"),
+                            _dev_ptr(frame_offsets, torch.int64, "frame_offsets"),
+                            _dev_ptr(chunk_offsets, torch.int64, "chunk_offsets"),
+                            n_clips, int(total_frames), int(total_chunks),
+                            _dev_ptr(out, torch.float32, "out"), st),
+           "logmel_compute_chunked")
     return out
 
 

@@ -17,6 +17,7 @@ namespace {
 constexpr int kNFFT = 400;
 constexpr int kHop = 160;
 constexpr int kMels = 128;
+constexpr int64_t kChunkFrames = LOGMEL_CHUNK_FRAMES;   // 30 s of 10 ms frames
 constexpr int kRing = 400;  // carry capacity in front of each workspace row
 
 struct DeviceGuard {
@@ -166,6 +167,63 @@ int logmel_frame_offsets(const int64_t* so, int64_t n_clips, int64_t* fo) {
   return LOGMEL_OK;
 }
 
+int logmel_chunk_offsets(const int64_t* so, int64_t n_clips, int64_t* co) {
+  if (!so || !co || n_clips < 0) return LOGMEL_ERR_INVALID_ARGUMENT;
+  if (so[0] != 0) return LOGMEL_ERR_INVALID_ARGUMENT;
+  for (int64_t i = 0; i < n_clips; ++i)
+    if (so[i + 1] < so[i]) return LOGMEL_ERR_INVALID_ARGUMENT;
+  int64_t acc = 0;
+  co[0] = 0;
+  for (int64_t i = 0; i < n_clips; ++i) {
+    acc += (frames_of(so[i + 1] - so[i]) + kChunkFrames - 1) / kChunkFrames;
+    co[i + 1] = acc;
+  }
+  return LOGMEL_OK;
+}
+
+int logmel_chunk_frames(const int64_t* so, int64_t n_clips, int64_t total_chunks, int64_t* cf) {
+  if (!so || !cf || n_clips < 0 || total_chunks < 0) return LOGMEL_ERR_INVALID_ARGUMENT;
+  std::vector<int64_t> co(n_clips + 1);
+  const int r = logmel_chunk_offsets(so, n_clips, co.data());
+  if (r != LOGMEL_OK) return r;
+  if (co[n_clips] != total_chunks) return LOGMEL_ERR_INVALID_ARGUMENT;
+  for (int64_t i = 0; i < n_clips; ++i) {
+    const int64_t F = frames_of(so[i + 1] - so[i]);
+    for (int64_t j = co[i]; j < co[i + 1]; ++j) {
+      const int64_t left = F - (j - co[i]) * kChunkFrames;
+      cf[j] = left < kChunkFrames ? left : kChunkFrames;
+    }
+  }
+  return LOGMEL_OK;
+}
+
+namespace {
+
+// Reads offsets back (one synchronisation) and checks them against the
+// sample offsets; for LOGMEL_VALIDATE=1.
+int validate_offsets(const int64_t* d_so, const int64_t* d_fo, const int64_t* d_co,
+                     int64_t n_clips, int64_t total_frames, int64_t total_chunks,
+                     hipStream_t st) {
+  std::vector<int64_t> so(n_clips + 1), fo(n_clips + 1), co(n_clips + 1), ref(n_clips + 1);
+  if (hipMemcpyAsync(so.data(), d_so, (n_clips + 1) * 8, hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipMemcpyAsync(fo.data(), d_fo, (n_clips + 1) * 8, hipMemcpyDeviceToHost, st) != hipSuccess ||
+      (d_co && hipMemcpyAsync(co.data(), d_co, (n_clips + 1) * 8, hipMemcpyDeviceToHost, st) !=
+                   hipSuccess) ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return LOGMEL_ERR_DEVICE;
+  if (logmel_frame_offsets(so.data(), n_clips, ref.data()) != LOGMEL_OK)
+    return LOGMEL_ERR_INVALID_ARGUMENT;
+  if (ref != fo || fo[n_clips] != total_frames) return LOGMEL_ERR_INVALID_ARGUMENT;
+  if (d_co) {
+    if (logmel_chunk_offsets(so.data(), n_clips, ref.data()) != LOGMEL_OK)
+      return LOGMEL_ERR_INVALID_ARGUMENT;
+    if (ref != co || co[n_clips] != total_chunks) return LOGMEL_ERR_INVALID_ARGUMENT;
+  }
+  return LOGMEL_OK;
+}
+
+}  // namespace
+
 int logmel_compute(const logmel_plan* plan, const float* d_samples,
                    const int64_t* d_sample_offsets, const int64_t* d_frame_offsets,
                    int64_t n_clips, int64_t total_frames, float* d_out, void* hip_stream) {
@@ -178,21 +236,45 @@ int logmel_compute(const logmel_plan* plan, const float* d_samples,
   if (!g.ok) return LOGMEL_ERR_DEVICE;
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   if (env_validate()) {
-    std::vector<int64_t> so(n_clips + 1), fo(n_clips + 1), ref(n_clips + 1);
-    if (hipMemcpyAsync(so.data(), d_sample_offsets, (n_clips + 1) * 8, hipMemcpyDeviceToHost, st) !=
-            hipSuccess ||
-        hipMemcpyAsync(fo.data(), d_frame_offsets, (n_clips + 1) * 8, hipMemcpyDeviceToHost, st) !=
-            hipSuccess ||
-        hipStreamSynchronize(st) != hipSuccess)
-      return LOGMEL_ERR_DEVICE;
-    if (logmel_frame_offsets(so.data(), n_clips, ref.data()) != LOGMEL_OK)
-      return LOGMEL_ERR_INVALID_ARGUMENT;
-    if (ref != fo || fo[n_clips] != total_frames) return LOGMEL_ERR_INVALID_ARGUMENT;
+    const int r = validate_offsets(d_sample_offsets, d_frame_offsets, nullptr, n_clips,
+                                   total_frames, 0, st);
+    if (r != LOGMEL_OK) return r;
   }
   const hipError_t e = logmel_launch_tiles(plan->tables, d_samples, d_sample_offsets,
-                                           d_sample_offsets + 1,
-                                           d_frame_offsets, n_clips, total_frames, d_out,
+                                           d_sample_offsets + 1, d_frame_offsets, n_clips,
+                                           total_frames, d_out, d_frame_offsets, 1, total_frames,
                                            plan->resident_waves, st);
+  return e == hipSuccess ? LOGMEL_OK : LOGMEL_ERR_DEVICE;
+}
+
+int logmel_compute_chunked(const logmel_plan* plan, const float* d_samples,
+                           const int64_t* d_sample_offsets, const int64_t* d_frame_offsets,
+                           const int64_t* d_chunk_offsets, int64_t n_clips,
+                           int64_t total_frames, int64_t total_chunks, float* d_out,
+                           void* hip_stream) {
+  if (!plan || n_clips < 0 || total_frames < 0 || total_chunks < 0)
+    return LOGMEL_ERR_INVALID_ARGUMENT;
+  if (total_chunks > INT64_MAX / (kChunkFrames * kMels)) return LOGMEL_ERR_INPUT_TOO_LONG;
+  if (total_frames > total_chunks * kChunkFrames) return LOGMEL_ERR_INVALID_ARGUMENT;
+  if (n_clips == 0 || total_chunks == 0) return LOGMEL_OK;
+  if (!d_samples || !d_sample_offsets || !d_frame_offsets || !d_chunk_offsets || !d_out)
+    return LOGMEL_ERR_INVALID_ARGUMENT;
+  DeviceGuard g(plan->cfg.device);
+  if (!g.ok) return LOGMEL_ERR_DEVICE;
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  if (env_validate()) {
+    const int r = validate_offsets(d_sample_offsets, d_frame_offsets, d_chunk_offsets, n_clips,
+                                   total_frames, total_chunks, st);
+    if (r != LOGMEL_OK) return r;
+  }
+  const int64_t out_rows = total_chunks * kChunkFrames;
+  if (logmel_launch_chunk_pad(d_out, d_frame_offsets, d_chunk_offsets, n_clips, out_rows, st) !=
+      hipSuccess)
+    return LOGMEL_ERR_DEVICE;
+  const hipError_t e = logmel_launch_tiles(plan->tables, d_samples, d_sample_offsets,
+                                           d_sample_offsets + 1, d_frame_offsets, n_clips,
+                                           total_frames, d_out, d_chunk_offsets, kChunkFrames,
+                                           out_rows, plan->resident_waves, st);
   return e == hipSuccess ? LOGMEL_OK : LOGMEL_ERR_DEVICE;
 }
 
@@ -316,8 +398,8 @@ int logmel_stream_push(logmel_stream* s, const float* d_new, const int64_t* push
   if (logmel_launch_stream_prep(s->ws, s->stride, d_new, s->meta_dev, n, st) != hipSuccess)
     return LOGMEL_ERR_DEVICE;
   if (logmel_launch_tiles(s->plan->tables, s->ws, s->meta_dev + 4 * n, s->meta_dev + 5 * n,
-                          s->meta_dev + 6 * n, n, total_frames, d_out,
-                          s->plan->resident_waves, st) != hipSuccess)
+                          s->meta_dev + 6 * n, n, total_frames, d_out, s->meta_dev + 6 * n, 1,
+                          total_frames, s->plan->resident_waves, st) != hipSuccess)
     return LOGMEL_ERR_DEVICE;
   // Advance the host shadow.
   for (int64_t j = 0; j < n; ++j) {

@@ -67,14 +67,24 @@ __device__ __forceinline__ int64_t upper_bound_i64(const int64_t* __restrict__ a
 // the tile's span starts at sample s0.
 struct TileSrc {
   int64_t g, s, s0;
+  int64_t row;  // output row of the lane's frame: row_base[clip] * row_unit + frame
   bool in_range, valid, fast;
+};
+
+// Where a clip's frames go: row_base[clip] * row_unit + (frame index in the
+// clip). The offline layout passes the frame offsets with unit 1; the
+// 30-s chunk layout passes the chunk offsets with unit 3000.
+struct RowMap {
+  const int64_t* __restrict__ base;
+  int64_t unit;
 };
 
 __device__ __forceinline__ TileSrc locate_tile(int64_t tile, int lane,
                                                const int64_t* __restrict__ seg_start,
                                                const int64_t* __restrict__ seg_end,
                                                const int64_t* __restrict__ frame_off,
-                                               int64_t n_clips, int64_t total_frames) {
+                                               RowMap rows, int64_t n_clips,
+                                               int64_t total_frames) {
   TileSrc t;
   const int64_t g0 = tile * kTile;
   t.g = g0 + (lane >> 1);
@@ -102,9 +112,9 @@ __device__ __forceinline__ TileSrc locate_tile(int64_t tile, int lane,
   const int64_t bidx = c0 + 1 + lane;
   const int64_t B = bidx <= n_clips ? frame_off[bidx] : INT64_MAX;
   const int64_t cl = min(c0 + lane, n_clips - 1);
-  const int64_t SS = seg_start[cl], SE = seg_end[cl];
+  const int64_t SS = seg_start[cl], SE = seg_end[cl], RB = rows.base[cl];
   const int64_t B63 = __shfl(B, 63);
-  int64_t c, fo_c, ss_c, se_c;
+  int64_t c, fo_c, ss_c, se_c, rb_c;
   // The cross-lane search below needs every lane (__shfl reads inactive
   // lanes as garbage), so the choice is made for the whole wavefront.
   if (__any(B63 <= gq)) {
@@ -114,6 +124,7 @@ __device__ __forceinline__ TileSrc locate_tile(int64_t tile, int lane,
     fo_c = frame_off[c];
     ss_c = seg_start[c];
     se_c = seg_end[c];
+    rb_c = rows.base[c];
   } else {
     int cnt = 0;
 #pragma unroll
@@ -125,9 +136,11 @@ __device__ __forceinline__ TileSrc locate_tile(int64_t tile, int lane,
     fo_c = j > 0 ? fo_prev : frame_off[c0];
     ss_c = __shfl(SS, j);
     se_c = __shfl(SE, j);
+    rb_c = __shfl(RB, j);
   }
   const int64_t f = gq - fo_c;
   t.s = ss_c + 160 * f;
+  t.row = rb_c * rows.unit + f;
   // A frame is only computed if all its 400 samples lie inside its clip.
   t.valid = t.in_range && f >= 0 && (t.s + 400 <= se_c);
   t.fast = __all(t.valid && c == __shfl(c, 0));
@@ -156,11 +169,15 @@ logmel_tiles_kernel(const float* __restrict__ samples,
                     const int64_t* __restrict__ seg_end,     // [n_clips] one past its last
                     const int64_t* __restrict__ frame_off,   // [n_clips + 1]
                     int64_t n_clips, int64_t total_frames,
-                    float* __restrict__ out,                 // [total_frames][128]
+                    float* __restrict__ out,                 // [out_rows][128]
+                    const int64_t* __restrict__ row_base,    // [n_clips] see RowMap
+                    int64_t row_unit, int64_t out_rows,
                     const double* __restrict__ tables)       // plan tables: window, rotation, pad
 {
   const float* span_pad = reinterpret_cast<const float*>(tables + kTabDoubles);
+  const RowMap rows{row_base, row_unit};
   __shared__ float4 span_lds[(kOddBase + kParityLen + 3) / 4];
+  __shared__ int64_t row_lds[2][kTile];   // output rows of the current and the next tile
   float* lds = reinterpret_cast<float*>(span_lds);
   const int lane = threadIdx.x;
   __builtin_assume(lane < kWaveLanes);
@@ -174,11 +191,13 @@ logmel_tiles_kernel(const float* __restrict__ samples,
   // are live), so the loads' latency hides behind the filterbank and the log.
   int64_t tile = blockIdx.x;
   if (tile >= n_tiles) return;
-  TileSrc cur = locate_tile(tile, lane, seg_start, seg_end, frame_off, n_clips, total_frames);
+  TileSrc cur = locate_tile(tile, lane, seg_start, seg_end, frame_off, rows, n_clips,
+                            total_frames);
+  if (role == 0) row_lds[0][fl] = cur.row;
   f4u span[kSpanRegs];
   if (cur.fast) load_span(samples + cur.s0, lane, span);
 
-  while (true) {
+  for (int it = 0;; ++it) {
     // Lane-derived LDS addresses are formed inside the loop: hoisted out of
     // it they would stay live across the transform.
     int ln = lane;
@@ -234,7 +253,10 @@ logmel_tiles_kernel(const float* __restrict__ samples,
     const int64_t next = tile + gridDim.x;
     const bool more = next < n_tiles;
     TileSrc nxt = cur;
-    if (more) nxt = locate_tile(next, lane, seg_start, seg_end, frame_off, n_clips, total_frames);
+    if (more) {
+      nxt = locate_tile(next, lane, seg_start, seg_end, frame_off, rows, n_clips, total_frames);
+      if (role == 0) row_lds[(it + 1) & 1][fl] = nxt.row;
+    }
     // Loaded on every path (from the plan's zero pad when there is no span
     // to fetch), so that no register merge waits for the loads here.
     load_span(more && nxt.fast ? samples + nxt.s0 : span_pad, lane, span);
@@ -242,8 +264,9 @@ logmel_tiles_kernel(const float* __restrict__ samples,
     float o[64];
     pair_logmel(P, role, o);
     const int64_t g = tile * kTile + fl;
-    if (g < total_frames) {
-      float4* dst = reinterpret_cast<float4*>(out + g * 128 + 64 * role);
+    const int64_t row = row_lds[it & 1][ln >> 1];
+    if (g < total_frames && row >= 0 && row < out_rows) {
+      float4* dst = reinterpret_cast<float4*>(out + row * 128 + 64 * role);
       if ((valid_mask >> lane) & 1) {
 #pragma unroll
         for (int i = 0; i < 16; ++i)
@@ -260,6 +283,26 @@ logmel_tiles_kernel(const float* __restrict__ samples,
     tile = next;
     cur = nxt;
   }
+}
+
+// Padding of the 30-s chunk layout: one workgroup per clip fills the rows of
+// its last chunk past its last frame, rows [chunk_off[i] * 3000 + F_i,
+// chunk_off[i + 1] * 3000), with the log of the floor (rows beyond out_rows
+// are skipped). `floor` is the fp32 1e-10 passed in at run time, so the value
+// comes from the same log instruction as a silent frame's and equals it.
+extern "C" __global__ void __launch_bounds__(256)
+logmel_chunk_pad_kernel(float* __restrict__ out, const int64_t* __restrict__ frame_off,
+                        const int64_t* __restrict__ chunk_off, int64_t out_rows, float floor)
+{
+  const float pad = __builtin_amdgcn_logf(floor) * kLn2;
+  const int64_t i = blockIdx.x;
+  const int64_t r0 = chunk_off[i] * 3000 + (frame_off[i + 1] - frame_off[i]);
+  const int64_t r1 = min(chunk_off[i + 1] * 3000, out_rows);
+  if (r0 >= r1 || r0 < 0) return;
+  float4* dst = reinterpret_cast<float4*>(out + r0 * 128);
+  const int64_t n = (r1 - r0) * 32;   // 32 float4 per row
+  const float4 v = make_float4(pad, pad, pad, pad);
+  for (int64_t k = threadIdx.x; k < n; k += 256) dst[k] = v;
 }
 
 // One workgroup per stream. meta layout (int64, n = n_streams):
@@ -303,7 +346,8 @@ logmel_stream_prep_kernel(float* __restrict__ ws, int64_t row_stride,
 hipError_t logmel_launch_tiles(const double* tables, const float* samples,
                                const int64_t* seg_start, const int64_t* seg_end,
                                const int64_t* frame_off, int64_t n_clips, int64_t total_frames,
-                               float* out, int resident_waves, hipStream_t stream) {
+                               float* out, const int64_t* row_base, int64_t row_unit,
+                               int64_t out_rows, int resident_waves, hipStream_t stream) {
   if (total_frames <= 0) return hipSuccess;
   const int64_t tiles = (total_frames + logmel::kTile - 1) / logmel::kTile;
   // One wavefront per SIMD is resident at a time; the grid is that many
@@ -311,8 +355,22 @@ hipError_t logmel_launch_tiles(const double* tables, const float* samples,
   const int64_t grid = tiles < resident_waves ? tiles : resident_waves;
   hipLaunchKernelGGL(logmel::logmel_tiles_kernel, dim3((unsigned)grid), dim3(logmel::kWaveLanes),
                      0, stream, samples, seg_start, seg_end, frame_off, n_clips, total_frames, out,
-                     tables);
+                     row_base, row_unit, out_rows, tables);
   return hipGetLastError();
+}
+
+hipError_t logmel_launch_chunk_pad(float* out, const int64_t* frame_off, const int64_t* chunk_off,
+                                   int64_t n_clips, int64_t out_rows, hipStream_t stream) {
+  // A launch covers at most 2^31 - 1 clips.
+  const int64_t chunk = ((int64_t)1 << 31) - 1;
+  for (int64_t c0 = 0; c0 < n_clips; c0 += chunk) {
+    const int64_t n = n_clips - c0 < chunk ? n_clips - c0 : chunk;
+    hipLaunchKernelGGL(logmel::logmel_chunk_pad_kernel, dim3((unsigned)n), dim3(256), 0, stream,
+                       out, frame_off + c0, chunk_off + c0, out_rows, kLogFloor);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t logmel_launch_stream_prep(float* ws, int64_t row_stride, const float* fresh,

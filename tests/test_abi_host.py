@@ -89,3 +89,27 @@ def test_null_arguments(lm):
     assert lm._compute(None, None, None, None, 1, 1, None, None) == lm.LOGMEL_ERR_INVALID_ARGUMENT
     assert lm._stream_create(None, 1, 1, ctypes.byref(h)) == lm.LOGMEL_ERR_INVALID_ARGUMENT
     assert lm._stream_push(None, None, None, None, None, None) == lm.LOGMEL_ERR_INVALID_ARGUMENT
+
+
+def test_chunk_offsets_and_frames_match_oracle(lm):
+    rng = np.random.default_rng(3)
+    lens = np.concatenate([[0, 399, 400, 480000, 480400, 960000, 480000 + 320],
+                           rng.integers(0, 2_000_000, 100), [83_520_000, 3_000_000_000]])
+    so = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    co = lm.logmel_chunk_offsets(so)
+    assert co.dtype == np.int64
+    assert np.array_equal(co, O.chunk_offsets(so))
+    cf = lm.logmel_chunk_frames(so, int(co[-1]))
+    assert np.array_equal(cf, O.chunk_frames(so))
+    assert lm.CHUNK_FRAMES == O.CHUNK_FRAMES
+
+
+def test_chunk_helpers_reject_bad_input(lm):
+    with pytest.raises(lm.LogmelError):
+        lm.logmel_chunk_offsets([0, 10, 5])
+    so = np.array([0, 480000], dtype=np.int64)
+    with pytest.raises(lm.LogmelError) as e:
+        lm.logmel_chunk_frames(so, 2)          # the batch has 1 chunk
+    assert e.value.status == lm.LOGMEL_ERR_INVALID_ARGUMENT
+    assert lm._compute_chunked(None, None, None, None, None, 1, 1, 1, None, None) == \
+        lm.LOGMEL_ERR_INVALID_ARGUMENT
