@@ -137,23 +137,42 @@ def bench_offline(args, lm, plan, torch):
     n_samples = int(so[-1])
     so_d = torch.from_numpy(so).to(dev)
     fo_d = torch.from_numpy(fo).to(dev)
-    set_bytes = 4 * n_samples + 512 * total
+    chunked = args.layout == "chunked"
+    if chunked:
+        co = lm.logmel_chunk_offsets(so)
+        n_chunks = int(co[-1])
+        co_d = torch.from_numpy(co).to(dev)
+        out_rows = n_chunks * lm.CHUNK_FRAMES
+        desc += "; 30-s chunk layout [chunks, 3000, 128]"
+    else:
+        out_rows = total
+    set_bytes = 4 * n_samples + 512 * out_rows
     n_sets = max(1, min(5, int(math.ceil(1.1e9 / set_bytes)))) if args.workload != "c4" else 1
     xs = [x] + [x.clone() for _ in range(n_sets - 1)]
-    outs = [torch.empty((total, 128), dtype=torch.float32, device=dev) for _ in range(n_sets)]
+    if chunked:
+        outs = [torch.empty((n_chunks, lm.CHUNK_FRAMES, 128), dtype=torch.float32, device=dev)
+                for _ in range(n_sets)]
+    else:
+        outs = [torch.empty((total, 128), dtype=torch.float32, device=dev) for _ in range(n_sets)]
     stream = torch.cuda.current_stream(dev)
+
+    def step(k):
+        if chunked:
+            lm.logmel_compute_chunked(plan, xs[k], so_d, fo_d, co_d, total, n_chunks, out=outs[k],
+                                      stream=stream)
+        else:
+            lm.logmel_compute(plan, xs[k], so_d, fo_d, total, out=outs[k], stream=stream)
+
     for i in range(args.warmup):
-        k = i % n_sets
-        lm.logmel_compute(plan, xs[k], so_d, fo_d, total, out=outs[k], stream=stream)
+        step(i % n_sets)
     torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        k = i % n_sets
         starts[i].record(stream)
-        lm.logmel_compute(plan, xs[k], so_d, fo_d, total, out=outs[k], stream=stream)
+        step(i % n_sets)
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -164,7 +183,7 @@ def bench_offline(args, lm, plan, torch):
     audio_s = n_samples / FS
     achieved_gbs = algo_bytes / kern_avg_s / 1e9
     achieved_tflops = FLOPS_PER_FRAME * total / kern_avg_s / 1e12
-    traffic = measured_traffic(args.workload)
+    traffic = measured_traffic(args.workload) if not chunked else None
     rec = {
         "metric": "audio-seconds/sec of 128-bin log-mel on 1 MI355X + % of HBM roofline",
         "value": audio_s / (ms_per_step / 1e3),
@@ -179,13 +198,15 @@ def bench_offline(args, lm, plan, torch):
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": desc, "clips": len(so) - 1, "samples": n_samples,
-                   "frames": total, "buffer_sets": n_sets},
+                   "frames": total, "output_rows": out_rows, "buffer_sets": n_sets},
         "frames_per_s": total / (ms_per_step / 1e3),
         # The kernel is bound by vector-ALU issue (an fp64 transform), not by
         # HBM: its roofline is the ALU one; the HBM figures ride along.
         "roofline": {"bound": "alu", "achieved": achieved_tflops, "peak": ALU_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved_tflops / ALU_PEAK_TFLOPS,
-                     "traffic": traffic, "kernel": "logmel_tiles_kernel",
+                     "traffic": traffic,
+                     "kernel": ("logmel_chunk_pad_kernel + logmel_tiles_kernel" if chunked
+                                else "logmel_tiles_kernel"),
                      "kernel_avg_us": kern_avg_s * 1e6,
                      "algorithmic_flops_per_launch": FLOPS_PER_FRAME * total,
                      "algorithmic_bytes_per_launch": algo_bytes,
@@ -278,6 +299,8 @@ def main():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="c2", choices=["c2", "c1", "c4", "c3"])
+    ap.add_argument("--layout", default="frames", choices=["frames", "chunked"],
+                    help="output layout: [frames, 128] or 30-s chunks [chunks, 3000, 128]")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--counter-pass", action="store_true",
