@@ -227,23 +227,28 @@ def bench_offline(args, lm, plan, torch):
 
 
 def bench_stream(args, lm, plan, torch):
-    """One step = 375 pushes of 1280 samples to 512 streams (30 s each)."""
+    """One step = every 30 s stream of 512 pushed through in pushes of the
+    audio clock (80 ms: 375 pushes of 1280 samples; 120 ms: 250 of 1920;
+    160 ms: 187 of 2560 and one of 1280)."""
     import logmel_synth as S
     import numpy as np
     dev = torch.device("cuda", 0)
-    n, pushes, P = 512, 375, 1280
+    n, N = 512, 480000
+    P = args.clock_ms * FS // 1000
     streams = S.config3_streams(device=dev)
-    chunks = [streams[:, c * P:(c + 1) * P].contiguous().reshape(-1) for c in range(pushes)]
+    lens = [min(P, N - a) for a in range(0, N, P)]
+    pushes = len(lens)
+    chunks = [streams[:, a:a + L].contiguous().reshape(-1) for a, L in zip(range(0, N, P), lens)]
     s = lm.logmel_stream_create(plan, n, P)
-    pl = np.full(n, P, dtype=np.int64)
-    out = torch.empty((n * 8, 128), dtype=torch.float32, device=dev)
+    pls = [np.full(n, L, dtype=np.int64) for L in lens]
+    out = torch.empty((n * (P // 160 + 1), 128), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def one_pass():
         lm.logmel_stream_reset(s)
         for c in range(pushes):
-            fo = lm.logmel_stream_frames_for_push(s, pl)
-            lm.logmel_stream_push(s, chunks[c], pl, out=out[:int(fo[-1])], stream=stream)
+            fo = lm.logmel_stream_frames_for_push(s, pls[c])
+            lm.logmel_stream_push(s, chunks[c], pls[c], out=out[:int(fo[-1])], stream=stream)
 
     for _ in range(args.warmup):
         one_pass()
@@ -254,7 +259,7 @@ def bench_stream(args, lm, plan, torch):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall / args.steps * 1e3
-    audio_s = n * pushes * P / FS
+    audio_s = n * N / FS
     frames = n * 2998
     rec = {
         "metric": "audio-seconds/sec of 128-bin log-mel on 1 MI355X + % of HBM roofline",
@@ -263,7 +268,8 @@ def bench_stream(args, lm, plan, torch):
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": "streaming: 512 streams x 375 pushes of 1280 samples (80 ms)",
+        "config": {"workload": f"streaming: 512 streams x 30 s in pushes of {P} samples "
+                               f"({args.clock_ms} ms audio clock, {pushes} pushes)",
                    "streams": n, "pushes": pushes, "push_samples": P},
         "frames_per_s": frames / (ms_per_step / 1e3),
         "push_latency_us": ms_per_step * 1e3 / pushes,
@@ -299,6 +305,8 @@ def main():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="c2", choices=["c2", "c1", "c4", "c3"])
+    ap.add_argument("--clock-ms", type=int, default=80, choices=[80, 120, 160],
+                    help="audio clock of the streaming workload (c3)")
     ap.add_argument("--layout", default="frames", choices=["frames", "chunked"],
                     help="output layout: [frames, 128] or 30-s chunks [chunks, 3000, 128]")
     ap.add_argument("--no-cpu-baseline", action="store_true")

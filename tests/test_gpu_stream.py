@@ -168,3 +168,36 @@ def test_reset(env):
     o2, _ = lm.logmel_stream_push(s, x.reshape(-1).contiguous(), [4000] * n)
     assert torch.equal(o1, o2)
     s.close()
+
+
+@pytest.mark.parametrize("push,first,steady", [(1920, 10, 12), (2560, 14, 16)])
+def test_other_clocks_equal_offline(env, push, first, steady):
+    """The 120 and 160 ms audio clocks (1920- and 2560-sample pushes): the
+    page-5 clocks other than 80 ms. 64 speech-like 30 s streams; the last
+    push of the 160 ms clock is the 1280-sample remainder."""
+    lm, plan, torch = env
+    say(f"clock {push} samples: generate")
+    streams = S.config3_streams(device="cuda", n_streams=64)
+    n, N = streams.shape
+    s = lm.logmel_stream_create(plan, n, push)
+    collect = [[] for _ in range(n)]
+    per_push = []
+    pos = 0
+    say(f"clock {push} samples: pushes")
+    while pos < N:
+        p = min(push, N - pos)
+        new = streams[:, pos:pos + p].contiguous().reshape(-1)
+        out, fo = lm.logmel_stream_push(s, new, np.full(n, p))
+        per_push.append(int(fo[1] - fo[0]))
+        for j in range(n):
+            collect[j].append(out[fo[j]:fo[j + 1]])
+        pos += p
+    full = N // push
+    assert per_push[0] == first and all(v == steady for v in per_push[1:full])
+    assert sum(per_push) == 2998
+    streamed = torch.stack([torch.cat(collect[j]) for j in range(n)])
+    ref, fo = offline(env, streams)
+    torch.cuda.synchronize()
+    assert torch.equal(streamed.reshape(-1, 128), ref), "stream != offline"
+    assert lm.logmel_stream_counters(s, 0) == (N, 2998)
+    s.close()

@@ -412,3 +412,31 @@ def test_chunked_layout():
     assert [O.num_frames(n) for n in lens] == [0, 3000, 0, 3001, 6000, 75]
     assert list(np.diff(co)) == [0, 1, 0, 2, 2, 1]
     assert O.chunk_frames(so).tolist() == [3000, 3000, 1, 3000, 3000, 75]
+
+
+# ------------------------------------------------------- streaming clocks
+
+def test_stream_clocks_page_facts(golden_dir):
+    facts = json.load(open(os.path.join(golden_dir, "page_facts.json")))
+    cl = facts["stream_clocks_ms"]
+    for ms, rate in zip(cl["value"], cl["decisions_per_s"]):
+        assert 1000.0 / ms == pytest.approx(rate, abs=0.05)
+    assert [ms * O.SAMPLE_RATE // 1000 for ms in cl["value"]] == [1280, 1920, 2560]
+    assert facts["stream_push_80ms"]["value"] == 1280
+
+
+@pytest.mark.parametrize("push,first,steady", [(1280, 6, 8), (1920, 10, 12), (2560, 14, 16)])
+def test_stream_schedule_and_carry(push, first, steady):
+    """Frames a push completes on the offline grid, and the carry left: by
+    brute enumeration of frame starts over the concatenated stream."""
+    emitted = 0
+    for c in range(1, 200):
+        n = c * push
+        F = _brute_frame_count(n)
+        per_push = F - emitted
+        emitted = F
+        assert per_push == (first if c == 1 else steady), (push, c)
+        # the carry: samples from the next frame's start to the end
+        carry = n - 160 * F
+        assert carry == 320 == 240 + ((n - 400) % 160)
+        assert O.num_frames(n) == F
