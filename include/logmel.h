@@ -145,6 +145,27 @@ int logmel_compute_chunked(const logmel_plan* plan, const float* d_samples,
                            int64_t total_frames, int64_t total_chunks, float* d_out,
                            void* hip_stream);
 
+/* Sample and output types of logmel_compute_ex. */
+#define LOGMEL_F32 0 /* fp32 */
+#define LOGMEL_I16 1 /* int16 PCM, input only: sample s means s / 32768 (page 1, §2.1 gives
+                        samples as floats in [-1.0, 1.0]; s / 32768 is exact in fp32, so an int16
+                        batch gives the fp32 batch's result bit for bit) */
+#define LOGMEL_F16 2 /* IEEE half, output only: each fp32 log-mel value rounded once to
+                        nearest; padding and the NaN rows of inconsistent offsets as in fp32 */
+
+/* The general offline call; logmel_compute and logmel_compute_chunked are
+ * this call with fp32 in and out.
+ *   d_samples          sample_type LOGMEL_F32 (float) or LOGMEL_I16 (int16_t)
+ *   d_chunk_offsets    NULL: the frame layout [total_frames][128]
+ *                      (total_chunks unused); else the 30-s chunk layout
+ *                      [total_chunks][3000][128] as in logmel_compute_chunked
+ *   d_out              out_type LOGMEL_F32 (float) or LOGMEL_F16 (half)
+ * Other types: UNSUPPORTED. Everything else as logmel_compute. */
+int logmel_compute_ex(const logmel_plan* plan, const void* d_samples, int sample_type,
+                      const int64_t* d_sample_offsets, const int64_t* d_frame_offsets,
+                      const int64_t* d_chunk_offsets, int64_t n_clips, int64_t total_frames,
+                      int64_t total_chunks, void* d_out, int out_type, void* hip_stream);
+
 /* Streaming (the 80 ms audio clock of the Audio8-ASR-Infinite page gives the
  * 1280-sample push). A stream object holds n_streams independent streams.
  * Each push appends new samples to every stream and emits every frame that

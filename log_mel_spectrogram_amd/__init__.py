@@ -33,6 +33,9 @@ LOGMEL_ERR_INPUT_TOO_LONG = -5
 
 N_MELS = 128
 CHUNK_FRAMES = 3000   # LOGMEL_CHUNK_FRAMES
+LOGMEL_F32 = 0
+LOGMEL_I16 = 1
+LOGMEL_F16 = 2
 N_FFT = 400
 HOP = 160
 SAMPLE_RATE = 16000
@@ -69,6 +72,8 @@ _chunk_offsets = _sig("logmel_chunk_offsets", ctypes.c_int, _i64p, _i64, _i64p)
 _chunk_frames = _sig("logmel_chunk_frames", ctypes.c_int, _i64p, _i64, _i64, _i64p)
 _compute_chunked = _sig("logmel_compute_chunked", ctypes.c_int, _p, _p, _p, _p, _p, _i64, _i64,
                         _i64, _p, _p)
+_compute_ex = _sig("logmel_compute_ex", ctypes.c_int, _p, _p, ctypes.c_int, _p, _p, _p, _i64, _i64,
+                   _i64, _p, ctypes.c_int, _p)
 _stream_create = _sig("logmel_stream_create", ctypes.c_int, _p, _i64, _i64, ctypes.POINTER(_p))
 _stream_destroy = _sig("logmel_stream_destroy", None, _p)
 _stream_reset = _sig("logmel_stream_reset", ctypes.c_int, _p)
@@ -83,7 +88,7 @@ EXPORTED = [
     "logmel_default_config", "logmel_abi_version", "logmel_status_string",
     "logmel_plan_create", "logmel_plan_destroy", "logmel_num_frames",
     "logmel_frame_offsets", "logmel_compute", "logmel_chunk_offsets", "logmel_chunk_frames",
-    "logmel_compute_chunked", "logmel_stream_create",
+    "logmel_compute_chunked", "logmel_compute_ex", "logmel_stream_create",
     "logmel_stream_destroy", "logmel_stream_reset", "logmel_stream_frames_for_push",
     "logmel_stream_push", "logmel_stream_counters", "logmel_stream_state_bytes",
     "logmel_stream_get_state", "logmel_stream_set_state",
@@ -258,6 +263,49 @@ def logmel_compute_chunked(plan: Plan, samples, sample_offsets, frame_offsets, c
                             n_clips, int(total_frames), int(total_chunks),
                             _dev_ptr(out, torch.float32, "out"), st),
            "logmel_compute_chunked")
+    return out
+
+
+def logmel_compute_ex(plan: Plan, samples, sample_offsets, frame_offsets, total_frames: int,
+                      chunk_offsets=None, total_chunks: int = 0, out=None, out_dtype=None,
+                      stream=None):
+    """The general offline call: samples fp32 or int16 (s / 32768), output
+    fp32 or fp16 (out_dtype, default fp32), frame layout [total_frames, 128]
+    or, with chunk_offsets, the 30-s chunk layout [total_chunks, 3000, 128]."""
+    torch = _torch()
+    n_clips = int(sample_offsets.numel()) - 1
+    if samples.dtype == torch.float32:
+        st_in = LOGMEL_F32
+    elif samples.dtype == torch.int16:
+        st_in = LOGMEL_I16
+    else:
+        raise TypeError(f"samples must be float32 or int16, got {samples.dtype}")
+    out_dtype = out_dtype or (out.dtype if out is not None else torch.float32)
+    if out_dtype == torch.float32:
+        st_out = LOGMEL_F32
+    elif out_dtype == torch.float16:
+        st_out = LOGMEL_F16
+    else:
+        raise TypeError(f"output must be float32 or float16, got {out_dtype}")
+    shape = ((int(total_chunks), CHUNK_FRAMES, N_MELS) if chunk_offsets is not None
+             else (int(total_frames), N_MELS))
+    if out is None:
+        out = torch.empty(shape, dtype=out_dtype, device=samples.device)
+    if tuple(out.shape) != shape:
+        raise ValueError(f"out must be {list(shape)}")
+    if frame_offsets.numel() != n_clips + 1:
+        raise ValueError("frame_offsets must have n_clips + 1 entries")
+    if chunk_offsets is not None and chunk_offsets.numel() != n_clips + 1:
+        raise ValueError("chunk_offsets must have n_clips + 1 entries")
+    st = _stream_handle(stream, samples.device)
+    _check(_compute_ex(plan.handle, _dev_ptr(samples, samples.dtype, "samples"), st_in,
+                       _dev_ptr(sample_offsets, torch.int64, "sample_offsets"),
+                       _dev_ptr(frame_offsets, torch.int64, "frame_offsets"),
+                       (None if chunk_offsets is None
+                        else _dev_ptr(chunk_offsets, torch.int64, "chunk_offsets")),
+                       n_clips, int(total_frames), int(total_chunks),
+                       _dev_ptr(out, out_dtype, "out"), st_out, st),
+           "logmel_compute_ex")
     return out
 
 

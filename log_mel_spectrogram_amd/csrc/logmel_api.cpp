@@ -224,40 +224,25 @@ int validate_offsets(const int64_t* d_so, const int64_t* d_fo, const int64_t* d_
 
 }  // namespace
 
-int logmel_compute(const logmel_plan* plan, const float* d_samples,
-                   const int64_t* d_sample_offsets, const int64_t* d_frame_offsets,
-                   int64_t n_clips, int64_t total_frames, float* d_out, void* hip_stream) {
+int logmel_compute_ex(const logmel_plan* plan, const void* d_samples, int sample_type,
+                      const int64_t* d_sample_offsets, const int64_t* d_frame_offsets,
+                      const int64_t* d_chunk_offsets, int64_t n_clips, int64_t total_frames,
+                      int64_t total_chunks, void* d_out, int out_type, void* hip_stream) {
   if (!plan || n_clips < 0 || total_frames < 0) return LOGMEL_ERR_INVALID_ARGUMENT;
-  if (total_frames > INT64_MAX / kMels) return LOGMEL_ERR_INPUT_TOO_LONG;
-  if (n_clips == 0 || total_frames == 0) return LOGMEL_OK;
-  if (!d_samples || !d_sample_offsets || !d_frame_offsets || !d_out)
-    return LOGMEL_ERR_INVALID_ARGUMENT;
-  DeviceGuard g(plan->cfg.device);
-  if (!g.ok) return LOGMEL_ERR_DEVICE;
-  hipStream_t st = static_cast<hipStream_t>(hip_stream);
-  if (env_validate()) {
-    const int r = validate_offsets(d_sample_offsets, d_frame_offsets, nullptr, n_clips,
-                                   total_frames, 0, st);
-    if (r != LOGMEL_OK) return r;
+  if (sample_type != LOGMEL_F32 && sample_type != LOGMEL_I16) return LOGMEL_ERR_UNSUPPORTED;
+  if (out_type != LOGMEL_F32 && out_type != LOGMEL_F16) return LOGMEL_ERR_UNSUPPORTED;
+  const bool chunked = d_chunk_offsets != nullptr;
+  int64_t out_rows = total_frames;
+  if (chunked) {
+    if (total_chunks < 0) return LOGMEL_ERR_INVALID_ARGUMENT;
+    if (total_chunks > INT64_MAX / (kChunkFrames * kMels)) return LOGMEL_ERR_INPUT_TOO_LONG;
+    if (total_frames > total_chunks * kChunkFrames) return LOGMEL_ERR_INVALID_ARGUMENT;
+    out_rows = total_chunks * kChunkFrames;
+  } else if (total_frames > INT64_MAX / kMels) {
+    return LOGMEL_ERR_INPUT_TOO_LONG;
   }
-  const hipError_t e = logmel_launch_tiles(plan->tables, d_samples, d_sample_offsets,
-                                           d_sample_offsets + 1, d_frame_offsets, n_clips,
-                                           total_frames, d_out, d_frame_offsets, 1, total_frames,
-                                           plan->resident_waves, st);
-  return e == hipSuccess ? LOGMEL_OK : LOGMEL_ERR_DEVICE;
-}
-
-int logmel_compute_chunked(const logmel_plan* plan, const float* d_samples,
-                           const int64_t* d_sample_offsets, const int64_t* d_frame_offsets,
-                           const int64_t* d_chunk_offsets, int64_t n_clips,
-                           int64_t total_frames, int64_t total_chunks, float* d_out,
-                           void* hip_stream) {
-  if (!plan || n_clips < 0 || total_frames < 0 || total_chunks < 0)
-    return LOGMEL_ERR_INVALID_ARGUMENT;
-  if (total_chunks > INT64_MAX / (kChunkFrames * kMels)) return LOGMEL_ERR_INPUT_TOO_LONG;
-  if (total_frames > total_chunks * kChunkFrames) return LOGMEL_ERR_INVALID_ARGUMENT;
-  if (n_clips == 0 || total_chunks == 0) return LOGMEL_OK;
-  if (!d_samples || !d_sample_offsets || !d_frame_offsets || !d_chunk_offsets || !d_out)
+  if (n_clips == 0 || out_rows == 0) return LOGMEL_OK;
+  if (!d_samples || !d_sample_offsets || !d_frame_offsets || !d_out)
     return LOGMEL_ERR_INVALID_ARGUMENT;
   DeviceGuard g(plan->cfg.device);
   if (!g.ok) return LOGMEL_ERR_DEVICE;
@@ -267,15 +252,34 @@ int logmel_compute_chunked(const logmel_plan* plan, const float* d_samples,
                                    total_frames, total_chunks, st);
     if (r != LOGMEL_OK) return r;
   }
-  const int64_t out_rows = total_chunks * kChunkFrames;
-  if (logmel_launch_chunk_pad(d_out, d_frame_offsets, d_chunk_offsets, n_clips, out_rows, st) !=
-      hipSuccess)
+  const int out_f16 = out_type == LOGMEL_F16;
+  if (chunked && logmel_launch_chunk_pad(d_out, out_f16, d_frame_offsets, d_chunk_offsets,
+                                         n_clips, out_rows, st) != hipSuccess)
     return LOGMEL_ERR_DEVICE;
-  const hipError_t e = logmel_launch_tiles(plan->tables, d_samples, d_sample_offsets,
-                                           d_sample_offsets + 1, d_frame_offsets, n_clips,
-                                           total_frames, d_out, d_chunk_offsets, kChunkFrames,
-                                           out_rows, plan->resident_waves, st);
+  const hipError_t e = logmel_launch_tiles(
+      plan->tables, d_samples, sample_type == LOGMEL_I16, d_sample_offsets, d_sample_offsets + 1,
+      d_frame_offsets, n_clips, total_frames, d_out, out_f16,
+      chunked ? d_chunk_offsets : d_frame_offsets, chunked ? kChunkFrames : 1, out_rows,
+      plan->resident_waves, st);
   return e == hipSuccess ? LOGMEL_OK : LOGMEL_ERR_DEVICE;
+}
+
+int logmel_compute(const logmel_plan* plan, const float* d_samples,
+                   const int64_t* d_sample_offsets, const int64_t* d_frame_offsets,
+                   int64_t n_clips, int64_t total_frames, float* d_out, void* hip_stream) {
+  return logmel_compute_ex(plan, d_samples, LOGMEL_F32, d_sample_offsets, d_frame_offsets, nullptr,
+                           n_clips, total_frames, 0, d_out, LOGMEL_F32, hip_stream);
+}
+
+int logmel_compute_chunked(const logmel_plan* plan, const float* d_samples,
+                           const int64_t* d_sample_offsets, const int64_t* d_frame_offsets,
+                           const int64_t* d_chunk_offsets, int64_t n_clips,
+                           int64_t total_frames, int64_t total_chunks, float* d_out,
+                           void* hip_stream) {
+  if (!d_chunk_offsets) return LOGMEL_ERR_INVALID_ARGUMENT;
+  return logmel_compute_ex(plan, d_samples, LOGMEL_F32, d_sample_offsets, d_frame_offsets,
+                           d_chunk_offsets, n_clips, total_frames, total_chunks, d_out,
+                           LOGMEL_F32, hip_stream);
 }
 
 // ---------------------------------------------------------------- streaming
@@ -397,8 +401,8 @@ int logmel_stream_push(logmel_stream* s, const float* d_new, const int64_t* push
   s->slot = (slot + 1) % logmel_stream::kSlots;
   if (logmel_launch_stream_prep(s->ws, s->stride, d_new, s->meta_dev, n, st) != hipSuccess)
     return LOGMEL_ERR_DEVICE;
-  if (logmel_launch_tiles(s->plan->tables, s->ws, s->meta_dev + 4 * n, s->meta_dev + 5 * n,
-                          s->meta_dev + 6 * n, n, total_frames, d_out, s->meta_dev + 6 * n, 1,
+  if (logmel_launch_tiles(s->plan->tables, s->ws, 0, s->meta_dev + 4 * n, s->meta_dev + 5 * n,
+                          s->meta_dev + 6 * n, n, total_frames, d_out, 0, s->meta_dev + 6 * n, 1,
                           total_frames, s->plan->resident_waves, st) != hipSuccess)
     return LOGMEL_ERR_DEVICE;
   // Advance the host shadow.

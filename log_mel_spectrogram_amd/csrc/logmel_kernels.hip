@@ -148,37 +148,169 @@ __device__ __forceinline__ TileSrc locate_tile(int64_t tile, int lane,
   return t;
 }
 
-// The span of a tile inside one clip: 16-byte groups lane + 64 i; lanes past
-// the span's end repeat its last group, so every load is issued without a
-// branch.
-static constexpr int kSpanRegs = (kSpanGroups + kWaveLanes - 1) / kWaveLanes;
+// ---------------------------------------------------------------------------
+// Input types. fp32 samples as given; int16 PCM samples s mean s / 32768
+// (full scale to [-1, 1), exact in fp32), so an int16 batch gives the fp32
+// batch's result bit for bit.
+// ---------------------------------------------------------------------------
+static constexpr float kI16Scale = 1.0f / 32768.0f;
 
-__device__ __forceinline__ void load_span(const float* __restrict__ src, int lane,
-                                          f4u (&span)[kSpanRegs]) {
+__device__ __forceinline__ float sample_value(const float* p) { return *p; }
+__device__ __forceinline__ float sample_value(const int16_t* p) { return (float)*p * kI16Scale; }
+
+// Position in a parity array of value i (4 padding slots after every 80).
+__device__ __forceinline__ int par_pos(int i) { return i + 4 * (i / 80); }
+
+// The span of a tile inside one clip, fp32: 16-byte groups lane + 64 i;
+// lanes past the span's end repeat its last group, so every load is issued
+// without a branch.
+static constexpr int kSpanRegs = (kSpanGroups + kWaveLanes - 1) / kWaveLanes;
+struct SpanF32 {
+  f4u g[kSpanRegs];
+};
+
+__device__ __forceinline__ void load_span(const float* __restrict__ src, int lane, SpanF32& sp) {
 #pragma unroll
   for (int i = 0; i < kSpanRegs; ++i) {
     const int j = min(lane + kWaveLanes * i, kSpanGroups - 1);
-    span[i] = *reinterpret_cast<const f4u*>(src + 4 * j);
+    sp.g[i] = *reinterpret_cast<const f4u*>(src + 4 * j);
   }
 }
 
-extern "C" __global__ void __attribute__((amdgpu_flat_work_group_size(64, 64),
-                                          amdgpu_waves_per_eu(1, 1)))
-logmel_tiles_kernel(const float* __restrict__ samples,
-                    const int64_t* __restrict__ seg_start,   // [n_clips] first sample of clip
-                    const int64_t* __restrict__ seg_end,     // [n_clips] one past its last
-                    const int64_t* __restrict__ frame_off,   // [n_clips + 1]
-                    int64_t n_clips, int64_t total_frames,
-                    float* __restrict__ out,                 // [out_rows][128]
-                    const int64_t* __restrict__ row_base,    // [n_clips] see RowMap
-                    int64_t row_unit, int64_t out_rows,
-                    const double* __restrict__ tables)       // plan tables: window, rotation, pad
-{
-  const float* span_pad = reinterpret_cast<const float*>(tables + kTabDoubles);
+__device__ __forceinline__ void span_to_lds(const SpanF32& sp, int ln, float* lds) {
+#pragma unroll
+  for (int i = 0; i < kSpanRegs; ++i) {
+    const int j = min(ln + kWaveLanes * i, kSpanGroups - 1);
+    // even values 2j, 2j + 1; reversed odd values 2678 - 2j (sample 4j + 3)
+    // and 2679 - 2j (sample 4j + 1)
+    const int e = par_pos(2 * j);
+    const int o = kOddBase + par_pos(kSpan / 2 - 2 - 2 * j);
+    *reinterpret_cast<float2*>(lds + e) = make_float2(sp.g[i].x, sp.g[i].z);
+    *reinterpret_cast<float2*>(lds + o) = make_float2(sp.g[i].w, sp.g[i].y);
+  }
+}
+
+// The span of a tile inside one clip, int16: 8-byte groups (4 samples) from
+// the 4-byte aligned sample a0 = s0 rounded down to even, group j = samples
+// a0 + 4j .. a0 + 4j + 3. With an even s0 the 1340 groups are the span; with
+// an odd s0 they start one sample early and the span's last sample comes as
+// a separate 2-byte load, so nothing outside [s0 - 1, s0 + 5360) is read.
+struct __attribute__((packed, aligned(4))) u2u {
+  uint32_t x, y;
+};
+struct SpanI16 {
+  u2u g[kSpanRegs];
+  int16_t tail;
+  int odd;
+};
+
+__device__ __forceinline__ void load_span(const int16_t* __restrict__ src, int lane, SpanI16& sp) {
+  // src points at the span's first sample s0; its parity is that of the
+  // address in 2-byte units
+  const int odd = (int)((reinterpret_cast<uintptr_t>(src) >> 1) & 1);
+  const int16_t* a0 = src - odd;
+#pragma unroll
+  for (int i = 0; i < kSpanRegs; ++i) {
+    const int j = min(lane + kWaveLanes * i, kSpanGroups - 1);
+    sp.g[i] = *reinterpret_cast<const u2u*>(a0 + 4 * j);
+  }
+  sp.tail = a0[odd ? kSpan : 0];
+  sp.odd = odd;
+}
+
+__device__ __forceinline__ float lo16(uint32_t v) { return (float)(int16_t)(v & 0xffff) * kI16Scale; }
+__device__ __forceinline__ float hi16(uint32_t v) { return (float)(int16_t)(v >> 16) * kI16Scale; }
+
+__device__ __forceinline__ void span_to_lds(const SpanI16& sp, int ln, float* lds) {
+  if (!sp.odd) {
+    // samples 4j .. 4j + 3 of the span, as in the fp32 layout
+#pragma unroll
+    for (int i = 0; i < kSpanRegs; ++i) {
+      const int j = min(ln + kWaveLanes * i, kSpanGroups - 1);
+      const float f0 = lo16(sp.g[i].x), f1 = hi16(sp.g[i].x);
+      const float f2 = lo16(sp.g[i].y), f3 = hi16(sp.g[i].y);
+      *reinterpret_cast<float2*>(lds + par_pos(2 * j)) = make_float2(f0, f2);
+      *reinterpret_cast<float2*>(lds + kOddBase + par_pos(kSpan / 2 - 2 - 2 * j)) =
+          make_float2(f3, f1);
+    }
+  } else {
+    // group j holds span samples 4j - 1 .. 4j + 2: even values 2j, 2j + 1
+    // (samples 4j, 4j + 2), odd values 2j - 1 and 2j (samples 4j - 1, 4j + 1)
+    // at reversed positions 2680 - 2j and 2679 - 2j; group 0's first sample
+    // lies before the span and goes to a padding slot.
+#pragma unroll
+    for (int i = 0; i < kSpanRegs; ++i) {
+      const int j = min(ln + kWaveLanes * i, kSpanGroups - 1);
+      const float f0 = lo16(sp.g[i].x), f1 = hi16(sp.g[i].x);
+      const float f2 = lo16(sp.g[i].y), f3 = hi16(sp.g[i].y);
+      *reinterpret_cast<float2*>(lds + par_pos(2 * j)) = make_float2(f1, f3);
+      lds[kOddBase + (j > 0 ? par_pos(kSpan / 2 - 2 * j) : 80)] = f0;
+      lds[kOddBase + par_pos(kSpan / 2 - 1 - 2 * j)] = f2;
+    }
+    // span sample 5359: odd value 2679, reversed position 0
+    if (ln == 0) lds[kOddBase] = (float)sp.tail * kI16Scale;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Output types: fp32, or fp16 (each value rounded once to nearest).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void store_bands(float* __restrict__ dst, const float (&o)[64], bool ok) {
+  float4* d = reinterpret_cast<float4*>(dst);
+  if (ok) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) d[i] = make_float4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+  } else {
+    // Offsets that promise a frame the clip cannot hold: a loud row, not a
+    // silent truncation.
+    const float qnan = __builtin_nanf("");
+#pragma unroll
+    for (int i = 0; i < 16; ++i) d[i] = make_float4(qnan, qnan, qnan, qnan);
+  }
+}
+
+// The fp32 value is fenced first, so that the conversion rounds the fp32
+// result (the compiler would otherwise fuse the log's last multiply into a
+// mixed-precision FMA rounding straight to fp16, which differs at ties).
+__device__ __forceinline__ uint32_t pack_half2(float a, float b) {
+  fence(a);
+  fence(b);
+  const _Float16 ha = (_Float16)a, hb = (_Float16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+
+__device__ __forceinline__ void store_bands(_Float16* __restrict__ dst, const float (&o)[64], bool ok) {
+  uint4* d = reinterpret_cast<uint4*>(dst);
+  if (ok) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      d[i] = make_uint4(pack_half2(o[8 * i], o[8 * i + 1]), pack_half2(o[8 * i + 2], o[8 * i + 3]),
+                        pack_half2(o[8 * i + 4], o[8 * i + 5]), pack_half2(o[8 * i + 6], o[8 * i + 7]));
+  } else {
+    const uint32_t qnan2 = 0x7e007e00u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) d[i] = make_uint4(qnan2, qnan2, qnan2, qnan2);
+  }
+}
+
+template <typename In> struct SpanOf;
+template <> struct SpanOf<float> { using type = SpanF32; };
+template <> struct SpanOf<int16_t> { using type = SpanI16; };
+
+template <typename In, typename Out>
+__device__ __forceinline__ void tiles_body(const In* __restrict__ samples,
+                                           const int64_t* __restrict__ seg_start,
+                                           const int64_t* __restrict__ seg_end,
+                                           const int64_t* __restrict__ frame_off,
+                                           int64_t n_clips, int64_t total_frames,
+                                           Out* __restrict__ out,
+                                           const int64_t* __restrict__ row_base,
+                                           int64_t row_unit, int64_t out_rows,
+                                           const double* __restrict__ tables,
+                                           float* lds, int64_t (&row_lds)[2][kTile]) {
+  // a readable stand-in for a span when there is none to fetch (zeros)
+  const In* span_pad = reinterpret_cast<const In*>(tables + kTabDoubles);
   const RowMap rows{row_base, row_unit};
-  __shared__ float4 span_lds[(kOddBase + kParityLen + 3) / 4];
-  __shared__ int64_t row_lds[2][kTile];   // output rows of the current and the next tile
-  float* lds = reinterpret_cast<float*>(span_lds);
   const int lane = threadIdx.x;
   __builtin_assume(lane < kWaveLanes);
   const int role = lane & 1;
@@ -194,7 +326,7 @@ logmel_tiles_kernel(const float* __restrict__ samples,
   TileSrc cur = locate_tile(tile, lane, seg_start, seg_end, frame_off, rows, n_clips,
                             total_frames);
   if (role == 0) row_lds[0][fl] = cur.row;
-  f4u span[kSpanRegs];
+  typename SpanOf<In>::type span;
   if (cur.fast) load_span(samples + cur.s0, lane, span);
 
   for (int it = 0;; ++it) {
@@ -207,16 +339,7 @@ logmel_tiles_kernel(const float* __restrict__ samples,
     if (cur.fast) {
       // Split the span by parity into LDS (layout above), then read back this
       // lane's 200 values.
-#pragma unroll
-      for (int i = 0; i < kSpanRegs; ++i) {
-        const int j = min(ln + kWaveLanes * i, kSpanGroups - 1);
-        // even values 2j, 2j + 1; reversed odd values 2678 - 2j (sample
-        // 4j + 3) and 2679 - 2j (sample 4j + 1)
-        const int e = 2 * j + 4 * (j / 40);
-        const int o = kOddBase + (kSpan / 2 - 2 - 2 * j) + 4 * ((kSpanGroups - 1 - j) / 40);
-        *reinterpret_cast<float2*>(lds + e) = make_float2(span[i].x, span[i].z);
-        *reinterpret_cast<float2*>(lds + o) = make_float2(span[i].w, span[i].y);
-      }
+      span_to_lds(span, ln, lds);
       __syncthreads();
       const float4* a = reinterpret_cast<const float4*>(
           lds + ((ln & 1) ? kOddBase + 84 * (kTile - 1 - (ln >> 1)) : 84 * (ln >> 1)));
@@ -231,11 +354,11 @@ logmel_tiles_kernel(const float* __restrict__ samples,
     } else if (cur.valid) {
       // Frames of several clips (or the batch's last, partial tile): each
       // lane gathers its own 200 samples; the caches serve the overlap.
-      const float* p = samples + cur.s + (role ? 399 : 0);
+      const In* p = samples + cur.s + (role ? 399 : 0);
       const int64_t step = role ? -2 : 2;
 #pragma unroll
       for (int m = 0; m < 200; ++m) {
-        v[m] = *p;
+        v[m] = sample_value(p);
         p += step;
       }
     } else {
@@ -265,44 +388,78 @@ logmel_tiles_kernel(const float* __restrict__ samples,
     pair_logmel(P, role, o);
     const int64_t g = tile * kTile + fl;
     const int64_t row = row_lds[it & 1][ln >> 1];
-    if (g < total_frames && row >= 0 && row < out_rows) {
-      float4* dst = reinterpret_cast<float4*>(out + row * 128 + 64 * role);
-      if ((valid_mask >> lane) & 1) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          dst[i] = make_float4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
-      } else {
-        // Offsets that promise a frame the clip cannot hold: a loud row, not
-        // a silent truncation.
-        const float qnan = __builtin_nanf("");
-#pragma unroll
-        for (int i = 0; i < 16; ++i) dst[i] = make_float4(qnan, qnan, qnan, qnan);
-      }
-    }
+    if (g < total_frames && row >= 0 && row < out_rows)
+      store_bands(out + row * 128 + 64 * role, o, (valid_mask >> lane) & 1);
     if (!more) break;
     tile = next;
     cur = nxt;
   }
 }
 
+#define LOGMEL_TILES_KERNEL(NAME, IN, OUT)                                                      \
+  extern "C" __global__ void __attribute__((amdgpu_flat_work_group_size(64, 64),                \
+                                            amdgpu_waves_per_eu(1, 1)))                         \
+  NAME(const IN* __restrict__ samples, const int64_t* __restrict__ seg_start,                   \
+       const int64_t* __restrict__ seg_end, const int64_t* __restrict__ frame_off,              \
+       int64_t n_clips, int64_t total_frames, OUT* __restrict__ out,                             \
+       const int64_t* __restrict__ row_base, int64_t row_unit, int64_t out_rows,                \
+       const double* __restrict__ tables) {                                                     \
+    __shared__ float4 span_lds[(kOddBase + kParityLen + 3) / 4];                                \
+    __shared__ int64_t row_lds[2][kTile];                                                       \
+    tiles_body<IN, OUT>(samples, seg_start, seg_end, frame_off, n_clips, total_frames, out,     \
+                        row_base, row_unit, out_rows, tables,                                   \
+                        reinterpret_cast<float*>(span_lds), row_lds);                           \
+  }
+
+// samples [seg_start[i], seg_end[i]) are clip i; frame f of clip i goes to
+// row row_base[i] * row_unit + f of out ([out_rows][128]); tables: the plan's
+// window, rotations and zero pad.
+LOGMEL_TILES_KERNEL(logmel_tiles_kernel, float, float)
+LOGMEL_TILES_KERNEL(logmel_tiles_i16_kernel, int16_t, float)
+LOGMEL_TILES_KERNEL(logmel_tiles_f16out_kernel, float, _Float16)
+LOGMEL_TILES_KERNEL(logmel_tiles_i16_f16out_kernel, int16_t, _Float16)
+
 // Padding of the 30-s chunk layout: one workgroup per clip fills the rows of
 // its last chunk past its last frame, rows [chunk_off[i] * 3000 + F_i,
 // chunk_off[i + 1] * 3000), with the log of the floor (rows beyond out_rows
 // are skipped). `floor` is the fp32 1e-10 passed in at run time, so the value
-// comes from the same log instruction as a silent frame's and equals it.
-extern "C" __global__ void __launch_bounds__(256)
-logmel_chunk_pad_kernel(float* __restrict__ out, const int64_t* __restrict__ frame_off,
-                        const int64_t* __restrict__ chunk_off, int64_t out_rows, float floor)
-{
+// comes from the same log instruction as a silent frame's and equals it (and
+// rounds to the same fp16).
+template <typename Out>
+__device__ __forceinline__ void chunk_pad_body(Out* __restrict__ out,
+                                               const int64_t* __restrict__ frame_off,
+                                               const int64_t* __restrict__ chunk_off,
+                                               int64_t out_rows, float floor) {
   const float pad = __builtin_amdgcn_logf(floor) * kLn2;
   const int64_t i = blockIdx.x;
   const int64_t r0 = chunk_off[i] * 3000 + (frame_off[i + 1] - frame_off[i]);
   const int64_t r1 = min(chunk_off[i + 1] * 3000, out_rows);
   if (r0 >= r1 || r0 < 0) return;
-  float4* dst = reinterpret_cast<float4*>(out + r0 * 128);
-  const int64_t n = (r1 - r0) * 32;   // 32 float4 per row
-  const float4 v = make_float4(pad, pad, pad, pad);
-  for (int64_t k = threadIdx.x; k < n; k += 256) dst[k] = v;
+  // 16-byte stores of the value's bits (a row is 512 or 256 bytes)
+  const Out v = (Out)pad;
+  uint32_t w;
+  if constexpr (sizeof(Out) == 4) {
+    w = __builtin_bit_cast(uint32_t, v);
+  } else {
+    const uint32_t h = __builtin_bit_cast(uint16_t, v);
+    w = h | (h << 16);
+  }
+  const uint4 v4 = make_uint4(w, w, w, w);
+  uint4* dst = reinterpret_cast<uint4*>(out + r0 * 128);
+  const int64_t n = (r1 - r0) * 128 * (int64_t)sizeof(Out) / 16;
+  for (int64_t k = threadIdx.x; k < n; k += 256) dst[k] = v4;
+}
+
+extern "C" __global__ void __launch_bounds__(256)
+logmel_chunk_pad_kernel(float* __restrict__ out, const int64_t* __restrict__ frame_off,
+                        const int64_t* __restrict__ chunk_off, int64_t out_rows, float floor) {
+  chunk_pad_body<float>(out, frame_off, chunk_off, out_rows, floor);
+}
+
+extern "C" __global__ void __launch_bounds__(256)
+logmel_chunk_pad_f16_kernel(_Float16* __restrict__ out, const int64_t* __restrict__ frame_off,
+                            const int64_t* __restrict__ chunk_off, int64_t out_rows, float floor) {
+  chunk_pad_body<_Float16>(out, frame_off, chunk_off, out_rows, floor);
 }
 
 // One workgroup per stream. meta layout (int64, n = n_streams):
@@ -343,30 +500,54 @@ logmel_stream_prep_kernel(float* __restrict__ ws, int64_t row_stride,
 // ---------------------------------------------------------------------------
 // Host-side launchers, called by the C-ABI layer.
 // ---------------------------------------------------------------------------
-hipError_t logmel_launch_tiles(const double* tables, const float* samples,
+hipError_t logmel_launch_tiles(const double* tables, const void* samples, int in_i16,
                                const int64_t* seg_start, const int64_t* seg_end,
                                const int64_t* frame_off, int64_t n_clips, int64_t total_frames,
-                               float* out, const int64_t* row_base, int64_t row_unit,
+                               void* out, int out_f16, const int64_t* row_base, int64_t row_unit,
                                int64_t out_rows, int resident_waves, hipStream_t stream) {
   if (total_frames <= 0) return hipSuccess;
   const int64_t tiles = (total_frames + logmel::kTile - 1) / logmel::kTile;
   // One wavefront per SIMD is resident at a time; the grid is that many
   // wavefronts (fewer for small batches) and each walks its share of tiles.
   const int64_t grid = tiles < resident_waves ? tiles : resident_waves;
-  hipLaunchKernelGGL(logmel::logmel_tiles_kernel, dim3((unsigned)grid), dim3(logmel::kWaveLanes),
-                     0, stream, samples, seg_start, seg_end, frame_off, n_clips, total_frames, out,
-                     row_base, row_unit, out_rows, tables);
+  const dim3 g((unsigned)grid), b(logmel::kWaveLanes);
+  if (!in_i16 && !out_f16) {
+    hipLaunchKernelGGL(logmel::logmel_tiles_kernel, g, b, 0, stream,
+                       static_cast<const float*>(samples), seg_start, seg_end, frame_off, n_clips,
+                       total_frames, static_cast<float*>(out), row_base, row_unit, out_rows, tables);
+  } else if (in_i16 && !out_f16) {
+    hipLaunchKernelGGL(logmel::logmel_tiles_i16_kernel, g, b, 0, stream,
+                       static_cast<const int16_t*>(samples), seg_start, seg_end, frame_off, n_clips,
+                       total_frames, static_cast<float*>(out), row_base, row_unit, out_rows, tables);
+  } else if (!in_i16) {
+    hipLaunchKernelGGL(logmel::logmel_tiles_f16out_kernel, g, b, 0, stream,
+                       static_cast<const float*>(samples), seg_start, seg_end, frame_off, n_clips,
+                       total_frames, static_cast<_Float16*>(out), row_base, row_unit, out_rows,
+                       tables);
+  } else {
+    hipLaunchKernelGGL(logmel::logmel_tiles_i16_f16out_kernel, g, b, 0, stream,
+                       static_cast<const int16_t*>(samples), seg_start, seg_end, frame_off, n_clips,
+                       total_frames, static_cast<_Float16*>(out), row_base, row_unit, out_rows,
+                       tables);
+  }
   return hipGetLastError();
 }
 
-hipError_t logmel_launch_chunk_pad(float* out, const int64_t* frame_off, const int64_t* chunk_off,
-                                   int64_t n_clips, int64_t out_rows, hipStream_t stream) {
+hipError_t logmel_launch_chunk_pad(void* out, int out_f16, const int64_t* frame_off,
+                                   const int64_t* chunk_off, int64_t n_clips, int64_t out_rows,
+                                   hipStream_t stream) {
   // A launch covers at most 2^31 - 1 clips.
   const int64_t chunk = ((int64_t)1 << 31) - 1;
   for (int64_t c0 = 0; c0 < n_clips; c0 += chunk) {
     const int64_t n = n_clips - c0 < chunk ? n_clips - c0 : chunk;
-    hipLaunchKernelGGL(logmel::logmel_chunk_pad_kernel, dim3((unsigned)n), dim3(256), 0, stream,
-                       out, frame_off + c0, chunk_off + c0, out_rows, kLogFloor);
+    if (out_f16)
+      hipLaunchKernelGGL(logmel::logmel_chunk_pad_f16_kernel, dim3((unsigned)n), dim3(256), 0,
+                         stream, static_cast<_Float16*>(out), frame_off + c0, chunk_off + c0,
+                         out_rows, kLogFloor);
+    else
+      hipLaunchKernelGGL(logmel::logmel_chunk_pad_kernel, dim3((unsigned)n), dim3(256), 0, stream,
+                         static_cast<float*>(out), frame_off + c0, chunk_off + c0, out_rows,
+                         kLogFloor);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -17,15 +17,17 @@ static constexpr int kTabPadFloats = 5360;
 static constexpr size_t kTabBytes = 8 * kTabDoubles + 4 * kTabPadFloats;
 
 // Frame f of clip i goes to row row_base[i] * row_unit + f of out (rows at or
-// beyond out_rows are not written).
-hipError_t logmel_launch_tiles(const double* tables, const float* samples,
+// beyond out_rows are not written). samples are fp32, or int16 PCM (s / 32768)
+// with in_i16; out is fp32, or fp16 with out_f16.
+hipError_t logmel_launch_tiles(const double* tables, const void* samples, int in_i16,
                                const int64_t* seg_start, const int64_t* seg_end,
                                const int64_t* frame_off, int64_t n_clips, int64_t total_frames,
-                               float* out, const int64_t* row_base, int64_t row_unit,
+                               void* out, int out_f16, const int64_t* row_base, int64_t row_unit,
                                int64_t out_rows, int resident_waves, hipStream_t stream);
 
-hipError_t logmel_launch_chunk_pad(float* out, const int64_t* frame_off, const int64_t* chunk_off,
-                                   int64_t n_clips, int64_t out_rows, hipStream_t stream);
+hipError_t logmel_launch_chunk_pad(void* out, int out_f16, const int64_t* frame_off,
+                                   const int64_t* chunk_off, int64_t n_clips, int64_t out_rows,
+                                   hipStream_t stream);
 
 hipError_t logmel_launch_stream_prep(float* ws, int64_t row_stride, const float* fresh,
                                      const int64_t* meta, int64_t n_streams,

@@ -113,3 +113,8 @@ def test_chunk_helpers_reject_bad_input(lm):
     assert e.value.status == lm.LOGMEL_ERR_INVALID_ARGUMENT
     assert lm._compute_chunked(None, None, None, None, None, 1, 1, 1, None, None) == \
         lm.LOGMEL_ERR_INVALID_ARGUMENT
+
+
+def test_compute_ex_null_arguments(lm):
+    assert lm._compute_ex(None, None, lm.LOGMEL_F32, None, None, None, 1, 1, 0, None,
+                          lm.LOGMEL_F32, None) == lm.LOGMEL_ERR_INVALID_ARGUMENT
