@@ -11,7 +11,8 @@ batch of 64 speech-like 30 s clips (64 x 480000 fp32 samples); the timed
 loop rotates over 5 copies of input and output buffers (1.1 GB) so that
 successive steps do not hit in the 256 MB Infinity Cache.
 
-``value`` is audio-seconds per second (sum of samples / 16000 per step,
+``dtype`` names the arithmetic of the path: the window and the transform in fp64 (the filterbank
+and the log in fp32). ``value`` is audio-seconds per second (sum of samples / 16000 per step,
 divided by the wall time per step, measured between device synchronisations
 around exactly K steps). The kernel is bound by vector-ALU issue, so
 ``roofline`` is the ALU roofline: ``achieved`` is the algorithmic flops per
@@ -130,6 +131,7 @@ def make_workload(name, device):
 
 
 def bench_offline(args, lm, plan, torch):
+    import numpy as np
     dev = torch.device("cuda", 0)
     x, so, desc = make_workload(args.workload, dev)
     fo = lm.logmel_frame_offsets(so)
@@ -138,6 +140,15 @@ def bench_offline(args, lm, plan, torch):
     so_d = torch.from_numpy(so).to(dev)
     fo_d = torch.from_numpy(fo).to(dev)
     chunked = args.layout == "chunked"
+    in_i16 = args.in_dtype == "i16"
+    out_f16 = args.out_dtype == "f16"
+    if in_i16:
+        # int16 PCM of the same signal (s / 32768 is what the kernel computes on)
+        x = torch.clamp(torch.round(x * 32768.0), -32768, 32767).to(torch.int16)
+        desc += "; int16 PCM input"
+    if out_f16:
+        desc += "; fp16 output"
+    out_dtype = torch.float16 if out_f16 else torch.float32
     if chunked:
         co = lm.logmel_chunk_offsets(so)
         n_chunks = int(co[-1])
@@ -146,18 +157,24 @@ def bench_offline(args, lm, plan, torch):
         desc += "; 30-s chunk layout [chunks, 3000, 128]"
     else:
         out_rows = total
-    set_bytes = 4 * n_samples + 512 * out_rows
+    set_bytes = (2 if in_i16 else 4) * n_samples + (256 if out_f16 else 512) * out_rows
     n_sets = max(1, min(5, int(math.ceil(1.1e9 / set_bytes)))) if args.workload != "c4" else 1
     xs = [x] + [x.clone() for _ in range(n_sets - 1)]
     if chunked:
-        outs = [torch.empty((n_chunks, lm.CHUNK_FRAMES, 128), dtype=torch.float32, device=dev)
+        outs = [torch.empty((n_chunks, lm.CHUNK_FRAMES, 128), dtype=out_dtype, device=dev)
                 for _ in range(n_sets)]
     else:
-        outs = [torch.empty((total, 128), dtype=torch.float32, device=dev) for _ in range(n_sets)]
+        outs = [torch.empty((total, 128), dtype=out_dtype, device=dev) for _ in range(n_sets)]
     stream = torch.cuda.current_stream(dev)
+    general = in_i16 or out_f16
 
     def step(k):
-        if chunked:
+        if general:
+            lm.logmel_compute_ex(plan, xs[k], so_d, fo_d, total,
+                                 chunk_offsets=co_d if chunked else None,
+                                 total_chunks=n_chunks if chunked else 0, out=outs[k],
+                                 stream=stream)
+        elif chunked:
             lm.logmel_compute_chunked(plan, xs[k], so_d, fo_d, co_d, total, n_chunks, out=outs[k],
                                       stream=stream)
         else:
@@ -183,7 +200,7 @@ def bench_offline(args, lm, plan, torch):
     audio_s = n_samples / FS
     achieved_gbs = algo_bytes / kern_avg_s / 1e9
     achieved_tflops = FLOPS_PER_FRAME * total / kern_avg_s / 1e12
-    traffic = measured_traffic(args.workload) if not chunked else None
+    traffic = measured_traffic(args.workload) if not (chunked or general) else None
     rec = {
         "metric": "audio-seconds/sec of 128-bin log-mel on 1 MI355X + % of HBM roofline",
         "value": audio_s / (ms_per_step / 1e3),
@@ -195,7 +212,7 @@ def bench_offline(args, lm, plan, torch):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f64",
         "data": "synthetic",
         "config": {"workload": desc, "clips": len(so) - 1, "samples": n_samples,
                    "frames": total, "output_rows": out_rows, "buffer_sets": n_sets},
@@ -205,8 +222,10 @@ def bench_offline(args, lm, plan, torch):
         "roofline": {"bound": "alu", "achieved": achieved_tflops, "peak": ALU_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved_tflops / ALU_PEAK_TFLOPS,
                      "traffic": traffic,
-                     "kernel": ("logmel_chunk_pad_kernel + logmel_tiles_kernel" if chunked
-                                else "logmel_tiles_kernel"),
+                     "kernel": (("logmel_chunk_pad_kernel + " if chunked else "")
+                                + {(0, 0): "logmel_tiles_kernel", (1, 0): "logmel_tiles_i16_kernel",
+                                   (0, 1): "logmel_tiles_f16out_kernel",
+                                   (1, 1): "logmel_tiles_i16_f16out_kernel"}[(in_i16, out_f16)]),
                      "kernel_avg_us": kern_avg_s * 1e6,
                      "algorithmic_flops_per_launch": FLOPS_PER_FRAME * total,
                      "algorithmic_bytes_per_launch": algo_bytes,
@@ -216,6 +235,8 @@ def bench_offline(args, lm, plan, torch):
     clips_host = None
     if not args.no_cpu_baseline:
         xh = x.cpu().numpy()
+        if xh.dtype == np.int16:
+            xh = xh.astype(np.float32) / np.float32(32768.0)
         nclip = min(len(so) - 1, 64)
         if args.workload == "c4":
             # the shortest clips of the ragged batch would skew nothing; take
@@ -267,7 +288,7 @@ def bench_stream(args, lm, plan, torch):
         "unit": "audio-seconds/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "vs_baseline": None, "dtype": "f64", "data": "synthetic",
         "config": {"workload": f"streaming: 512 streams x 30 s in pushes of {P} samples "
                                f"({args.clock_ms} ms audio clock, {pushes} pushes)",
                    "streams": n, "pushes": pushes, "push_samples": P},
@@ -307,6 +328,10 @@ def main():
     ap.add_argument("--workload", default="c2", choices=["c2", "c1", "c4", "c3"])
     ap.add_argument("--clock-ms", type=int, default=80, choices=[80, 120, 160],
                     help="audio clock of the streaming workload (c3)")
+    ap.add_argument("--in-dtype", default="f32", choices=["f32", "i16"],
+                    help="sample type: fp32, or int16 PCM (the workload quantised to 16 bits)")
+    ap.add_argument("--out-dtype", default="f32", choices=["f32", "f16"],
+                    help="output type: fp32 or fp16")
     ap.add_argument("--layout", default="frames", choices=["frames", "chunked"],
                     help="output layout: [frames, 128] or 30-s chunks [chunks, 3000, 128]")
     ap.add_argument("--no-cpu-baseline", action="store_true")

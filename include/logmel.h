@@ -155,7 +155,9 @@ int logmel_compute_chunked(const logmel_plan* plan, const float* d_samples,
 
 /* The general offline call; logmel_compute and logmel_compute_chunked are
  * this call with fp32 in and out.
- *   d_samples          sample_type LOGMEL_F32 (float) or LOGMEL_I16 (int16_t)
+ *   d_samples          sample_type LOGMEL_F32 (float) or LOGMEL_I16 (int16_t);
+ *                      the buffer start must be 4-byte aligned (INVALID_ARGUMENT
+ *                      otherwise); clips may start at any sample
  *   d_chunk_offsets    NULL: the frame layout [total_frames][128]
  *                      (total_chunks unused); else the 30-s chunk layout
  *                      [total_chunks][3000][128] as in logmel_compute_chunked

@@ -244,6 +244,8 @@ int logmel_compute_ex(const logmel_plan* plan, const void* d_samples, int sample
   if (n_clips == 0 || out_rows == 0) return LOGMEL_OK;
   if (!d_samples || !d_sample_offsets || !d_frame_offsets || !d_out)
     return LOGMEL_ERR_INVALID_ARGUMENT;
+  // the kernels read samples with 4-byte aligned loads from the buffer start
+  if (reinterpret_cast<uintptr_t>(d_samples) % 4 != 0) return LOGMEL_ERR_INVALID_ARGUMENT;
   DeviceGuard g(plan->cfg.device);
   if (!g.ok) return LOGMEL_ERR_DEVICE;
   hipStream_t st = static_cast<hipStream_t>(hip_stream);

@@ -169,7 +169,9 @@ struct SpanF32 {
   f4u g[kSpanRegs];
 };
 
-__device__ __forceinline__ void load_span(const float* __restrict__ src, int lane, SpanF32& sp) {
+__device__ __forceinline__ void load_span(const float* __restrict__ base, int64_t s0, int lane,
+                                          SpanF32& sp) {
+  const float* src = base + s0;
 #pragma unroll
   for (int i = 0; i < kSpanRegs; ++i) {
     const int j = min(lane + kWaveLanes * i, kSpanGroups - 1);
@@ -204,11 +206,12 @@ struct SpanI16 {
   int odd;
 };
 
-__device__ __forceinline__ void load_span(const int16_t* __restrict__ src, int lane, SpanI16& sp) {
-  // src points at the span's first sample s0; its parity is that of the
-  // address in 2-byte units
-  const int odd = (int)((reinterpret_cast<uintptr_t>(src) >> 1) & 1);
-  const int16_t* a0 = src - odd;
+__device__ __forceinline__ void load_span(const int16_t* __restrict__ base, int64_t s0, int lane,
+                                          SpanI16& sp) {
+  // base is 4-byte aligned (the host checks), so sample s0's address is
+  // 4-byte aligned when s0 is even
+  const int odd = (int)(s0 & 1);
+  const int16_t* a0 = base + (s0 - odd);
 #pragma unroll
   for (int i = 0; i < kSpanRegs; ++i) {
     const int j = min(lane + kWaveLanes * i, kSpanGroups - 1);
@@ -327,7 +330,7 @@ __device__ __forceinline__ void tiles_body(const In* __restrict__ samples,
                             total_frames);
   if (role == 0) row_lds[0][fl] = cur.row;
   typename SpanOf<In>::type span;
-  if (cur.fast) load_span(samples + cur.s0, lane, span);
+  if (cur.fast) load_span(samples, cur.s0, lane, span);
 
   for (int it = 0;; ++it) {
     // Lane-derived LDS addresses are formed inside the loop: hoisted out of
@@ -382,7 +385,7 @@ __device__ __forceinline__ void tiles_body(const In* __restrict__ samples,
     }
     // Loaded on every path (from the plan's zero pad when there is no span
     // to fetch), so that no register merge waits for the loads here.
-    load_span(more && nxt.fast ? samples + nxt.s0 : span_pad, lane, span);
+    load_span(more && nxt.fast ? samples : span_pad, more && nxt.fast ? nxt.s0 : 0, lane, span);
 
     float o[64];
     pair_logmel(P, role, o);
