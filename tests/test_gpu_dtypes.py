@@ -164,3 +164,17 @@ def test_unsupported_types(env):
 def ctypes_ptr(t):
     import ctypes
     return ctypes.c_void_p(t.data_ptr())
+
+
+def test_misaligned_sample_buffer_rejected(env):
+    lm, plan, torch = env
+    say("int16 buffer starting 2 bytes into an allocation is rejected")
+    dev = torch.device("cuda", 0)
+    base = torch.zeros(2001, dtype=torch.int16, device=dev)
+    x = base[1:]
+    assert x.data_ptr() % 4 == 2
+    so = torch.tensor([0, 2000], dtype=torch.int64, device=dev)
+    fo = torch.tensor([0, 10], dtype=torch.int64, device=dev)
+    with pytest.raises(lm.LogmelError) as e:
+        lm.logmel_compute_ex(plan, x, so, fo, 10)
+    assert e.value.status == lm.LOGMEL_ERR_INVALID_ARGUMENT
