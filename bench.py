@@ -50,10 +50,20 @@ FS = 16000
 
 
 def kernel_source_hash():
+    """Hash of the kernel sources with comments and blank space removed, so
+    that a comment edit does not invalidate a counter summary."""
+    import re
     h = hashlib.sha256()
     for f in ("logmel_kernels.hip", "logmel_frame.h", "logmel_launch.h", "gen_tables.py"):
-        with open(os.path.join(ROOT, "log_mel_spectrogram_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "log_mel_spectrogram_amd", "csrc", f)) as fh:
+            text = fh.read()
+        if f.endswith(".py"):
+            text = re.sub(r"#[^\n]*", "", text)
+            text = re.sub(r'"""(.|\n)*?"""', "", text)
+        else:
+            text = re.sub(r"/\*(.|\n)*?\*/", "", text)
+            text = re.sub(r"//[^\n]*", "", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -102,28 +102,6 @@ __device__ __forceinline__ void dft8(cd (&v)[8]) {
   v[3] = c_add(e3, t3); v[7] = c_sub(e3, t3);
 }
 
-// In-place forward 25-point DFT, 5 x 5: n = na + 5 nb, k = 5 ka + kb.
-__device__ __forceinline__ void dft25(cd (&z)[25]) {
-  cd t[5][5];
-#pragma unroll
-  for (int na = 0; na < 5; ++na) {
-    cd a = z[na], b = z[na + 5], c = z[na + 10], d = z[na + 15], e = z[na + 20];
-    dft5(a, b, c, d, e);
-    t[na][0] = a; t[na][1] = b; t[na][2] = c; t[na][3] = d; t[na][4] = e;
-  }
-#pragma unroll
-  for (int na = 1; na < 5; ++na)
-#pragma unroll
-    for (int kb = 1; kb < 5; ++kb)
-      t[na][kb] = c_twiddle(t[na][kb], kDCos25[na * kb], kDSin25[na * kb]);
-#pragma unroll
-  for (int kb = 0; kb < 5; ++kb) {
-    cd a = t[0][kb], b = t[1][kb], c = t[2][kb], d = t[3][kb], e = t[4][kb];
-    dft5(a, b, c, d, e);
-    z[kb] = a; z[5 + kb] = b; z[10 + kb] = c; z[15 + kb] = d; z[20 + kb] = e;
-  }
-}
-
 // Forward 5-point DFT of real input: y0 real, y1 and y2 (y3 = conj y2 and
 // y4 = conj y1 are not formed).
 __device__ __forceinline__ void dft5_real(double x0, double x1, double x2, double x3, double x4,

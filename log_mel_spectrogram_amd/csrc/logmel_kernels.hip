@@ -1,6 +1,9 @@
 // HIP kernels of the log-mel front end for gfx950 (MI355X).
 //
-// logmel_tiles_kernel: the offline hot path over a packed ragged batch.
+// logmel_tiles_kernel: the offline hot path over a packed ragged batch
+//   (fp32 in, fp32 out; logmel_tiles_i16_kernel, logmel_tiles_f16out_kernel
+//   and logmel_tiles_i16_f16out_kernel are the same code for int16 PCM
+//   input and fp16 output).
 //   The flattened frame space [0, total_frames) is cut into tiles of 32
 //   consecutive frames, one frame per lane pair (role 0: even samples, role
 //   1: odd samples; see logmel_frame.h). A persistent grid of one wavefront
@@ -10,7 +13,11 @@
 //   its 5360-sample span once, coalesced, and shares it through LDS; a tile
 //   across clips lets each lane gather its own 200 samples (the caches serve
 //   the overlap). The pair's transform runs in registers and each lane
-//   writes its 64 bands once.
+//   writes its 64 bands once, at the row the caller's layout gives the frame
+//   (frame-major, or 30-s chunks).
+//
+// logmel_chunk_pad_kernel (and _f16): the padding rows of the 30-s chunk
+//   layout.
 //
 // logmel_stream_prep_kernel: the streaming push, step 1. Moves each stream's
 //   carry (the samples of its next, not yet complete frame) to sit right
