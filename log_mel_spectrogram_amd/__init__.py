@@ -173,10 +173,13 @@ class Plan:
         _check(_plan_create(ctypes.byref(cfg), ctypes.byref(h)), "logmel_plan_create")
         self.handle = h
         self.device = int(cfg.device)
+        # kept on the object: at interpreter exit the module's globals may be
+        # gone before __del__ runs
+        self._destroy = _plan_destroy
 
     def close(self):
         if getattr(self, "handle", None):
-            _plan_destroy(self.handle)
+            self._destroy(self.handle)
             self.handle = None
 
     def __del__(self):
@@ -336,10 +339,11 @@ class Stream:
         self.plan = plan
         self.n_streams = int(n_streams)
         self.max_push = int(max_push)
+        self._destroy = _stream_destroy
 
     def close(self):
         if getattr(self, "handle", None):
-            _stream_destroy(self.handle)
+            self._destroy(self.handle)
             self.handle = None
 
     def __del__(self):
