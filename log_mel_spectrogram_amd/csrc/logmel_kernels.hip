@@ -11,8 +11,9 @@
 //   while it finishes the current one. A tile may straddle clips: each pair
 //   finds its clip from the int64 frame offsets. A tile inside one clip reads
 //   its 5360-sample span once, coalesced, and shares it through LDS; a tile
-//   across clips lets each lane gather its own 200 samples (the caches serve
-//   the overlap). The pair's transform runs in registers and each lane
+//   across clips stages the spans of its clips' runs of frames in LDS the
+//   same way (up to 8 runs; beyond that each lane gathers its own 200
+//   samples). The pair's transform runs in registers and each lane
 //   writes its 64 bands once, at the row the caller's layout gives the frame
 //   (frame-major, or 30-s chunks).
 //
@@ -263,6 +264,112 @@ __device__ __forceinline__ void span_to_lds(const SpanI16& sp, int ln, float* ld
 }
 
 // ---------------------------------------------------------------------------
+// Tiles across clips. The valid frames of such a tile form pieces: runs
+// whose starts advance by exactly one hop (frames of one clip, in order).
+// They are staged in LDS like a one-clip span, in a virtual span of 160-
+// sample slots: each piece takes one slot per frame plus two spare slots
+// after its last frame, so frame f sits at slot f + 2 b(f), where b(f)
+// counts the pieces other than the first that start at or before f. A frame
+// at slot t reads virtual samples [160 t, 160 t + 400): its slot, the next
+// one and 80 samples of the one after, which hold the following frames of
+// its piece or the spare slots, all filled from the frame's own clip. With
+// at most kMaxBreaks pieces after the first, the virtual span of kPieceT
+// slots (plus half a slot) fits in LDS; tiles of more pieces, which only
+// clips shorter than about 100 ms produce, gather per lane.
+// ---------------------------------------------------------------------------
+static constexpr int kMaxBreaks = 7;
+static constexpr int kPieceT = kTile + 1 + 2 * kMaxBreaks;          // 47
+static constexpr int kPieceSpan = 160 * kPieceT + 80;               // 7600 samples
+static constexpr int kPieceGroups = kPieceSpan / 4;                 // 1900
+static constexpr int kPieceRegs = (kPieceGroups + kWaveLanes - 1) / kWaveLanes;   // 30
+static constexpr int kPieceParityLen = kPieceSpan / 2 - 1 + 4 * ((kPieceSpan / 2 - 1) / 80) + 1;
+// the odd sequence starts at the same bank offset, relative to the frames'
+// reads, as in the one-clip layout
+static constexpr int kPieceOddBase = 4024;
+static_assert(kPieceOddBase >= kPieceParityLen && kPieceOddBase % 4 == 0, "piece layout");
+static_assert((kPieceOddBase + 84 * (kPieceT - 2)) % 64 == (kOddBase + 84 * (kTile - 1)) % 64,
+              "piece layout banks");
+static constexpr int kLdsFloats =
+    (kPieceOddBase + kPieceParityLen > kOddBase + kParityLen ? kPieceOddBase + kPieceParityLen
+                                                            : kOddBase + kParityLen);
+
+// Slot t of the virtual span: samples [g, g + lim) of the batch fill its
+// first lim positions (lim = 0: nothing to fetch).
+struct __attribute__((aligned(16))) PieceSlot {
+  int64_t g;
+  int lim, pad;
+};
+
+__device__ __forceinline__ float4 load_group(const float* p) {
+  const f4u t = *reinterpret_cast<const f4u*>(p);
+  return make_float4(t.x, t.y, t.z, t.w);
+}
+__device__ __forceinline__ float4 load_group(const int16_t* p) {
+  return make_float4(sample_value(p), sample_value(p + 1), sample_value(p + 2), sample_value(p + 3));
+}
+
+// Slot of each lane's frame in the pieces layout, and the number of pieces
+// after the first (wave-uniform).
+__device__ __forceinline__ void piece_slot(const TileSrc& t, int ln, int& sigma, int& breaks) {
+  const int64_t s_prev = __shfl(t.s, ln - 2);
+  const bool v_prev = __shfl((int)t.valid, ln - 2) != 0;
+  const bool brk = t.valid && ln >= 2 && !(v_prev && t.s == s_prev + 160);
+  const uint64_t bm = __ballot(brk) & 0x5555555555555555ull;
+  breaks = __popcll(bm);
+  sigma = (ln >> 1) + 2 * __popcll(bm & ((2ull << (ln & ~1)) - 1));
+}
+
+template <typename In>
+__device__ __forceinline__ void pieces_to_lds(const In* __restrict__ samples, const TileSrc& t,
+                                              const In* __restrict__ pad, int sigma,
+                                              int ln, float* lds, PieceSlot* slots) {
+  // Slot table: clear, then each valid frame's spare slots, then its next
+  // and its own slot, each step after the last (later writes win: within a
+  // piece they give the following frames' own slots).
+  if (ln <= kPieceT) slots[ln].lim = 0;
+  __syncthreads();
+  const bool w = !(ln & 1) && t.valid;
+  if (w) slots[sigma + 2] = PieceSlot{t.s + 320, 80, 0};
+  __syncthreads();
+  if (w) slots[sigma + 1] = PieceSlot{t.s + 160, 160, 0};
+  __syncthreads();
+  if (w) slots[sigma] = PieceSlot{t.s, 160, 0};
+  __syncthreads();
+  // One 16-byte read per slot (start and count together), all issued before
+  // the first is used.
+  int4 sl[kPieceRegs];
+#pragma unroll
+  for (int i = 0; i < kPieceRegs; ++i) {
+    const int j = min(ln + kWaveLanes * i, kPieceGroups - 1);
+    sl[i] = *reinterpret_cast<const int4*>(slots + j / 40);
+  }
+#pragma unroll
+  for (int i = 0; i < kPieceRegs; ++i) asm volatile("" : "+v"(sl[i].x), "+v"(sl[i].y), "+v"(sl[i].z));
+  // Group j (samples 4j .. 4j + 3 of the virtual span) lies in slot j / 40;
+  // positions past the slot's samples read zeros from the pad, so every
+  // lane loads and none waits alone.
+  const In* src[kPieceRegs];
+#pragma unroll
+  for (int i = 0; i < kPieceRegs; ++i) {
+    const int j = min(ln + kWaveLanes * i, kPieceGroups - 1);
+    const int off = 4 * j - 160 * (j / 40);
+    const int64_t g = (int64_t)(((uint64_t)(uint32_t)sl[i].y << 32) | (uint32_t)sl[i].x);
+    src[i] = off < sl[i].z ? samples + g + off : pad;
+  }
+  float4 val[kPieceRegs];
+#pragma unroll
+  for (int i = 0; i < kPieceRegs; ++i) val[i] = load_group(src[i]);
+#pragma unroll
+  for (int i = 0; i < kPieceRegs; ++i) {
+    const int j = min(ln + kWaveLanes * i, kPieceGroups - 1);
+    const int e = par_pos(2 * j);
+    const int o = kPieceOddBase + par_pos(kPieceSpan / 2 - 2 - 2 * j);
+    *reinterpret_cast<float2*>(lds + e) = make_float2(val[i].x, val[i].z);
+    *reinterpret_cast<float2*>(lds + o) = make_float2(val[i].w, val[i].y);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Output types: fp32, or fp16 (each value rounded once to nearest).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void store_bands(float* __restrict__ dst, const float (&o)[64], bool ok) {
@@ -317,7 +424,8 @@ __device__ __forceinline__ void tiles_body(const In* __restrict__ samples,
                                            const int64_t* __restrict__ row_base,
                                            int64_t row_unit, int64_t out_rows,
                                            const double* __restrict__ tables,
-                                           float* lds, int64_t (&row_lds)[2][kTile]) {
+                                           float* lds, int64_t (&row_lds)[2][kTile],
+                                           PieceSlot* slots) {
   // a readable stand-in for a span when there is none to fetch (zeros)
   const In* span_pad = reinterpret_cast<const In*>(tables + kTabDoubles);
   const RowMap rows{row_base, row_unit};
@@ -346,6 +454,7 @@ __device__ __forceinline__ void tiles_body(const In* __restrict__ samples,
     asm volatile("" : "+v"(ln));
     // This lane's 200 samples: x[s + 2m] for role 0, x[s + 399 - 2m] for role 1.
     float v[200];
+    int sigma, breaks;
     if (cur.fast) {
       // Split the span by parity into LDS (layout above), then read back this
       // lane's 200 values.
@@ -361,9 +470,24 @@ __device__ __forceinline__ void tiles_body(const In* __restrict__ samples,
         v[4 * q + 2] = t.z;
         v[4 * q + 3] = t.w;
       }
+    } else if (piece_slot(cur, ln, sigma, breaks), breaks <= kMaxBreaks) {
+      // Tiles across clips (and the batch's last, partial tile): the same
+      // through the pieces layout.
+      pieces_to_lds(samples, cur, span_pad, sigma, ln, lds, slots);
+      __syncthreads();
+      const float4* a = reinterpret_cast<const float4*>(
+          lds + ((ln & 1) ? kPieceOddBase + 84 * (kPieceT - 2 - sigma) : 84 * sigma));
+#pragma unroll
+      for (int q = 0; q < 50; ++q) {
+        const float4 t = a[q + q / 20];
+        v[4 * q] = t.x;
+        v[4 * q + 1] = t.y;
+        v[4 * q + 2] = t.z;
+        v[4 * q + 3] = t.w;
+      }
     } else if (cur.valid) {
-      // Frames of several clips (or the batch's last, partial tile): each
-      // lane gathers its own 200 samples; the caches serve the overlap.
+      // Frames of more than kMaxBreaks + 1 pieces: each lane gathers its own
+      // 200 samples; the caches serve the overlap.
       const In* p = samples + cur.s + (role ? 399 : 0);
       const int64_t step = role ? -2 : 2;
 #pragma unroll
@@ -414,11 +538,12 @@ __device__ __forceinline__ void tiles_body(const In* __restrict__ samples,
        int64_t n_clips, int64_t total_frames, OUT* __restrict__ out,                             \
        const int64_t* __restrict__ row_base, int64_t row_unit, int64_t out_rows,                \
        const double* __restrict__ tables) {                                                     \
-    __shared__ float4 span_lds[(kOddBase + kParityLen + 3) / 4];                                \
+    __shared__ float4 span_lds[(kLdsFloats + 3) / 4];                                           \
     __shared__ int64_t row_lds[2][kTile];                                                       \
+    __shared__ PieceSlot slots[kPieceT + 1];                                                    \
     tiles_body<IN, OUT>(samples, seg_start, seg_end, frame_off, n_clips, total_frames, out,     \
                         row_base, row_unit, out_rows, tables,                                   \
-                        reinterpret_cast<float*>(span_lds), row_lds);                           \
+                        reinterpret_cast<float*>(span_lds), row_lds, slots);                    \
   }
 
 // samples [seg_start[i], seg_end[i]) are clip i; frame f of clip i goes to

@@ -82,6 +82,28 @@ def test_int16_equals_fp32_and_oracle(env):
     say(f"int16 edge batch: {rep}")
 
 
+def test_int16_short_clips(env):
+    """Tiles across short clips (odd and even starts) staged from int16."""
+    lm, plan, torch = env
+    say("int16: short clips")
+    rng = np.random.default_rng(43)
+    lens = [0 if f == 0 else 160 * (int(f) - 1) + 400 + int(rng.integers(0, 160))
+            for f in rng.integers(0, 10, 300)]
+    so = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    s16 = int16_batch(lens, 44)
+    x32 = s16.astype(np.float32) / np.float32(32768.0)
+    fo, co, so_d, fo_d, co_d = offsets(env, so)
+    dev = torch.device("cuda", 0)
+    T = int(fo[-1])
+    o16 = lm.logmel_compute_ex(plan, torch.from_numpy(s16).to(dev), so_d, fo_d, T)
+    o32 = lm.logmel_compute_ex(plan, torch.from_numpy(x32).to(dev), so_d, fo_d, T)
+    torch.cuda.synchronize()
+    assert torch.equal(o16, o32), "int16 != fp32"
+    L, E, _ = O.logmel_packed(x32, so)
+    rep = assert_parity(o16.cpu().numpy(), L, E, "int16 short clips")
+    say(f"int16 short clips: {rep}")
+
+
 def test_int16_config2_quantised(env):
     lm, plan, torch = env
     say("int16: config2 quantised to 16 bits, bitwise against fp32")

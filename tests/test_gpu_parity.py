@@ -88,6 +88,40 @@ def test_many_boundaries_in_one_tile(env):
     check_against_oracle(env, x, so, "many boundaries per tile")
 
 
+def short_clip_lengths(rng):
+    """Clips of 0 to 40 frames: runs of 2, 3, 4 and 8-frame clips (tiles of
+    up to 8 clip pieces are staged in LDS, more gather per lane), random
+    mixes with odd leftovers, empty and sub-frame clips between them."""
+    def clip(frames):
+        return 0 if frames == 0 else 160 * (frames - 1) + 400 + int(rng.integers(0, 160))
+    lens = []
+    for frames, count in [(4, 40), (3, 40), (8, 20), (2, 30), (1, 10)]:
+        lens += [clip(frames) for _ in range(count)]
+    lens += [clip(int(f)) for f in rng.integers(0, 13, 80)]
+    lens += [int(n) for n in rng.integers(0, 400, 10)]
+    lens += [clip(int(f)) for f in rng.integers(30, 41, 10)]
+    order = rng.permutation(len(lens) - 50)
+    return [lens[i] for i in order] + lens[-50:]
+
+
+def test_short_clips_staged_across_clips(env):
+    """Tiles across many short clips: every frame against the oracle, and bit
+    for bit the frames of the same clip computed alone (a one-clip call)."""
+    import torch
+    rng = np.random.default_rng(26)
+    lens = short_clip_lengths(rng)
+    so = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    x = torch.from_numpy((0.5 * rng.normal(size=int(so[-1]))).clip(-1, 1).astype(np.float32))
+    Lg, L, E = check_against_oracle(env, x, so, f"{len(lens)} short clips")
+    fo = O.frame_offsets(so)
+    say("short clips, each alone")
+    for i in range(len(lens)):
+        if fo[i + 1] == fo[i]:
+            continue
+        alone, _ = run_gpu(env, x[so[i]:so[i + 1]], np.array([0, lens[i]], dtype=np.int64))
+        assert np.array_equal(alone, Lg[fo[i]:fo[i + 1]]), f"clip {i} ({lens[i]} samples)"
+
+
 def test_random_ragged_batch(env):
     import torch
     rng = np.random.default_rng(23)
