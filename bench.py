@@ -104,9 +104,10 @@ def cpu_baseline(clips, seconds):
     audio_per_pass = sum(c.size for c in clips) / FS
     with ctx.Pool(cores) as pool:
         pool.map(_oracle_worker, [(clips[i % len(clips)], 1) for i in range(cores)])  # warm
+        # calibrate on a few passes (one pass is too short against the pool's overhead)
         t0 = time.perf_counter()
-        pool.map(_oracle_worker, [(c, 1) for c in clips])
-        one = time.perf_counter() - t0
+        pool.map(_oracle_worker, [(c, 4) for c in clips])
+        one = (time.perf_counter() - t0) / 4
         reps = max(1, int(seconds / max(one, 1e-3)))
         t0 = time.perf_counter()
         pool.map(_oracle_worker, [(c, reps) for c in clips])
