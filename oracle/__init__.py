@@ -11,4 +11,6 @@ from .logmel_oracle import (  # noqa: F401
     mel_vertices_hz, mel_filterbank, frames_of, power_spectrum, mel_energy,
     log_compress, logmel_frames, logmel_clip, logmel_packed, logmel_selected,
     num_chunks, chunk_offsets, chunk_frames, logmel_chunked,
+    RESAMPLE_ZEROS, RESAMPLE_ROLLOFF, RESAMPLE_BETA, resample_length, resample_offsets,
+    resample_cutoff, resample_halfwidth, resample_kernel, resample_clip, resample_packed,
 )

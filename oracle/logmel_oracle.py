@@ -45,6 +45,23 @@ that start in seconds 30 j .. 30 j + 30), so chunking never changes a frame;
 the rows of the last chunk past the clip's last frame hold ln(1e-10), the
 value the recipe gives silence; a clip with no frame has no chunk.
 
+Resampling to 16 kHz (page 1, §6, the offline example in "可运行代码示例":
+the processor takes 16 kHz input only and the example refuses other rates,
+noting that a library resampler would be used in practice; page 1, §2.1:
+speech content of interest lies below 8 kHz, hence 16 kHz). The pages name
+no method. Reading: band-limited interpolation with a Kaiser-windowed sinc
+(the textbook method of J. O. Smith's bandlimited interpolation). Output
+sample n sits at time n / 16000 s, that is at input position
+p = n R / 16000 for input rate R, and
+    y[n] = sum_k x[k] h(p - k),   over the clip's samples k (zero outside),
+    h(d) = (2 fc / R) sinc(2 fc d / R) kaiser(d / H),  |d| < H,  else 0,
+with cutoff fc = 0.96 min(R, 16000) / 2, half-width H = 24 R / (2 fc) input
+samples (24 zero crossings of the sinc on each side), kaiser(r) =
+I0(9 sqrt(1 - r^2)) / I0(9). A clip of N samples gives ceil(16000 N / R)
+output samples (those with p < N). At R = 16000 nothing is resampled: the
+output is the input. These parameters are a reading; nothing in the pages
+fixes them.
+
 Everything here is fp64. The fp32 samples are upcast exactly.
 """
 
@@ -259,3 +276,88 @@ def logmel_chunked(samples: np.ndarray, sample_offsets):
             rows = Li[CHUNK_FRAMES * j:CHUNK_FRAMES * (j + 1)]
             out[co[i] + j, :rows.shape[0]] = rows
     return out, co
+
+
+# ---------------------------------------------------------------------------
+# Resampling to 16 kHz (see the reading in the module docstring)
+# ---------------------------------------------------------------------------
+
+RESAMPLE_ZEROS = 24        # zero crossings of the sinc on each side
+RESAMPLE_ROLLOFF = 0.96    # cutoff as a fraction of the lower Nyquist frequency
+RESAMPLE_BETA = 9.0        # Kaiser window shape
+
+
+def resample_length(n_samples: int, rate: int) -> int:
+    """Output samples of a clip of ``n_samples`` at ``rate`` Hz: the n >= 0
+    with n rate < 16000 n_samples, i.e. ceil(16000 N / R)."""
+    return -(-int(n_samples) * SAMPLE_RATE // int(rate))
+
+
+def resample_offsets(sample_offsets, rate: int) -> np.ndarray:
+    """Exclusive prefix sum of per-clip output lengths, int64."""
+    so = np.asarray(sample_offsets, dtype=np.int64).reshape(-1)
+    n = [resample_length(int(so[i + 1] - so[i]), rate) for i in range(so.size - 1)]
+    return np.concatenate([[0], np.cumsum(np.asarray(n, dtype=np.int64))]).astype(np.int64)
+
+
+def resample_cutoff(rate: int) -> float:
+    """Cutoff fc in Hz."""
+    return RESAMPLE_ROLLOFF * min(int(rate), SAMPLE_RATE) / 2.0
+
+
+def resample_halfwidth(rate: int) -> float:
+    """Half-width H of the kernel in input samples."""
+    return RESAMPLE_ZEROS * int(rate) / (2.0 * resample_cutoff(rate))
+
+
+def resample_kernel(d, rate: int) -> np.ndarray:
+    """h(d) for offsets d (input samples, fp64): the windowed sinc above.
+    ``numpy.sinc`` and ``numpy.i0`` are the library primitives."""
+    d = np.asarray(d, dtype=np.float64)
+    fc = resample_cutoff(rate)
+    H = resample_halfwidth(rate)
+    r = d / H
+    inside = np.abs(r) < 1.0
+    win = np.i0(RESAMPLE_BETA * np.sqrt(np.where(inside, 1.0 - r * r, 0.0))) / np.i0(RESAMPLE_BETA)
+    return np.where(inside, (2.0 * fc / rate) * np.sinc(2.0 * fc * d / rate) * win, 0.0)
+
+
+def resample_clip(x: np.ndarray, rate: int):
+    """One clip resampled to 16 kHz: (y fp64 [ceil(16000 N / R)], a) where
+    a[n] = sum_k |x[k] h(p - k)| (the scale of output n's rounding).
+
+    The position of output n is p = n R / 16000, kept exact as the integer
+    part q = floor(n R / 16000) and the remainder n R mod 16000."""
+    x = np.asarray(x, dtype=np.float64)
+    N = x.size
+    rate = int(rate)
+    n_out = resample_length(N, rate)
+    if rate == SAMPLE_RATE:
+        return x.copy(), np.abs(x)
+    n = np.arange(n_out, dtype=np.int64)
+    q = (n * rate) // SAMPLE_RATE
+    frac = ((n * rate) % SAMPLE_RATE) / SAMPLE_RATE
+    J = int(np.ceil(resample_halfwidth(rate)))
+    y = np.zeros(n_out)
+    a = np.zeros(n_out)
+    for j in range(-J, J + 1):
+        k = q + j
+        ok = (k >= 0) & (k < N)
+        h = resample_kernel(frac - j, rate)
+        t = np.where(ok, x[np.clip(k, 0, max(N - 1, 0))] if N else 0.0, 0.0) * h
+        y += t
+        a += np.abs(t)
+    return y, a
+
+
+def resample_packed(samples: np.ndarray, sample_offsets, rate: int):
+    """A packed batch resampled clip by clip: (y fp64, out_offsets, a)."""
+    so = np.asarray(sample_offsets, dtype=np.int64).reshape(-1)
+    oo = resample_offsets(so, rate)
+    y = np.zeros(int(oo[-1]))
+    a = np.zeros(int(oo[-1]))
+    for i in range(so.size - 1):
+        yi, ai = resample_clip(samples[so[i]:so[i + 1]], rate)
+        y[oo[i]:oo[i + 1]] = yi
+        a[oo[i]:oo[i + 1]] = ai
+    return y, oo, a

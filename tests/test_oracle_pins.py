@@ -440,3 +440,152 @@ def test_stream_schedule_and_carry(push, first, steady):
         carry = n - 160 * F
         assert carry == 320 == 240 + ((n - 400) % 160)
         assert O.num_frames(n) == F
+
+
+# ------------------------------------------------------- resampling to 16 kHz
+#
+# The pages name no resampling method (the reading is in the oracle's
+# docstring); these pin the oracle's resampler to what band-limited
+# interpolation must do whatever its parameters: exact output counts, the
+# time base (an output sample sits at n / 16000 s), passband tones kept,
+# out-of-band tones removed, zero padding at clip edges, and the window.
+
+RATES = [8000, 11025, 22050, 24000, 32000, 44100, 48000, 96000]
+
+
+def _interior(rate, n_in, n_out):
+    """Outputs whose kernel support lies inside the clip."""
+    H = O.resample_halfwidth(rate)
+    n = np.arange(n_out)
+    p = n * rate / 16000
+    return (p - H >= 0) & (p + H <= n_in - 1)
+
+
+@pytest.mark.parametrize("rate", RATES)
+def test_resample_length_brute(rate):
+    rng = np.random.default_rng(rate)
+    for N in list(range(0, 40)) + list(rng.integers(0, 100000, 30)):
+        N = int(N)
+        brute = 0
+        while brute * rate < 16000 * N:     # output n exists iff its time n/16000 < N/rate
+            brute += 1
+        assert O.resample_length(N, rate) == brute, (rate, N)
+    lens = rng.integers(0, 5000, 20)
+    so = np.concatenate([[0], np.cumsum(lens)])
+    oo = O.resample_offsets(so, rate)
+    assert oo[0] == 0 and np.array_equal(np.diff(oo), [O.resample_length(int(n), rate) for n in lens])
+
+
+def test_resample_16k_is_identity():
+    x = np.random.default_rng(1).standard_normal(1234)
+    y, a = O.resample_clip(x, 16000)
+    assert np.array_equal(y, x)
+
+
+@pytest.mark.parametrize("rate", [8000, 22050, 32000, 44100, 48000, 96000])
+def test_resample_passband_tones(rate):
+    """A tone well inside the passband comes out as the same tone sampled at
+    16 kHz (amplitude and phase), away from the clip edges."""
+    n_in = rate // 2
+    k = np.arange(n_in)
+    top = 3000.0 if rate < 16000 else 6000.0
+    for f in (300.0, 1000.0, top):
+        th = 0.7
+        x = np.sin(2 * np.pi * f * k / rate + th)
+        y, _ = O.resample_clip(x, rate)
+        n = np.arange(y.size)
+        ref = np.sin(2 * np.pi * f * n / 16000 + th)
+        m = _interior(rate, n_in, y.size)
+        assert m.sum() > 1000
+        assert np.abs(y - ref)[m].max() < 1e-3, (rate, f)
+
+
+@pytest.mark.parametrize("rate,f", [(48000, 9000.0), (48000, 12000.0), (44100, 15000.0),
+                                    (96000, 30000.0), (22050, 10000.0)])
+def test_resample_stopband_tones(rate, f):
+    """A tone above 8 kHz (which would alias into the 16 kHz band) is removed."""
+    n_in = rate // 2
+    x = np.sin(2 * np.pi * f * np.arange(n_in) / rate)
+    y, _ = O.resample_clip(x, rate)
+    m = _interior(rate, n_in, y.size)
+    assert np.abs(y[m]).max() < 1e-4, (rate, f)
+
+
+@pytest.mark.parametrize("rate", [8000, 44100, 48000])
+def test_resample_dc_gain(rate):
+    y, _ = O.resample_clip(np.ones(rate // 4), rate)
+    m = _interior(rate, rate // 4, y.size)
+    assert np.abs(y[m] - 1.0).max() < 1e-4
+
+
+@pytest.mark.parametrize("rate,k0,n0", [(48000, 3 * 500, 500), (44100, 441 * 4, 160 * 4),
+                                        (8000, 700, 1400), (22050, 441 * 2, 320 * 2)])
+def test_resample_impulse_time_base(rate, k0, n0):
+    """An impulse at input sample k0 whose time k0/R equals output time
+    n0/16000 gives an output symmetric about n0 with its peak there (the
+    kernel is even): pins the time base and the index arithmetic."""
+    x = np.zeros(4 * k0)
+    x[k0] = 1.0
+    y, _ = O.resample_clip(x, rate)
+    assert k0 * 16000 == n0 * rate
+    assert int(np.argmax(y)) == n0
+    d = np.arange(1, 200)
+    np.testing.assert_allclose(y[n0 + d], y[n0 - d], rtol=0, atol=1e-15)
+    # the peak is the kernel's centre value 2 fc / R (the window is 1 there)
+    assert y[n0] == pytest.approx(2 * O.resample_cutoff(rate) / rate, rel=1e-14)
+
+
+@pytest.mark.parametrize("rate", [11025, 44100, 48000, 24000])
+def test_resample_shift_and_zero_edges(rate):
+    """Delaying the input by M = R / gcd(R, 16000) samples delays the output
+    by L = 16000 / gcd samples exactly; a clip's output equals the output of
+    the same clip with zeros around it (samples outside a clip are zero)."""
+    g = math.gcd(rate, 16000)
+    M, L = rate // g, 16000 // g
+    x = np.random.default_rng(rate).uniform(-1, 1, 3000 + rate // 50)
+    y, _ = O.resample_clip(x, rate)
+    P = 2 * (int(O.resample_halfwidth(rate)) // M + 2)
+    xz = np.concatenate([np.zeros(P * M), x, np.zeros(P * M)])
+    yz, _ = O.resample_clip(xz, rate)
+    np.testing.assert_array_equal(yz[P * L: P * L + y.size], y)
+    assert yz.size == y.size + 2 * P * L
+
+
+def test_resample_kernel_against_library_window_and_sinc_zeros():
+    """The window is numpy's Kaiser window sampled over the support; the
+    kernel vanishes at the sinc's zero crossings and peaks at 2 fc / R."""
+    for rate in (44100, 48000, 8000):
+        fc = O.resample_cutoff(rate)
+        H = O.resample_halfwidth(rate)
+        K = 50
+        r = (np.arange(2 * K + 1) - K) / K          # window positions in [-1, 1]
+        d = r * H
+        sinc = np.sinc(2 * fc * d / rate)
+        with np.errstate(invalid="ignore", divide="ignore"):
+            win = O.resample_kernel(d, rate) / ((2 * fc / rate) * sinc)
+        ok = (np.abs(sinc) > 1e-6) & (np.abs(r) < 1)
+        np.testing.assert_allclose(win[ok], np.kaiser(2 * K + 1, O.RESAMPLE_BETA)[ok], rtol=1e-12)
+        m = np.arange(1, O.RESAMPLE_ZEROS)
+        zeros = m * rate / (2 * fc)
+        assert np.abs(O.resample_kernel(zeros, rate)).max() < 1e-15
+        assert np.abs(O.resample_kernel(-zeros, rate)).max() < 1e-15
+        assert O.resample_kernel(0.0, rate) == pytest.approx(2 * fc / rate, rel=1e-15)
+        assert O.resample_kernel(H, rate) == 0.0 and O.resample_kernel(-H * 1.0001, rate) == 0.0
+
+
+@pytest.mark.parametrize("rate", [8000, 44100, 48000])
+def test_resample_half_gain_at_cutoff(rate):
+    """A windowed sinc's transition is centred on its cutoff, where the gain
+    is one half: pins the cutoff at 0.96 of the lower Nyquist frequency
+    (7680 Hz into 16 kHz, 3840 Hz out of 8 kHz)."""
+    f = 0.96 * min(rate, 16000) / 2
+    n_in = rate
+    x = np.sin(2 * np.pi * f * np.arange(n_in) / rate)
+    y, _ = O.resample_clip(x, rate)
+    m = _interior(rate, n_in, y.size)
+    n = np.arange(y.size)[m]
+    # amplitude by projection on the tone at 16 kHz
+    c = np.cos(2 * np.pi * f * n / 16000)
+    s = np.sin(2 * np.pi * f * n / 16000)
+    A = np.hypot(np.dot(y[m], c), np.dot(y[m], s)) / (0.5 * n.size)
+    assert A == pytest.approx(0.5, abs=0.01), (rate, A)
