@@ -219,6 +219,60 @@ int64_t logmel_stream_state_bytes(const logmel_stream* s);
 int logmel_stream_get_state(logmel_stream* s, void* state_host, void* hip_stream);
 int logmel_stream_set_state(logmel_stream* s, const void* state_host, void* hip_stream);
 
+/* ---------------------------------------------------------------------------
+ * Resampling to 16 kHz, the step before the front end for audio at another
+ * rate. The pages require 16 kHz input (page 1, §6, the offline example in
+ * "可运行代码示例": other rates are refused, with a library resampler named
+ * for real use; page 1, §2.1: 16 kHz because speech content of interest lies
+ * below 8 kHz). They name no method; this library's reading is band-limited
+ * interpolation with a Kaiser-windowed sinc (J. O. Smith's bandlimited
+ * interpolation): output sample n of a clip sits at input position
+ * p = n R / 16000 (R the input rate) and is
+ *   y[n] = sum_k x[k] h(p - k) over the clip's samples (zero outside it),
+ *   h(d) = (2 fc / R) sinc(2 fc d / R) I0(9 sqrt(1 - (d/H)^2)) / I0(9), |d| < H,
+ * with cutoff fc = 0.96 min(R, 16000) / 2 Hz and half-width
+ * H = 24 R / (2 fc) input samples (24 zero crossings each side). A clip of
+ * N samples gives ceil(16000 N / R) outputs. At R = 16000 the output is the
+ * input. The taps are computed in fp64 and rounded to fp32; each output is
+ * an fp32 dot product of at most 2 ceil(H) + 1 terms.
+ * --------------------------------------------------------------------------- */
+#define LOGMEL_RESAMPLE_ZEROS 24
+
+/* Output length for n_samples at in_rate Hz: ceil(16000 n / in_rate); -1 for
+ * a negative length, a rate outside [1000, 384000], or n above INT64_MAX / 16000. */
+int64_t logmel_resample_length(int64_t n_samples, int32_t in_rate);
+
+/* Exclusive prefix sum of per-clip output lengths (host arrays of
+ * n_clips + 1 int64). INVALID_ARGUMENT for offsets that do not start at 0 or
+ * decrease; UNSUPPORTED for a rate outside [1000, 384000]. */
+int logmel_resample_offsets(int32_t in_rate, const int64_t* sample_offsets_host, int64_t n_clips,
+                            int64_t* out_offsets_host);
+
+/* A resampler for one input rate: owns the device taps table ([L][2J + 1]
+ * fp32 with 16000 / R = L / M in lowest terms). UNSUPPORTED for rates outside
+ * [1000, 384000] and for rates with so many phases that the table does not
+ * fit the kernel's LDS (it holds every common rate: 8000, 11025, 12000,
+ * 16000, 22050, 24000, 32000, 44100, 48000, 88200, 96000, 176400, 192000). */
+typedef struct logmel_resampler logmel_resampler;
+int logmel_resampler_create(const logmel_plan* plan, int32_t in_rate, logmel_resampler** out);
+void logmel_resampler_destroy(logmel_resampler* r);
+/* Phase count L and taps per phase (2J + 1) of a resampler. */
+int logmel_resampler_info(const logmel_resampler* r, int64_t* phases, int64_t* taps_per_phase);
+
+/* Resamples a packed batch of clips to 16 kHz.
+ *   d_samples          fp32 or int16 PCM (sample_type LOGMEL_F32 / LOGMEL_I16;
+ *                      int16 s means s / 32768), clips packed back to back
+ *   d_sample_offsets   int64 [n_clips + 1], clip i = [so[i], so[i+1])
+ *   d_out_offsets      int64 [n_clips + 1] from logmel_resample_offsets()
+ *   d_out              fp32 [total_out], clip i's output at [oo[i], oo[i+1]);
+ *                      it is itself a packed 16 kHz batch for logmel_compute
+ *                      with d_out_offsets as its sample offsets
+ * One kernel launch on hip_stream; the offsets are a precondition, checked
+ * only with LOGMEL_VALIDATE=1 (one synchronisation). */
+int logmel_resample(const logmel_resampler* r, const void* d_samples, int sample_type,
+                    const int64_t* d_sample_offsets, const int64_t* d_out_offsets,
+                    int64_t n_clips, int64_t total_out, float* d_out, void* hip_stream);
+
 const char* logmel_status_string(int status);
 
 /* Version of this ABI, for binding checks. */

@@ -83,6 +83,15 @@ _stream_counters = _sig("logmel_stream_counters", ctypes.c_int, _p, _i64, _i64p,
 _stream_state_bytes = _sig("logmel_stream_state_bytes", _i64, _p)
 _stream_get_state = _sig("logmel_stream_get_state", ctypes.c_int, _p, _p, _p)
 _stream_set_state = _sig("logmel_stream_set_state", ctypes.c_int, _p, _p, _p)
+_resample_length = _sig("logmel_resample_length", _i64, _i64, ctypes.c_int32)
+_resample_offsets = _sig("logmel_resample_offsets", ctypes.c_int, ctypes.c_int32, _i64p, _i64,
+                         _i64p)
+_resampler_create = _sig("logmel_resampler_create", ctypes.c_int, _p, ctypes.c_int32,
+                         ctypes.POINTER(_p))
+_resampler_destroy = _sig("logmel_resampler_destroy", None, _p)
+_resampler_info = _sig("logmel_resampler_info", ctypes.c_int, _p, _i64p, _i64p)
+_resample = _sig("logmel_resample", ctypes.c_int, _p, _p, ctypes.c_int, _p, _p, _i64, _i64, _p,
+                 _p)
 
 EXPORTED = [
     "logmel_default_config", "logmel_abi_version", "logmel_status_string",
@@ -91,7 +100,9 @@ EXPORTED = [
     "logmel_compute_chunked", "logmel_compute_ex", "logmel_stream_create",
     "logmel_stream_destroy", "logmel_stream_reset", "logmel_stream_frames_for_push",
     "logmel_stream_push", "logmel_stream_counters", "logmel_stream_state_bytes",
-    "logmel_stream_get_state", "logmel_stream_set_state",
+    "logmel_stream_get_state", "logmel_stream_set_state", "logmel_resample_length",
+    "logmel_resample_offsets", "logmel_resampler_create", "logmel_resampler_destroy",
+    "logmel_resampler_info", "logmel_resample",
 ]
 
 
@@ -418,3 +429,96 @@ def logmel_stream_set_state(s: Stream, state: bytes, stream=None):
     buf = ctypes.create_string_buffer(state, len(state))
     st = _stream_handle(stream, None)
     _check(_stream_set_state(s.handle, ctypes.cast(buf, _p), st), "logmel_stream_set_state")
+
+
+# ------------------------------------------------------- resampling to 16 kHz
+
+def logmel_resample_length(n_samples: int, in_rate: int) -> int:
+    """ceil(16000 n / in_rate); -1 for an unsupported rate or length."""
+    return int(_resample_length(int(n_samples), int(in_rate)))
+
+
+def logmel_resample_offsets(sample_offsets, in_rate: int) -> np.ndarray:
+    """Exclusive prefix sum of the clips' 16 kHz output lengths (int64)."""
+    so = _i64_array(sample_offsets)
+    if so.size < 1:
+        raise LogmelError(LOGMEL_ERR_INVALID_ARGUMENT, "logmel_resample_offsets")
+    oo = np.zeros(so.size, dtype=np.int64)
+    _check(_resample_offsets(int(in_rate), _ptr64(so), so.size - 1, _ptr64(oo)),
+           "logmel_resample_offsets")
+    return oo
+
+
+class Resampler:
+    """Owns a logmel_resampler handle (one input rate)."""
+
+    def __init__(self, plan: Plan, in_rate: int):
+        h = _p()
+        _check(_resampler_create(plan.handle, int(in_rate), ctypes.byref(h)),
+               "logmel_resampler_create")
+        self.handle = h
+        self.plan = plan
+        self.rate = int(in_rate)
+        self._destroy = _resampler_destroy
+
+    def close(self):
+        if getattr(self, "handle", None):
+            self._destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        self.close()
+
+
+def logmel_resampler_create(plan: Plan, in_rate: int) -> Resampler:
+    return Resampler(plan, in_rate)
+
+
+def logmel_resampler_destroy(r: Resampler):
+    r.close()
+
+
+def logmel_resampler_info(r: Resampler):
+    """(phases L, taps per phase)."""
+    a, b = _i64(), _i64()
+    _check(_resampler_info(r.handle, ctypes.byref(a), ctypes.byref(b)), "logmel_resampler_info")
+    return int(a.value), int(b.value)
+
+
+def logmel_resample(r: Resampler, samples, sample_offsets, out_offsets, total_out: int,
+                    out=None, stream=None):
+    """Resamples a packed batch (fp32 or int16 samples, int64 offsets on the
+    device) to 16 kHz; returns out fp32 [total_out]."""
+    torch = _torch()
+    n_clips = int(sample_offsets.numel()) - 1
+    if samples.dtype == torch.float32:
+        st_in = LOGMEL_F32
+    elif samples.dtype == torch.int16:
+        st_in = LOGMEL_I16
+    else:
+        raise TypeError(f"samples must be float32 or int16, got {samples.dtype}")
+    if out is None:
+        out = torch.empty(int(total_out), dtype=torch.float32, device=samples.device)
+    if tuple(out.shape) != (int(total_out),):
+        raise ValueError(f"out must be [{total_out}]")
+    if out_offsets.numel() != n_clips + 1:
+        raise ValueError("out_offsets must have n_clips + 1 entries")
+    st = _stream_handle(stream, samples.device)
+    _check(_resample(r.handle, _dev_ptr(samples, samples.dtype, "samples"), st_in,
+                     _dev_ptr(sample_offsets, torch.int64, "sample_offsets"),
+                     _dev_ptr(out_offsets, torch.int64, "out_offsets"), n_clips, int(total_out),
+                     _dev_ptr(out, torch.float32, "out"), st),
+           "logmel_resample")
+    return out
+
+
+def resample(r: Resampler, samples, sample_offsets_host, stream=None):
+    """Convenience: host int64 sample offsets in; returns (16 kHz samples,
+    their host offsets)."""
+    torch = _torch()
+    so = _i64_array(sample_offsets_host)
+    oo = logmel_resample_offsets(so, r.rate)
+    dev = samples.device
+    y = logmel_resample(r, samples, torch.from_numpy(so).to(dev), torch.from_numpy(oo).to(dev),
+                        int(oo[-1]), stream=stream)
+    return y, oo

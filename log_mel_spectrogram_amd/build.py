@@ -34,7 +34,8 @@ def build(verbose: bool = False) -> str:
                            os.path.join(CSRC, "logmel_tables.h")])
     tmp = LIB + ".tmp"
     cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           os.path.join(CSRC, "logmel_kernels.hip"), os.path.join(CSRC, "logmel_api.cpp"),
+           os.path.join(CSRC, "logmel_kernels.hip"), os.path.join(CSRC, "logmel_resample.hip"),
+           os.path.join(CSRC, "logmel_api.cpp"),
            "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)

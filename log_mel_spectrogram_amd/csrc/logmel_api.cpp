@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <cmath>
 #include <cstdlib>
 #include <cstring>
 #include <new>
@@ -484,6 +485,214 @@ int logmel_stream_set_state(logmel_stream* s, const void* state_host, void* hip_
   }
   // The host buffer is the caller's: finish the copies before returning.
   return hipStreamSynchronize(st) == hipSuccess ? LOGMEL_OK : LOGMEL_ERR_DEVICE;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Resampling to 16 kHz: a Kaiser-windowed sinc (the reading and its
+// parameters are stated in logmel.h).
+// ---------------------------------------------------------------------------
+
+namespace {
+
+constexpr int kResZeros = LOGMEL_RESAMPLE_ZEROS;
+constexpr double kResRolloff = 0.96;
+constexpr double kResBeta = 9.0;
+constexpr int32_t kResMinRate = 1000;
+constexpr int32_t kResMaxRate = 384000;
+
+int64_t gcd64(int64_t a, int64_t b) {
+  while (b) {
+    const int64_t t = a % b;
+    a = b;
+    b = t;
+  }
+  return a;
+}
+
+// Modified Bessel function of the first kind, order 0, by its power series
+// sum_k ((x / 2)^k / k!)^2 (all terms positive; converges for any x).
+double bessel_i0(double x) {
+  const double h = 0.5 * x;
+  double term = 1.0, sum = 1.0;
+  for (int k = 1; k < 500; ++k) {
+    term *= (h / k) * (h / k);
+    sum += term;
+    if (term < 1e-17 * sum) break;
+  }
+  return sum;
+}
+
+struct ResGeometry {
+  int64_t L, M;   // 16000 / R = L / M in lowest terms
+  int J;          // taps j = 0 .. 2J cover input samples q - J .. q + J
+  double fc, H;   // cutoff (Hz) and half-width (input samples)
+};
+
+ResGeometry res_geometry(int32_t rate) {
+  ResGeometry g;
+  const int64_t d = gcd64(rate, 16000);
+  g.L = 16000 / d;
+  g.M = rate / d;
+  g.fc = kResRolloff * (rate < 16000 ? rate : 16000) / 2.0;
+  g.H = kResZeros * (double)rate / (2.0 * g.fc);
+  g.J = rate == 16000 ? 0 : (int)std::ceil(g.H);
+  return g;
+}
+
+// Taps table [L][2J + 1]: row phi, tap j is h(phi / L + J - j).
+std::vector<float> res_taps(int32_t rate, const ResGeometry& g) {
+  const int T = 2 * g.J + 1;
+  std::vector<float> t((size_t)(g.L * T));
+  if (rate == 16000) {   // no resampling: the output is the input
+    t[0] = 1.0f;
+    return t;
+  }
+  const double i0b = bessel_i0(kResBeta);
+  const double pi = 3.14159265358979323846;
+  for (int64_t phi = 0; phi < g.L; ++phi) {
+    for (int j = 0; j < T; ++j) {
+      const double dd = ((double)phi / (double)g.L + g.J) - j;   // p - k, input samples
+      const double r = dd / g.H;
+      double h = 0.0;
+      if (std::fabs(r) < 1.0) {
+        const double u = 2.0 * g.fc * dd / rate;
+        const double sinc = u == 0.0 ? 1.0 : std::sin(pi * u) / (pi * u);
+        h = (2.0 * g.fc / rate) * sinc * bessel_i0(kResBeta * std::sqrt(1.0 - r * r)) / i0b;
+      }
+      t[(size_t)(phi * T + j)] = (float)h;
+    }
+  }
+  return t;
+}
+
+// LDS the kernel needs: the taps, then a span of input samples covering a
+// block of 1024 outputs (window starts advance by at most ceil(M / L) + 1
+// samples per output, the +1 at clip boundaries).
+int64_t res_span_cap(const ResGeometry& g) {
+  const int64_t tab = ((g.L * (2 * g.J + 1)) + 3) & ~int64_t(3);
+  return kResLdsFloats - tab;
+}
+int64_t res_span_need(const ResGeometry& g) {
+  return (kResThreadsHost - 1) * ((g.M + g.L - 1) / g.L + 1) + (2 * g.J + 1) + 4;
+}
+
+bool res_rate_ok(int32_t rate) { return rate >= kResMinRate && rate <= kResMaxRate; }
+
+}  // namespace
+
+struct logmel_resampler {
+  const logmel_plan* plan;
+  int32_t rate;
+  ResGeometry geo;
+  int span_cap;
+  int grid;
+  float* taps = nullptr;   // device [L][2J + 1]
+};
+
+extern "C" {
+
+int64_t logmel_resample_length(int64_t n_samples, int32_t in_rate) {
+  if (n_samples < 0 || !res_rate_ok(in_rate)) return -1;
+  if (n_samples > INT64_MAX / 16000) return -1;
+  return (n_samples * 16000 + in_rate - 1) / in_rate;
+}
+
+int logmel_resample_offsets(int32_t in_rate, const int64_t* so, int64_t n_clips, int64_t* oo) {
+  if (!so || !oo || n_clips < 0) return LOGMEL_ERR_INVALID_ARGUMENT;
+  if (!res_rate_ok(in_rate)) return LOGMEL_ERR_UNSUPPORTED;
+  if (so[0] != 0) return LOGMEL_ERR_INVALID_ARGUMENT;
+  for (int64_t i = 0; i < n_clips; ++i)
+    if (so[i + 1] < so[i]) return LOGMEL_ERR_INVALID_ARGUMENT;
+  if (so[n_clips] > INT64_MAX / 16000) return LOGMEL_ERR_INPUT_TOO_LONG;
+  int64_t acc = 0;
+  oo[0] = 0;
+  for (int64_t i = 0; i < n_clips; ++i) {
+    acc += logmel_resample_length(so[i + 1] - so[i], in_rate);
+    oo[i + 1] = acc;
+  }
+  return LOGMEL_OK;
+}
+
+int logmel_resampler_create(const logmel_plan* plan, int32_t in_rate, logmel_resampler** out) {
+  if (!plan || !out) return LOGMEL_ERR_INVALID_ARGUMENT;
+  *out = nullptr;
+  if (!res_rate_ok(in_rate)) return LOGMEL_ERR_UNSUPPORTED;
+  const ResGeometry geo = res_geometry(in_rate);
+  if (geo.L * (2 * geo.J + 1) > kResLdsFloats || res_span_need(geo) > res_span_cap(geo))
+    return LOGMEL_ERR_UNSUPPORTED;   // a rate whose phase count needs too large a table
+  const std::vector<float> taps = res_taps(in_rate, geo);
+  logmel_resampler* r = new (std::nothrow) logmel_resampler;
+  if (!r) return LOGMEL_ERR_OUT_OF_MEMORY;
+  r->plan = plan;
+  r->rate = in_rate;
+  r->geo = geo;
+  r->span_cap = (int)res_span_cap(geo);
+  r->grid = plan->resident_waves / 4;   // one workgroup per compute unit
+  DeviceGuard g(plan->cfg.device);
+  if (!g.ok) {
+    delete r;
+    return LOGMEL_ERR_DEVICE;
+  }
+  if (hipMalloc(&r->taps, taps.size() * sizeof(float)) != hipSuccess) {
+    delete r;
+    return LOGMEL_ERR_OUT_OF_MEMORY;
+  }
+  if (hipMemcpy(r->taps, taps.data(), taps.size() * sizeof(float), hipMemcpyHostToDevice) !=
+      hipSuccess) {
+    (void)hipFree(r->taps);
+    delete r;
+    return LOGMEL_ERR_DEVICE;
+  }
+  *out = r;
+  return LOGMEL_OK;
+}
+
+void logmel_resampler_destroy(logmel_resampler* r) {
+  if (!r) return;
+  if (r->taps) {
+    DeviceGuard g(r->plan->cfg.device);
+    (void)hipFree(r->taps);
+  }
+  delete r;
+}
+
+int logmel_resampler_info(const logmel_resampler* r, int64_t* phases, int64_t* taps_per_phase) {
+  if (!r) return LOGMEL_ERR_INVALID_ARGUMENT;
+  if (phases) *phases = r->geo.L;
+  if (taps_per_phase) *taps_per_phase = 2 * r->geo.J + 1;
+  return LOGMEL_OK;
+}
+
+int logmel_resample(const logmel_resampler* r, const void* d_samples, int sample_type,
+                    const int64_t* d_sample_offsets, const int64_t* d_out_offsets,
+                    int64_t n_clips, int64_t total_out, float* d_out, void* hip_stream) {
+  if (!r || n_clips < 0 || total_out < 0) return LOGMEL_ERR_INVALID_ARGUMENT;
+  if (sample_type != LOGMEL_F32 && sample_type != LOGMEL_I16) return LOGMEL_ERR_UNSUPPORTED;
+  if (n_clips == 0 || total_out == 0) return LOGMEL_OK;
+  if (!d_samples || !d_sample_offsets || !d_out_offsets || !d_out)
+    return LOGMEL_ERR_INVALID_ARGUMENT;
+  DeviceGuard g(r->plan->cfg.device);
+  if (!g.ok) return LOGMEL_ERR_DEVICE;
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  if (env_validate()) {
+    std::vector<int64_t> so(n_clips + 1), oo(n_clips + 1), ref(n_clips + 1);
+    if (hipMemcpyAsync(so.data(), d_sample_offsets, (n_clips + 1) * 8, hipMemcpyDeviceToHost,
+                       st) != hipSuccess ||
+        hipMemcpyAsync(oo.data(), d_out_offsets, (n_clips + 1) * 8, hipMemcpyDeviceToHost, st) !=
+            hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess)
+      return LOGMEL_ERR_DEVICE;
+    if (logmel_resample_offsets(r->rate, so.data(), n_clips, ref.data()) != LOGMEL_OK ||
+        ref != oo || oo[n_clips] != total_out)
+      return LOGMEL_ERR_INVALID_ARGUMENT;
+  }
+  if (logmel_launch_resample(d_samples, sample_type == LOGMEL_I16, d_sample_offsets,
+                             d_out_offsets, n_clips, total_out, d_out, r->taps, (int)r->geo.L,
+                             (int)r->geo.M, r->geo.J, r->span_cap, r->grid, st) != hipSuccess)
+    return LOGMEL_ERR_DEVICE;
+  return LOGMEL_OK;
 }
 
 }  // extern "C"

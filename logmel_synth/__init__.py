@@ -109,10 +109,10 @@ N_HARM = 20
 _FIR_TAPS = 65
 
 
-def _bandpass_fir() -> np.ndarray:
-    """65-tap windowed-sinc band-pass, 2..6 kHz at 16 kHz (Hann taper)."""
+def _bandpass_fir(fs: int = FS) -> np.ndarray:
+    """65-tap windowed-sinc band-pass, 2..6 kHz at fs (Hann taper)."""
     m = np.arange(_FIR_TAPS, dtype=np.float64) - (_FIR_TAPS - 1) / 2
-    lo, hi = 2000.0 / FS, 6000.0 / FS
+    lo, hi = 2000.0 / fs, 6000.0 / fs
     h = 2 * hi * np.sinc(2 * hi * m) - 2 * lo * np.sinc(2 * lo * m)
     taper = 0.5 - 0.5 * np.cos(2 * np.pi * np.arange(_FIR_TAPS) / (_FIR_TAPS - 1))
     return h * taper
@@ -120,6 +120,13 @@ def _bandpass_fir() -> np.ndarray:
 
 _FIR = _bandpass_fir()
 _FIR_GAIN = float(np.sqrt(np.sum(_FIR ** 2)))
+
+
+def _fir_at(fs: int):
+    if fs == FS:
+        return _FIR, _FIR_GAIN
+    f = _bandpass_fir(fs)
+    return f, float(np.sqrt(np.sum(f ** 2)))
 
 
 @dataclass
@@ -132,7 +139,7 @@ class SpeechLayout:
     burst_off: np.ndarray   # int64 offset of the burst inside its syllable
 
 
-def speech_layout(seed: int, n: int) -> SpeechLayout:
+def speech_layout(seed: int, n: int, fs: int = FS) -> SpeechLayout:
     """Syllable plan of G(seed, n).
 
     Syllables of U(100, 400) ms, each followed by an exact-zero gap of
@@ -145,7 +152,7 @@ def speech_layout(seed: int, n: int) -> SpeechLayout:
     starts, lengths = [], []
     pos = 0
     while pos < n:
-        L = int(round(rng.uniform(0.100, 0.400) * FS))
+        L = int(round(rng.uniform(0.100, 0.400) * fs))
         starts.append(pos)
         lengths.append(L)
         pos += L + int(round(0.0526 * L))
@@ -155,13 +162,13 @@ def speech_layout(seed: int, n: int) -> SpeechLayout:
     f0 = rng.uniform(80.0, 300.0, S)
     phases = rng.uniform(0.0, 2 * np.pi, (S, N_HARM))
     has = rng.uniform(size=S) < 0.5
-    blen = np.rint(rng.uniform(0.020, 0.080, S) * FS).astype(np.int64)
+    blen = np.rint(rng.uniform(0.020, 0.080, S) * fs).astype(np.int64)
     boff = np.floor(rng.uniform(size=S) * (lengths - blen + 1)).astype(np.int64)
     blen = np.where(has, blen, 0)
     return SpeechLayout(starts, lengths, f0, phases, blen, boff)
 
 
-def _speech_chunk(lay_t, key: int, a: int, b: int, device) -> torch.Tensor:
+def _speech_chunk(lay_t, key: int, a: int, b: int, device, fs: int = FS) -> torch.Tensor:
     starts, lengths, f0, phases, blen, boff = lay_t
     n = torch.arange(a, b, dtype=torch.int64, device=device)
     s = torch.searchsorted(starts, n, right=True) - 1
@@ -170,7 +177,7 @@ def _speech_chunk(lay_t, key: int, a: int, b: int, device) -> torch.Tensor:
     inside = t < L
     tf = t.to(torch.float64)
     env = 0.5 - 0.5 * torch.cos((2 * math.pi) * tf / L.to(torch.float64))
-    w = (2 * math.pi / FS) * f0[s] * tf
+    w = (2 * math.pi / fs) * f0[s] * tf
     harm = torch.zeros(b - a, dtype=torch.float64, device=device)
     ph = phases[s]
     for h in range(1, N_HARM + 1):
@@ -185,26 +192,30 @@ def _speech_chunk(lay_t, key: int, a: int, b: int, device) -> torch.Tensor:
         half = (_FIR_TAPS - 1) // 2
         idx = torch.arange(a - half, b + half, dtype=torch.int64, device=device)
         g = gaussian(key, idx)
+        fir, fir_gain = _fir_at(fs)
         filt = torch.zeros(b - a, dtype=torch.float64, device=device)
         for j in range(_FIR_TAPS):
-            filt += float(_FIR[j]) * g[j:j + (b - a)]
+            filt += float(fir[j]) * g[j:j + (b - a)]
         taper = 0.5 - 0.5 * torch.cos((2 * math.pi) * nb.to(torch.float64)
                                       / bl.clamp(min=1).to(torch.float64))
-        x = x + torch.where(in_burst, (0.1 / _FIR_GAIN) * filt * taper,
+        x = x + torch.where(in_burst, (0.1 / fir_gain) * filt * taper,
                             torch.zeros_like(filt))
     return x
 
 
 def speech_like(seed: int, n: int, device="cpu", out: torch.Tensor | None = None,
-                chunk: int = 1 << 21) -> torch.Tensor:
+                chunk: int = 1 << 21, fs: int = FS) -> torch.Tensor:
     """G(seed, n): fp32 [n] speech-like clip, peak-normalised to 0.9.
 
     Harmonic series (20 harmonics, amplitude 1/h) at a per-syllable pitch
     under a raised-cosine syllable envelope, plus 2..6 kHz noise bursts of
     RMS 0.1 under a raised-cosine taper, separated by exact-zero gaps.
-    ``out`` may be a preallocated fp32 view of length n on ``device``.
+    ``out`` may be a preallocated fp32 view of length n on ``device``. ``fs``
+    is the sample rate the clip is made at (16 kHz unless another is asked
+    for, as input for resampling); durations and pitches are in seconds and
+    Hz, so a clip at another rate has the same structure.
     """
-    lay = speech_layout(seed, n)
+    lay = speech_layout(seed, n, fs)
     lay_t = tuple(torch.as_tensor(v, device=device) for v in
                   (lay.starts, lay.lengths, lay.f0, lay.phases, lay.burst_len,
                    lay.burst_off))
@@ -213,7 +224,7 @@ def speech_like(seed: int, n: int, device="cpu", out: torch.Tensor | None = None
     peak = 0.0
     for a in range(0, n, chunk):
         b = min(n, a + chunk)
-        xc = _speech_chunk(lay_t, seed, a, b, device)
+        xc = _speech_chunk(lay_t, seed, a, b, device, fs)
         peak = max(peak, float(xc.abs().max()))
         out[a:b] = xc.to(torch.float32)
     if peak > 0:
@@ -258,6 +269,14 @@ def config2(device="cpu", n_clips: int = 64):
     """64 clips of 480000 samples, clip i = G(100 + i, 480000), packed."""
     return pack([480000] * n_clips,
                 lambda i, v: speech_like(100 + i, 480000, device, out=v), device)
+
+
+def config2_at(rate: int, device="cpu", n_clips: int = 64, seconds: int = 30):
+    """Config 2's clips made at another sample rate (input for resampling):
+    clip i = G(100 + i, seconds * rate) at ``rate``, packed."""
+    n = int(seconds) * int(rate)
+    return pack([n] * n_clips,
+                lambda i, v: speech_like(100 + i, n, device, out=v, fs=int(rate)), device)
 
 
 def config3_streams(device="cpu", n_streams: int = 512, n_samples: int = 480000):

@@ -13,4 +13,5 @@ from .logmel_oracle import (  # noqa: F401
     num_chunks, chunk_offsets, chunk_frames, logmel_chunked,
     RESAMPLE_ZEROS, RESAMPLE_ROLLOFF, RESAMPLE_BETA, resample_length, resample_offsets,
     resample_cutoff, resample_halfwidth, resample_kernel, resample_clip, resample_packed,
+    resample_selected,
 )

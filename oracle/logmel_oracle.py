@@ -361,3 +361,32 @@ def resample_packed(samples: np.ndarray, sample_offsets, rate: int):
         y[oo[i]:oo[i + 1]] = yi
         a[oo[i]:oo[i + 1]] = ai
     return y, oo, a
+
+
+def resample_selected(samples: np.ndarray, sample_offsets, rate: int, rows):
+    """Chosen outputs of resample_packed, each from its definition (for
+    batches too large to resample whole): (y fp64, a) at flat output rows."""
+    so = np.asarray(sample_offsets, dtype=np.int64).reshape(-1)
+    oo = resample_offsets(so, rate)
+    rows = np.asarray(rows, dtype=np.int64)
+    clip = np.searchsorted(oo, rows, side="right") - 1
+    y = np.zeros(rows.size)
+    a = np.zeros(rows.size)
+    J = int(np.ceil(resample_halfwidth(rate)))
+    for t, (g, c) in enumerate(zip(rows, clip)):
+        n = int(g - oo[c])
+        N = int(so[c + 1] - so[c])
+        if int(rate) == SAMPLE_RATE:
+            y[t] = samples[so[c] + n]
+            a[t] = abs(y[t])
+            continue
+        q = (n * int(rate)) // SAMPLE_RATE
+        frac = ((n * int(rate)) % SAMPLE_RATE) / SAMPLE_RATE
+        j = np.arange(-J, J + 1)
+        k = q + j
+        ok = (k >= 0) & (k < N)
+        xs = np.asarray(samples[so[c] + k[ok]], dtype=np.float64)
+        terms = xs * resample_kernel(frac - j[ok], rate)
+        y[t] = terms.sum()
+        a[t] = np.abs(terms).sum()
+    return y, a

@@ -118,3 +118,32 @@ def test_chunk_helpers_reject_bad_input(lm):
 def test_compute_ex_null_arguments(lm):
     assert lm._compute_ex(None, None, lm.LOGMEL_F32, None, None, None, 1, 1, 0, None,
                           lm.LOGMEL_F32, None) == lm.LOGMEL_ERR_INVALID_ARGUMENT
+
+
+def test_resample_lengths_and_offsets_match_oracle(lm):
+    rng = np.random.default_rng(4)
+    for rate in (8000, 11025, 16000, 22050, 44100, 48000, 96000, 192000, 7350, 1000, 384000):
+        for n in list(range(0, 60)) + list(rng.integers(0, 10**9, 40)) + [2**40]:
+            assert lm.logmel_resample_length(int(n), rate) == O.resample_length(int(n), rate)
+        lens = rng.integers(0, 3 * rate, 50)
+        so = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+        oo = lm.logmel_resample_offsets(so, rate)
+        assert oo.dtype == np.int64 and np.array_equal(oo, O.resample_offsets(so, rate))
+
+
+def test_resample_helpers_reject_bad_input(lm):
+    assert lm.logmel_resample_length(-1, 44100) == -1
+    assert lm.logmel_resample_length(100, 999) == -1
+    assert lm.logmel_resample_length(100, 384001) == -1
+    assert lm.logmel_resample_length(2**62, 44100) == -1
+    with pytest.raises(lm.LogmelError) as e:
+        lm.logmel_resample_offsets([0, 10, 5], 44100)
+    assert e.value.status == lm.LOGMEL_ERR_INVALID_ARGUMENT
+    with pytest.raises(lm.LogmelError) as e:
+        lm.logmel_resample_offsets([0, 10], 500)
+    assert e.value.status == lm.LOGMEL_ERR_UNSUPPORTED
+    h = ctypes.c_void_p()
+    assert lm._resampler_create(None, 44100, ctypes.byref(h)) == lm.LOGMEL_ERR_INVALID_ARGUMENT
+    assert lm._resample(None, None, lm.LOGMEL_F32, None, None, 1, 1, None, None) == \
+        lm.LOGMEL_ERR_INVALID_ARGUMENT
+    assert lm._resampler_info(None, None, None) == lm.LOGMEL_ERR_INVALID_ARGUMENT
