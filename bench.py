@@ -2,6 +2,7 @@
 """Throughput of the 128-bin log-mel front end on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c4|c3|c1]
+                    [--in-rate R]  (c2 made at R Hz, resampled to 16 kHz in the step)
 
 Prints one JSON line. A step is one logmel_compute over one batch of
 synthetic input already resident in HBM: framing, window, rFFT, power, mel
@@ -258,6 +259,112 @@ def bench_offline(args, lm, plan, torch):
     return rec, clips_host
 
 
+# fp32 vector peak as published (packed FP32); without packed instructions,
+# which this build does not emit, the ceiling is half of it.
+FP32_PEAK_TFLOPS = 157.3
+
+
+def _resample_worker(args):
+    x, rate, reps = args
+    from oracle import logmel_clip, resample_clip
+    for _ in range(reps):
+        y, _ = resample_clip(x, rate)
+        logmel_clip(y.astype("float32"))
+    return 0
+
+
+def bench_resampled(args, lm, plan, torch):
+    """One step = the 64 x 30 s batch made at --in-rate, resampled to 16 kHz
+    (logmel_resample) and then turned into log-mel (logmel_compute): two
+    launches on one stream, each timed with its own HIP events."""
+    import logmel_synth as S
+    import numpy as np
+    import multiprocessing as mp
+    dev = torch.device("cuda", 0)
+    rate = args.in_rate
+    x, so = S.config2_at(rate, device=dev)
+    r = lm.logmel_resampler_create(plan, rate)
+    L, T = lm.logmel_resampler_info(r)
+    oo = lm.logmel_resample_offsets(so, rate)
+    fo = lm.logmel_frame_offsets(oo)
+    n_out, total = int(oo[-1]), int(fo[-1])
+    n_in = int(so[-1])
+    so_d, oo_d, fo_d = (torch.from_numpy(a).to(dev) for a in (so, oo, fo))
+    n_sets = 3
+    xs = [x] + [x.clone() for _ in range(n_sets - 1)]
+    ys = [torch.empty(n_out, dtype=torch.float32, device=dev) for _ in range(n_sets)]
+    outs = [torch.empty((total, 128), dtype=torch.float32, device=dev) for _ in range(n_sets)]
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+
+    def step(k, e=None):
+        if e: e[0].record(stream)
+        lm.logmel_resample(r, xs[k], so_d, oo_d, n_out, out=ys[k], stream=stream)
+        if e: e[1].record(stream)
+        lm.logmel_compute(plan, ys[k], oo_d, fo_d, total, out=outs[k], stream=stream)
+        if e: e[2].record(stream)
+
+    for i in range(args.warmup):
+        step(i % n_sets)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i % n_sets, ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    rs_s = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps / 1e3
+    lm_s = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps / 1e3
+    ms_per_step = wall / args.steps * 1e3
+    # taps inside the kernel's support per output: 2 H on average
+    H = 24 * rate / (0.96 * min(rate, FS))
+    rs_flops = 2 * (2 * H) * n_out
+    rs_bytes = 4 * n_in + 4 * n_out + 16 * len(so)
+    rs_tflops = rs_flops / rs_s / 1e12
+    rec = {
+        "metric": "audio-seconds/sec of 128-bin log-mel on 1 MI355X + % of HBM roofline",
+        "value": (n_in / rate) / (ms_per_step / 1e3),
+        "unit": "audio-seconds/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32+f64", "data": "synthetic",
+        "config": {"workload": f"offline batch: 64 speech-like clips x 30 s made at {rate} Hz "
+                               f"({30 * rate} fp32 samples each), resampled to 16 kHz, then log-mel",
+                   "clips": len(so) - 1, "in_rate": rate, "samples_in": n_in,
+                   "samples_16k": n_out, "frames": total, "phases": L, "taps_per_phase": T,
+                   "buffer_sets": n_sets},
+        "frames_per_s": total / (ms_per_step / 1e3),
+        "resample_kernel_avg_us": rs_s * 1e6,
+        "logmel_kernel_avg_us": lm_s * 1e6,
+        "roofline": {"bound": "alu", "achieved": rs_tflops, "peak": FP32_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": rs_tflops / FP32_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "logmel_resample_kernel", "kernel_avg_us": rs_s * 1e6,
+                     "algorithmic_flops_per_launch": rs_flops,
+                     "algorithmic_bytes_per_launch": rs_bytes,
+                     "hbm_achieved_gbs": rs_bytes / rs_s / 1e9,
+                     "hbm_frac": rs_bytes / rs_s / 1e9 / HBM_PEAK_GBS},
+    }
+    if not args.no_cpu_baseline:
+        xh = x.cpu().numpy()
+        clips = [xh[so[i]:so[i + 1]] for i in range(16)]
+        for v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+            os.environ[v] = "1"
+        cores = min(len(os.sched_getaffinity(0)), 16)
+        with mp.get_context("spawn").Pool(cores) as pool:
+            t0 = time.perf_counter()
+            pool.map(_resample_worker, [(c, rate, 1) for c in clips])
+            dt = time.perf_counter() - t0
+        audio = sum(c.size for c in clips) / rate
+        rec["cpu_baseline"] = {"value": audio / dt, "unit": "audio-seconds/s", "cores": cores,
+                               "kind": "oracle",
+                               "sample": f"16 clips of the workload ({audio:.0f} audio-s): "
+                                         f"oracle resampling then oracle log-mel, one pass, "
+                                         f"{dt:.1f} s wall"}
+    else:
+        rec["cpu_baseline"] = None
+    r.close()
+    return rec
+
+
 def bench_stream(args, lm, plan, torch):
     """One step = every 30 s stream of 512 pushed through in pushes of the
     audio clock (80 ms: 375 pushes of 1280 samples; 120 ms: 250 of 1920;
@@ -345,6 +452,8 @@ def main():
                     help="output type: fp32 or fp16")
     ap.add_argument("--layout", default="frames", choices=["frames", "chunked"],
                     help="output layout: [frames, 128] or 30-s chunks [chunks, 3000, 128]")
+    ap.add_argument("--in-rate", type=int, default=16000,
+                    help="make the c2 batch at this rate and resample it to 16 kHz in the step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--counter-pass", action="store_true",
@@ -356,6 +465,8 @@ def main():
               "on their own share of the batch)", file=sys.stderr)
         sys.exit(2)
     defaults = {"c2": (200, 20), "c1": (500, 50), "c4": (5, 2), "c3": (3, 1)}
+    if args.in_rate != FS:
+        defaults["c2"] = (50, 5)
     if args.steps is None:
         args.steps = defaults[args.workload][0]
     if args.warmup is None:
@@ -369,6 +480,12 @@ def main():
     plan = lm.logmel_plan_create(0)
     if args.counter_pass:
         counter_pass(args, lm, plan, torch)
+        return
+    if args.in_rate != FS:
+        if args.workload != "c2":
+            print("bench.py: --in-rate applies to the c2 workload", file=sys.stderr)
+            sys.exit(2)
+        print(json.dumps(bench_resampled(args, lm, plan, torch)), flush=True)
         return
     if args.workload == "c3":
         rec, clips = bench_stream(args, lm, plan, torch)

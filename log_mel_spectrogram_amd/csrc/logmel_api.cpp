@@ -527,7 +527,9 @@ double bessel_i0(double x) {
 struct ResGeometry {
   int64_t L, M;   // 16000 / R = L / M in lowest terms
   int J;          // taps j = 0 .. 2J cover input samples q - J .. q + J
+  int Tp;         // 2J + 1 rounded up to a multiple of 16 (table row length)
   double fc, H;   // cutoff (Hz) and half-width (input samples)
+  int G;          // periods of L outputs per block, in groups of 64
 };
 
 ResGeometry res_geometry(int32_t rate) {
@@ -538,13 +540,22 @@ ResGeometry res_geometry(int32_t rate) {
   g.fc = kResRolloff * (rate < 16000 ? rate : 16000) / 2.0;
   g.H = kResZeros * (double)rate / (2.0 * g.fc);
   g.J = rate == 16000 ? 0 : (int)std::ceil(g.H);
+  g.Tp = (2 * g.J + 1 + 15) / 16 * 16;
+  // A block of 64 G periods needs about 64 G M + Tp staged samples; at
+  // most 1024 (period group, phase) items per block.
+  const int64_t room = kResLdsFloats - g.Tp - 64;
+  int64_t G = room / (64 * g.M);
+  const int64_t item_cap = 1024 / g.L > 1 ? 1024 / g.L : 1;
+  if (G > item_cap) G = item_cap;
+  g.G = (int)(G < 1 ? 0 : G);
   return g;
 }
 
-// Taps table [L][2J + 1]: row phi, tap j is h(phi / L + J - j).
+// Taps table [L][Tp]: row phi, tap j < 2J + 1 is h(phi / L + J - j); the
+// row's last Tp - 2J - 1 entries are zero.
 std::vector<float> res_taps(int32_t rate, const ResGeometry& g) {
   const int T = 2 * g.J + 1;
-  std::vector<float> t((size_t)(g.L * T));
+  std::vector<float> t((size_t)(g.L * g.Tp), 0.0f);
   if (rate == 16000) {   // no resampling: the output is the input
     t[0] = 1.0f;
     return t;
@@ -561,22 +572,14 @@ std::vector<float> res_taps(int32_t rate, const ResGeometry& g) {
         const double sinc = u == 0.0 ? 1.0 : std::sin(pi * u) / (pi * u);
         h = (2.0 * g.fc / rate) * sinc * bessel_i0(kResBeta * std::sqrt(1.0 - r * r)) / i0b;
       }
-      t[(size_t)(phi * T + j)] = (float)h;
+      t[(size_t)(phi * g.Tp + j)] = (float)h;
     }
   }
   return t;
 }
 
-// LDS the kernel needs: the taps, then a span of input samples covering a
-// block of 1024 outputs (window starts advance by at most ceil(M / L) + 1
-// samples per output, the +1 at clip boundaries).
-int64_t res_span_cap(const ResGeometry& g) {
-  const int64_t tab = ((g.L * (2 * g.J + 1)) + 3) & ~int64_t(3);
-  return kResLdsFloats - tab;
-}
-int64_t res_span_need(const ResGeometry& g) {
-  return (kResThreadsHost - 1) * ((g.M + g.L - 1) / g.L + 1) + (2 * g.J + 1) + 4;
-}
+// Largest taps table accepted (floats, device memory).
+constexpr int64_t kResMaxTableFloats = int64_t(1) << 24;
 
 bool res_rate_ok(int32_t rate) { return rate >= kResMinRate && rate <= kResMaxRate; }
 
@@ -586,7 +589,6 @@ struct logmel_resampler {
   const logmel_plan* plan;
   int32_t rate;
   ResGeometry geo;
-  int span_cap;
   int grid;
   float* taps = nullptr;   // device [L][2J + 1]
 };
@@ -620,15 +622,14 @@ int logmel_resampler_create(const logmel_plan* plan, int32_t in_rate, logmel_res
   *out = nullptr;
   if (!res_rate_ok(in_rate)) return LOGMEL_ERR_UNSUPPORTED;
   const ResGeometry geo = res_geometry(in_rate);
-  if (geo.L * (2 * geo.J + 1) > kResLdsFloats || res_span_need(geo) > res_span_cap(geo))
-    return LOGMEL_ERR_UNSUPPORTED;   // a rate whose phase count needs too large a table
+  if (geo.G < 1 || geo.L * geo.Tp > kResMaxTableFloats)
+    return LOGMEL_ERR_UNSUPPORTED;   // 64 input periods beyond LDS, or too many phases
   const std::vector<float> taps = res_taps(in_rate, geo);
   logmel_resampler* r = new (std::nothrow) logmel_resampler;
   if (!r) return LOGMEL_ERR_OUT_OF_MEMORY;
   r->plan = plan;
   r->rate = in_rate;
   r->geo = geo;
-  r->span_cap = (int)res_span_cap(geo);
   r->grid = plan->resident_waves / 4;   // one workgroup per compute unit
   DeviceGuard g(plan->cfg.device);
   if (!g.ok) {
@@ -690,7 +691,8 @@ int logmel_resample(const logmel_resampler* r, const void* d_samples, int sample
   }
   if (logmel_launch_resample(d_samples, sample_type == LOGMEL_I16, d_sample_offsets,
                              d_out_offsets, n_clips, total_out, d_out, r->taps, (int)r->geo.L,
-                             (int)r->geo.M, r->geo.J, r->span_cap, r->grid, st) != hipSuccess)
+                             (int)r->geo.M, r->geo.J, r->geo.Tp, r->geo.G, r->grid, st) !=
+      hipSuccess)
     return LOGMEL_ERR_DEVICE;
   return LOGMEL_OK;
 }

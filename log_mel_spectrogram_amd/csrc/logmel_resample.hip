@@ -4,18 +4,27 @@
 // 0 <= phi < L), and is the dot product of the clip's samples
 // x[q - J .. q + J] (zero outside the clip) with the phi-th row of taps,
 // taps[phi][j] = h(phi / L + J - j). The host builds the taps (fp64 math,
-// rounded once to fp32); see logmel_api.cpp.
+// rounded once to fp32, rows zero-padded to Tp, a multiple of 16); see
+// logmel_api.cpp.
 //
-// logmel_resample_kernel: a persistent grid of 1024-thread workgroups, one
-// per compute unit. A workgroup copies the taps table into LDS once, then
-// walks blocks of 1024 consecutive outputs of the packed batch, one output
-// per thread. For each block it stages the input samples the block's
-// windows cover (one coalesced pass; int16 PCM is converted to s / 32768 on
-// the way) and every thread forms its dot product from LDS, in fp32 with
-// four partial sums. Clips are packed back to back, so the block's windows
-// always cover one contiguous range of the batch even when the block spans
-// clips; a thread whose window crosses its clip's edge masks the samples
-// outside the clip.
+// logmel_resample_kernel: a persistent grid of one 1024-thread workgroup per
+// compute unit. The outputs of the packed batch are cut into blocks of
+// 64 G periods of L outputs each (a period's outputs have the L different
+// phases; inside one clip, output r of every period has the same phase). A
+// workgroup stages the input samples a block's windows cover in LDS (one
+// coalesced pass; int16 PCM is converted to s / 32768 on the way), then its
+// 16 wavefronts take the block's (period group, phase) items in turn: lane l
+// of a wavefront forms output r of period 64 g + l. All lanes of an item
+// share their taps, which the wavefront reads with scalar loads straight
+// into scalar registers; each lane's window starts M samples after its left
+// neighbour's, so with M odd the 64 lanes' LDS reads of one tap fall on 64
+// different banks. Per multiply-add: one LDS read.
+// Clips are packed back to back, so a block's windows cover one contiguous
+// range of the batch even when the block spans clips. A lane whose window
+// crosses its clip's edge or lies beyond the staged span (blocks of many
+// tiny clips) forms its output alone, masked to its clip, with its own row
+// of taps; lanes of one item in different clips (different phases) take one
+// pass of the shared-tap loop per phase.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -23,7 +32,7 @@
 
 namespace logmel {
 
-static constexpr int kResThreads = kResThreadsHost;
+static constexpr int kResChunk = 16;   // taps per unrolled step
 
 __device__ __forceinline__ float res_sample(const float* p, int64_t k) { return p[k]; }
 __device__ __forceinline__ float res_sample(const int16_t* p, int64_t k) {
@@ -40,6 +49,133 @@ __device__ __forceinline__ int64_t last_le(const int64_t* __restrict__ a, int64_
   return lo;
 }
 
+// floor(a / L) for 0 <= a: an fp64 estimate off by at most one below 2^52,
+// corrected; larger values divide exactly.
+__device__ __forceinline__ int64_t div_by(int64_t a, int L, double inv_L) {
+  if (a >= (int64_t(1) << 52)) return a / L;
+  int64_t q = (int64_t)((double)a * inv_L);
+  const int64_t rem = a - q * L;
+  if (rem < 0) q -= 1;
+  else if (rem >= L) q += 1;
+  return q;
+}
+
+// A lane's current clip: its index, output range [o_lo, o_hi) and sample
+// range [lo, hi). A lane's successive outputs usually stay in one clip, so
+// the clip is looked up again only when an output leaves it.
+struct ResClip {
+  int64_t c, o_lo, o_hi, lo, hi;
+};
+
+__device__ __forceinline__ ResClip res_clip(int64_t g, const int64_t* __restrict__ in_off,
+                                            const int64_t* __restrict__ out_off,
+                                            int64_t n_clips) {
+  ResClip r;
+  r.c = last_le(out_off, n_clips, g);
+  r.o_lo = out_off[r.c];
+  r.o_hi = out_off[r.c + 1];
+  r.lo = in_off[r.c];
+  r.hi = in_off[r.c + 1];
+  return r;
+}
+
+// Where output g (inside clip cl) comes from: the global index k0 of its
+// window's first sample, and its phase.
+struct ResSrc {
+  int64_t c, lo, hi, k0;
+  int phi;
+};
+
+__device__ __forceinline__ ResSrc res_pos(int64_t g, const ResClip& cl, int L, int M, int J,
+                                          double inv_L) {
+  ResSrc s;
+  s.c = cl.c;
+  s.lo = cl.lo;
+  s.hi = cl.hi;
+  const int64_t nm = (g - cl.o_lo) * M;
+  const int64_t q = div_by(nm, L, inv_L);
+  s.phi = (int)(nm - q * L);
+  s.k0 = cl.lo + q - J;
+  return s;
+}
+
+// The same lookup by a whole wavefront (g uniform): a 64-ary search, one
+// load per lane and one ballot per level. Returns the last c in [0, n)
+// with a[c] <= g.
+__device__ __forceinline__ int64_t wave_last_le(const int64_t* __restrict__ a, int64_t n,
+                                                int64_t v, int lane) {
+  int64_t c0 = 0, len = n;   // answer in [c0, c0 + len); a[c0] <= v
+  while (len > 1) {
+    const int64_t stride = (len + 63) / 64;
+    const int64_t idx = c0 + lane * stride;
+    const bool le = idx < c0 + len && a[idx] <= v;
+    const int cnt = __popcll(__ballot(le));
+    const int64_t lo = c0 + (int64_t)(cnt - 1) * stride;
+    len = min(stride, c0 + len - lo);
+    c0 = lo;
+  }
+  return c0;
+}
+
+__device__ __forceinline__ int64_t wave_k0(int64_t g, const int64_t* __restrict__ in_off,
+                                           const int64_t* __restrict__ out_off, int64_t n_clips,
+                                           int L, int M, int J, double inv_L, int lane) {
+  const int64_t c = wave_last_le(out_off, n_clips, g, lane);
+  const int64_t nm = (g - out_off[c]) * M;
+  return in_off[c] + div_by(nm, L, inv_L) - J;
+}
+
+// One output alone, with its own row of taps; samples outside [lo, hi) are
+// zero; from the staged span when it holds the window, else from memory.
+template <typename In>
+__device__ __forceinline__ float res_one(const ResSrc& s, const float* __restrict__ taps, int Tp,
+                                         int T, const float* span, int64_t s0, int span_len,
+                                         const In* __restrict__ x) {
+  const float* tp = taps + (int64_t)s.phi * Tp;
+  const int jlo = (int)max((int64_t)0, s.lo - s.k0);
+  const int jhi = (int)min((int64_t)T, s.hi - s.k0);
+  const int64_t off = s.k0 - s0;
+  float a = 0.0f;
+  if (off + jlo >= 0 && off + jhi <= span_len) {
+    for (int j = jlo; j < jhi; ++j) a = __builtin_fmaf(tp[j], span[off + j], a);
+  } else {
+    for (int j = jlo; j < jhi; ++j) a = __builtin_fmaf(tp[j], res_sample(x, s.k0 + j), a);
+  }
+  return a;
+}
+
+// 16 taps (scalar registers) and 16 samples (vector registers) of a chunk.
+struct ResChunk {
+  float t[kResChunk];
+  float v[kResChunk];
+};
+
+__device__ __forceinline__ void res_load(const __attribute__((address_space(4))) float* trow,
+                                         const float* sp, int ch, ResChunk& c) {
+#pragma unroll
+  for (int j = 0; j < kResChunk; ++j) {
+    c.t[j] = trow[ch * kResChunk + j];
+    c.v[j] = sp[ch * kResChunk + j];
+  }
+}
+
+// Ties every value of a chunk to this point, so that its loads are all
+// issued before and waited here, in one wait.
+__device__ __forceinline__ void res_wait(ResChunk& c) {
+#pragma unroll
+  for (int j = 0; j < kResChunk; j += 4)
+    asm volatile("" : "+s"(c.t[j]), "+s"(c.t[j + 1]), "+s"(c.t[j + 2]), "+s"(c.t[j + 3]),
+                      "+v"(c.v[j]), "+v"(c.v[j + 1]), "+v"(c.v[j + 2]), "+v"(c.v[j + 3]));
+}
+
+__device__ __forceinline__ void res_fma(const ResChunk& c, float& a0, float& a1) {
+#pragma unroll
+  for (int j = 0; j < kResChunk; j += 2) {
+    a0 = __builtin_fmaf(c.t[j], c.v[j], a0);
+    a1 = __builtin_fmaf(c.t[j + 1], c.v[j + 1], a1);
+  }
+}
+
 template <typename In>
 __device__ __forceinline__ void resample_body(const In* __restrict__ x,
                                               const int64_t* __restrict__ in_off,
@@ -47,85 +183,116 @@ __device__ __forceinline__ void resample_body(const In* __restrict__ x,
                                               int64_t n_clips, int64_t total_out,
                                               float* __restrict__ y,
                                               const float* __restrict__ taps, int L, int M, int J,
-                                              int span_cap, float* lds, int64_t* bounds) {
+                                              int Tp, int G, float* span, int64_t* bounds) {
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n_waves = blockDim.x >> 6;
   const int T = 2 * J + 1;
-  const int tab_len = L * T;
-  float* tab = lds;
-  float* span = lds + ((tab_len + 3) & ~3);
-  for (int i = tid; i < tab_len; i += kResThreads) tab[i] = taps[i];
+  const double inv_L = 1.0 / L;
   const int64_t total_in = in_off[n_clips];
+  const int64_t per_block = (int64_t)64 * G * L;
+  const int items = G * L;
 
-  for (int64_t g0 = (int64_t)blockIdx.x * kResThreads; g0 < total_out;
-       g0 += (int64_t)gridDim.x * kResThreads) {
-    const int64_t g = g0 + tid;
-    const bool active = g < total_out;
-    const int64_t gq = active ? g : total_out - 1;
-    // the output's clip (clips without samples have no outputs and are
-    // skipped: their out_off entry equals the next one)
-    const int64_t c = last_le(out_off, n_clips, gq);
-    const int64_t n = gq - out_off[c];
-    const int64_t nm = n * M;
-    const int64_t q = nm / L;
-    const int phi = (int)(nm - q * L);
-    const int64_t lo = in_off[c], hi = in_off[c + 1];
-    const int64_t k0 = lo + q - J;            // global index of tap 0's sample
-    // The block's windows: from thread 0's first sample to the last active
-    // thread's last (window starts never decrease along the packed outputs).
-    const int last = (int)min((int64_t)kResThreads, total_out - g0) - 1;
+  for (int64_t g0 = (int64_t)blockIdx.x * per_block; g0 < total_out;
+       g0 += (int64_t)gridDim.x * per_block) {
+    // The block's windows run from its first output's first sample to its
+    // last output's last (window starts never decrease along the outputs).
+    const int64_t g_last = min(g0 + per_block, total_out) - 1;
     __syncthreads();                          // the previous block's span is consumed
-    if (tid == 0) bounds[0] = k0;
-    if (tid == last) bounds[1] = k0 + T;
+    if (wave == 0) {
+      const int64_t k_first = wave_k0(g0, in_off, out_off, n_clips, L, M, J, inv_L, lane);
+      const int64_t k_last = wave_k0(g_last, in_off, out_off, n_clips, L, M, J, inv_L, lane);
+      if (lane == 0) {
+        bounds[0] = k_first;
+        bounds[1] = k_last + Tp;
+      }
+    }
     __syncthreads();
     const int64_t s0 = bounds[0];
-    const int span_len = (int)min(bounds[1] - s0, (int64_t)span_cap);
-    for (int i = tid; i < span_len; i += kResThreads) {
+    const int span_len = (int)min(max(bounds[1] - s0, (int64_t)0), (int64_t)kResLdsFloats);
+    for (int i = tid; i < span_len; i += blockDim.x) {
       const int64_t k = s0 + i;
       span[i] = (k >= 0 && k < total_in) ? res_sample(x, k) : 0.0f;
     }
     __syncthreads();
-    if (!active) continue;
-    const int64_t off = k0 - s0;
-    const float* tp = tab + phi * T;
-    float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
-    if (off >= 0 && off + T <= span_len) {
-      const float* sp = span + off;
-      if (k0 >= lo && k0 + T <= hi) {
-        // the whole window inside the clip
-        int j = 0;
-        for (; j + 4 <= T; j += 4) {
-          a0 = __builtin_fmaf(tp[j], sp[j], a0);
-          a1 = __builtin_fmaf(tp[j + 1], sp[j + 1], a1);
-          a2 = __builtin_fmaf(tp[j + 2], sp[j + 2], a2);
-          a3 = __builtin_fmaf(tp[j + 3], sp[j + 3], a3);
-        }
-        for (; j < T; ++j) a0 = __builtin_fmaf(tp[j], sp[j], a0);
-      } else {
-        // a clip edge inside the window: samples outside the clip are zero
-        const int jlo = (int)max((int64_t)0, lo - k0);
-        const int jhi = (int)min((int64_t)T, hi - k0);
-        for (int j = jlo; j < jhi; ++j) a0 = __builtin_fmaf(tp[j], sp[j], a0);
+
+    ResClip cl{-1, 0, -1, 0, 0};
+    for (int it = wave; it < items; it += n_waves) {
+      const int gi = it / L;
+      const int r = it - gi * L;
+      const int64_t g = g0 + (int64_t)(gi * 64 + lane) * L + r;
+      const bool active = g < total_out;
+      ResSrc s{};
+      bool ok = false;
+      int64_t off = 0;
+      if (active) {
+        if (!(cl.o_lo <= g && g < cl.o_hi)) cl = res_clip(g, in_off, out_off, n_clips);
+        s = res_pos(g, cl, L, M, J, inv_L);
+        off = s.k0 - s0;
+        ok = s.k0 >= s.lo && s.k0 + T <= s.hi && off >= 0 && off + Tp <= span_len;
       }
-    } else {
-      // not reached for packed offsets (the span covers every window); kept
-      // as a correct path from global memory
-      const int jlo = (int)max((int64_t)0, lo - k0);
-      const int jhi = (int)min((int64_t)T, hi - k0);
-      for (int j = jlo; j < jhi; ++j) a0 = __builtin_fmaf(tp[j], res_sample(x, k0 + j), a0);
+      // The lanes with a whole window, one phase at a time (one pass unless
+      // the item's outputs lie in several clips): the first waiting lane's
+      // phase, shared by the lanes that have it.
+      uint64_t waiting = __ballot(ok);
+      while (waiting) {
+        const int lead = __builtin_ctzll(waiting);
+        const int phi_w = __builtin_amdgcn_readlane(s.phi, lead);
+        const bool mine = ok && s.phi == phi_w;
+        waiting &= ~__ballot(mine);
+        if (mine) {
+          // The lanes here all have phase phi_w: the row address is uniform
+          // (taken with readfirstlane, so that it stays scalar), read through
+          // the constant address space, so the taps load with scalar loads
+          // into scalar registers.
+          const int pu = __builtin_amdgcn_readfirstlane(s.phi);
+          const __attribute__((address_space(4))) float* trow =
+              (const __attribute__((address_space(4))) float*)(taps + (int64_t)pu * Tp);
+          const float* sp = span + off;
+          float a0 = 0.0f, a1 = 0.0f;
+          const int full = T / kResChunk;
+          // Software pipeline over chunks of 16 taps, two buffers: the next
+          // chunk's taps (scalar loads) and samples (LDS reads) are issued
+          // before this chunk's multiply-adds and waited after them (scalar
+          // loads return out of order, so one wait covers both kinds).
+          ResChunk A, B;
+          res_load(trow, sp, 0, A);
+          res_wait(A);
+          int ch = 0;
+          for (; ch + 2 <= full; ch += 2) {
+            res_load(trow, sp, ch + 1, B);
+            asm volatile("" ::: "memory");
+            res_fma(A, a0, a1);
+            res_wait(B);
+            res_load(trow, sp, min(ch + 2, full - 1), A);
+            asm volatile("" ::: "memory");
+            res_fma(B, a0, a1);
+            res_wait(A);
+          }
+          if (ch < full) res_fma(A, a0, a1);
+          // the last chunk: samples past the window's T taps are not read
+          const int base = full * kResChunk;
+#pragma unroll
+          for (int j = 0; j < kResChunk; ++j)
+            if (base + j < T) a0 = __builtin_fmaf(trow[base + j], sp[base + j], a0);
+          y[g] = a0 + a1;
+        }
+      }
+      if (active && !ok) y[g] = res_one(s, taps, Tp, T, span, s0, span_len, x);
     }
-    y[g] = (a0 + a1) + (a2 + a3);
   }
 }
 
 #define LOGMEL_RESAMPLE_KERNEL(NAME, IN)                                                         \
-  extern "C" __global__ void __launch_bounds__(kResThreads)                                      \
+  extern "C" __global__ void __launch_bounds__(1024)                                             \
   NAME(const IN* __restrict__ x, const int64_t* __restrict__ in_off,                             \
        const int64_t* __restrict__ out_off, int64_t n_clips, int64_t total_out,                   \
-       float* __restrict__ y, const float* __restrict__ taps, int L, int M, int J,                \
-       int span_cap) {                                                                           \
-    __shared__ float lds[kResLdsFloats];                                                         \
+       float* __restrict__ y, const float* __restrict__ taps, int L, int M, int J, int Tp,       \
+       int G) {                                                                                  \
+    __shared__ float span[kResLdsFloats];                                                        \
     __shared__ int64_t bounds[2];                                                                \
-    resample_body<IN>(x, in_off, out_off, n_clips, total_out, y, taps, L, M, J, span_cap, lds,   \
+    resample_body<IN>(x, in_off, out_off, n_clips, total_out, y, taps, L, M, J, Tp, G, span,     \
                       bounds);                                                                   \
   }
 
@@ -136,18 +303,19 @@ LOGMEL_RESAMPLE_KERNEL(logmel_resample_i16_kernel, int16_t)
 
 hipError_t logmel_launch_resample(const void* x, int in_i16, const int64_t* in_off,
                                   const int64_t* out_off, int64_t n_clips, int64_t total_out,
-                                  float* y, const float* taps, int L, int M, int J, int span_cap,
+                                  float* y, const float* taps, int L, int M, int J, int Tp, int G,
                                   int grid, hipStream_t stream) {
   if (total_out <= 0) return hipSuccess;
-  const int64_t blocks = (total_out + logmel::kResThreads - 1) / logmel::kResThreads;
+  const int64_t per_block = (int64_t)64 * G * L;
+  const int64_t blocks = (total_out + per_block - 1) / per_block;
   const int g = (int)(blocks < grid ? blocks : grid);
   if (in_i16)
-    hipLaunchKernelGGL(logmel::logmel_resample_i16_kernel, dim3(g), dim3(logmel::kResThreads), 0,
-                       stream, static_cast<const int16_t*>(x), in_off, out_off, n_clips,
-                       total_out, y, taps, L, M, J, span_cap);
+    hipLaunchKernelGGL(logmel::logmel_resample_i16_kernel, dim3(g), dim3(1024), 0, stream,
+                       static_cast<const int16_t*>(x), in_off, out_off, n_clips, total_out, y,
+                       taps, L, M, J, Tp, G);
   else
-    hipLaunchKernelGGL(logmel::logmel_resample_kernel, dim3(g), dim3(logmel::kResThreads), 0,
-                       stream, static_cast<const float*>(x), in_off, out_off, n_clips, total_out,
-                       y, taps, L, M, J, span_cap);
+    hipLaunchKernelGGL(logmel::logmel_resample_kernel, dim3(g), dim3(1024), 0, stream,
+                       static_cast<const float*>(x), in_off, out_off, n_clips, total_out, y,
+                       taps, L, M, J, Tp, G);
   return hipGetLastError();
 }
