@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "logmel_launch.h"
+#include "logmel_resample_launch.h"
 
 namespace {
 

@@ -28,7 +28,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "logmel_launch.h"
+#include "logmel_resample_launch.h"
 
 namespace logmel {
 
@@ -218,9 +218,19 @@ __device__ __forceinline__ void resample_body(const In* __restrict__ x,
     __syncthreads();
 
     ResClip cl{-1, 0, -1, 0, 0};
+    // items it = wave, wave + n_waves, ... as (period group gi, phase r)
+    // with it = gi L + r, stepped without a division
+    int gi = wave / L, r = wave - (wave / L) * L;
+    const int step_q = n_waves / L, step_r = n_waves - (n_waves / L) * L;
     for (int it = wave; it < items; it += n_waves) {
-      const int gi = it / L;
-      const int r = it - gi * L;
+      if (it != wave) {
+        gi += step_q;
+        r += step_r;
+        if (r >= L) {
+          r -= L;
+          ++gi;
+        }
+      }
       const int64_t g = g0 + (int64_t)(gi * 64 + lane) * L + r;
       const bool active = g < total_out;
       ResSrc s{};
