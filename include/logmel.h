@@ -207,6 +207,16 @@ int logmel_stream_frames_for_push(const logmel_stream* s, const int64_t* push_le
 int logmel_stream_push(logmel_stream* s, const float* d_new, const int64_t* push_len_host,
                        float* d_out, int64_t* out_frame_offsets_host, void* hip_stream);
 
+/* logmel_stream_push with the sample and output types of logmel_compute_ex:
+ * d_new fp32 or int16 PCM (sample_type LOGMEL_F32 / LOGMEL_I16; s means
+ * s / 32768, exact), d_out fp32 or fp16 (out_type LOGMEL_F32 / LOGMEL_F16,
+ * each value the fp32 result rounded once to nearest). A stream may mix
+ * types from push to push: its carry is kept as fp32 values. UNSUPPORTED for
+ * other types. */
+int logmel_stream_push_ex(logmel_stream* s, const void* d_new, int sample_type,
+                          const int64_t* push_len_host, void* d_out, int out_type,
+                          int64_t* out_frame_offsets_host, void* hip_stream);
+
 /* Total samples pushed and frames emitted so far for stream j. */
 int logmel_stream_counters(const logmel_stream* s, int64_t j, int64_t* samples_seen,
                            int64_t* frames_emitted);

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "liblogmel.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is not built; run `python -m log_mel_spectrogram_amd.build` "
+        f"{LIB_PATH} is not built; run `python log_mel_spectrogram_amd/build.py` "
         "(hipcc for gfx950). There is no CPU fallback.")
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -79,6 +79,8 @@ _stream_destroy = _sig("logmel_stream_destroy", None, _p)
 _stream_reset = _sig("logmel_stream_reset", ctypes.c_int, _p)
 _stream_frames_for_push = _sig("logmel_stream_frames_for_push", ctypes.c_int, _p, _i64p, _i64p)
 _stream_push = _sig("logmel_stream_push", ctypes.c_int, _p, _p, _i64p, _p, _i64p, _p)
+_stream_push_ex = _sig("logmel_stream_push_ex", ctypes.c_int, _p, _p, ctypes.c_int, _i64p, _p,
+                       ctypes.c_int, _i64p, _p)
 _stream_counters = _sig("logmel_stream_counters", ctypes.c_int, _p, _i64, _i64p, _i64p)
 _stream_state_bytes = _sig("logmel_stream_state_bytes", _i64, _p)
 _stream_get_state = _sig("logmel_stream_get_state", ctypes.c_int, _p, _p, _p)
@@ -99,7 +101,7 @@ EXPORTED = [
     "logmel_frame_offsets", "logmel_compute", "logmel_chunk_offsets", "logmel_chunk_frames",
     "logmel_compute_chunked", "logmel_compute_ex", "logmel_stream_create",
     "logmel_stream_destroy", "logmel_stream_reset", "logmel_stream_frames_for_push",
-    "logmel_stream_push", "logmel_stream_counters", "logmel_stream_state_bytes",
+    "logmel_stream_push", "logmel_stream_push_ex", "logmel_stream_counters", "logmel_stream_state_bytes",
     "logmel_stream_get_state", "logmel_stream_set_state", "logmel_resample_length",
     "logmel_resample_offsets", "logmel_resampler_create", "logmel_resampler_destroy",
     "logmel_resampler_info", "logmel_resample",
@@ -383,25 +385,47 @@ def logmel_stream_frames_for_push(s: Stream, push_len) -> np.ndarray:
     return fo
 
 
-def logmel_stream_push(s: Stream, new_samples, push_len, out=None, stream=None):
-    """Pushes packed new samples; returns (out [frames, 128], frame offsets)."""
+def logmel_stream_push(s: Stream, new_samples, push_len, out=None, stream=None, out_dtype=None):
+    """Pushes packed new samples; returns (out [frames, 128], frame offsets).
+
+    new_samples fp32 or int16 (s / 32768); output fp32 or fp16 (out_dtype,
+    default fp32, or out's dtype)."""
     torch = _torch()
     pl = _i64_array(push_len)
     if pl.size != s.n_streams:
         raise ValueError("push_len must have n_streams entries")
     if int(pl.sum()) != int(new_samples.numel()):
         raise ValueError("new_samples must hold sum(push_len) samples")
+    if new_samples.dtype == torch.float32:
+        st_in = LOGMEL_F32
+    elif new_samples.dtype == torch.int16:
+        st_in = LOGMEL_I16
+    else:
+        raise TypeError(f"new_samples must be float32 or int16, got {new_samples.dtype}")
+    out_dtype = out_dtype or (out.dtype if out is not None else torch.float32)
+    if out_dtype == torch.float32:
+        st_out = LOGMEL_F32
+    elif out_dtype == torch.float16:
+        st_out = LOGMEL_F16
+    else:
+        raise TypeError(f"output must be float32 or float16, got {out_dtype}")
     fo = logmel_stream_frames_for_push(s, pl)
     total = int(fo[-1])
     if out is None:
-        out = torch.empty((total, N_MELS), dtype=torch.float32, device=new_samples.device)
+        out = torch.empty((total, N_MELS), dtype=out_dtype, device=new_samples.device)
     if tuple(out.shape) != (total, N_MELS):
         raise ValueError(f"out must be [{total}, {N_MELS}]")
     st = _stream_handle(stream, new_samples.device)
     fo2 = np.zeros(s.n_streams + 1, dtype=np.int64)
-    _check(_stream_push(s.handle, _dev_ptr(new_samples, torch.float32, "new_samples"),
-                        _ptr64(pl), _dev_ptr(out, torch.float32, "out"), _ptr64(fo2), st),
-           "logmel_stream_push")
+    if st_in == LOGMEL_F32 and st_out == LOGMEL_F32:
+        _check(_stream_push(s.handle, _dev_ptr(new_samples, torch.float32, "new_samples"),
+                            _ptr64(pl), _dev_ptr(out, torch.float32, "out"), _ptr64(fo2), st),
+               "logmel_stream_push")
+    else:
+        _check(_stream_push_ex(s.handle, _dev_ptr(new_samples, new_samples.dtype, "new_samples"),
+                               st_in, _ptr64(pl), _dev_ptr(out, out_dtype, "out"), st_out,
+                               _ptr64(fo2), st),
+               "logmel_stream_push_ex")
     return out, fo2
 
 

@@ -1,6 +1,6 @@
 """Builds liblogmel.so in-tree for gfx950 with hipcc.
 
-    python -m log_mel_spectrogram_amd.build
+    python log_mel_spectrogram_amd/build.py
 
 Steps: generate csrc/logmel_tables.h (fp64 math, fp32 literals), then one
 hipcc invocation compiling the kernels and the C-ABI layer into a shared
@@ -35,6 +35,7 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
            os.path.join(CSRC, "logmel_kernels.hip"), os.path.join(CSRC, "logmel_resample.hip"),
+           os.path.join(CSRC, "logmel_stream.hip"),
            os.path.join(CSRC, "logmel_api.cpp"),
            "-o", tmp]
     if verbose:

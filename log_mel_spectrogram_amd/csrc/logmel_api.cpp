@@ -362,7 +362,16 @@ int logmel_stream_frames_for_push(const logmel_stream* s, const int64_t* push_le
 
 int logmel_stream_push(logmel_stream* s, const float* d_new, const int64_t* push_len,
                        float* d_out, int64_t* fo_out, void* hip_stream) {
+  return logmel_stream_push_ex(s, d_new, LOGMEL_F32, push_len, d_out, LOGMEL_F32, fo_out,
+                               hip_stream);
+}
+
+int logmel_stream_push_ex(logmel_stream* s, const void* d_new, int sample_type,
+                          const int64_t* push_len, void* d_out, int out_type, int64_t* fo_out,
+                          void* hip_stream) {
   if (!s || !push_len) return LOGMEL_ERR_INVALID_ARGUMENT;
+  if (sample_type != LOGMEL_F32 && sample_type != LOGMEL_I16) return LOGMEL_ERR_UNSUPPORTED;
+  if (out_type != LOGMEL_F32 && out_type != LOGMEL_F16) return LOGMEL_ERR_UNSUPPORTED;
   const int64_t n = s->n;
   int64_t total_new = 0;
   for (int64_t j = 0; j < n; ++j) {
@@ -403,11 +412,13 @@ int logmel_stream_push(logmel_stream* s, const float* d_new, const int64_t* push
       hipEventRecord(s->slot_done[slot], st) != hipSuccess)
     return LOGMEL_ERR_DEVICE;
   s->slot = (slot + 1) % logmel_stream::kSlots;
-  if (logmel_launch_stream_prep(s->ws, s->stride, d_new, s->meta_dev, n, st) != hipSuccess)
+  if (logmel_launch_stream_prep(s->ws, s->stride, d_new, sample_type == LOGMEL_I16, s->meta_dev,
+                                n, st) != hipSuccess)
     return LOGMEL_ERR_DEVICE;
   if (logmel_launch_tiles(s->plan->tables, s->ws, 0, s->meta_dev + 4 * n, s->meta_dev + 5 * n,
-                          s->meta_dev + 6 * n, n, total_frames, d_out, 0, s->meta_dev + 6 * n, 1,
-                          total_frames, s->plan->resident_waves, st) != hipSuccess)
+                          s->meta_dev + 6 * n, n, total_frames, d_out, out_type == LOGMEL_F16,
+                          s->meta_dev + 6 * n, 1, total_frames, s->plan->resident_waves, st) !=
+      hipSuccess)
     return LOGMEL_ERR_DEVICE;
   // Advance the host shadow.
   for (int64_t j = 0; j < n; ++j) {

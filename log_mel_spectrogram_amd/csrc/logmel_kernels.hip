@@ -20,12 +20,10 @@
 // logmel_chunk_pad_kernel (and _f16): the padding rows of the 30-s chunk
 //   layout.
 //
-// logmel_stream_prep_kernel: the streaming push, step 1. Moves each stream's
-//   carry (the samples of its next, not yet complete frame) to sit right
-//   before the new samples in the stream's workspace row, and appends the new
-//   samples. The frames themselves are then computed by logmel_tiles_kernel
-//   over the per-stream segments, so a streamed frame is bit-for-bit the
-//   offline frame.
+// The streaming push's first step (moving each stream's carry and appending
+// its new samples) is in logmel_stream.hip; its frames are then computed by
+// logmel_tiles_kernel over the per-stream segments, so a streamed frame is
+// bit-for-bit the offline frame.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -597,39 +595,6 @@ logmel_chunk_pad_f16_kernel(_Float16* __restrict__ out, const int64_t* __restric
   chunk_pad_body<_Float16>(out, frame_off, chunk_off, out_rows, floor);
 }
 
-// One workgroup per stream. meta layout (int64, n = n_streams):
-//   [0n, 1n)  carry source index in ws (absolute)
-//   [1n, 2n)  carry length (< 400)
-//   [2n, 3n)  offset of the stream's new samples in `fresh`
-//   [3n, 4n)  number of new samples
-//   [4n, 5n)  segment start in ws  (= row base + 400 - carry length)
-//   [5n, 6n)  segment end in ws    (= row base + 400 + new samples)
-//   [6n, 7n+1) output frame offsets
-extern "C" __global__ void __launch_bounds__(256)
-logmel_stream_prep_kernel(float* __restrict__ ws, int64_t row_stride,
-                          const float* __restrict__ fresh,
-                          const int64_t* __restrict__ meta, int64_t n_streams)
-{
-  const int64_t j = blockIdx.x;
-  const int t = threadIdx.x;
-  const int64_t base = j * row_stride;
-  const int64_t src = meta[j];
-  const int64_t clen = meta[n_streams + j];
-  const int64_t noff = meta[2 * n_streams + j];
-  const int64_t nlen = meta[3 * n_streams + j];
-  // The carry can overlap its destination: read it all before any write.
-  float c0 = 0.f, c1 = 0.f;
-  if (t < clen) c0 = ws[src + t];
-  if (t + 256 < clen) c1 = ws[src + t + 256];
-  __syncthreads();
-  const int64_t dst = base + 400 - clen;
-  if (t < clen) ws[dst + t] = c0;
-  if (t + 256 < clen) ws[dst + t + 256] = c1;
-  float* row = ws + base + 400;
-  const float* in = fresh + noff;
-  for (int64_t i = t; i < nlen; i += 256) row[i] = in[i];
-}
-
 }  // namespace logmel
 
 // ---------------------------------------------------------------------------
@@ -687,13 +652,4 @@ hipError_t logmel_launch_chunk_pad(void* out, int out_f16, const int64_t* frame_
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
-}
-
-hipError_t logmel_launch_stream_prep(float* ws, int64_t row_stride, const float* fresh,
-                                     const int64_t* meta, int64_t n_streams,
-                                     hipStream_t stream) {
-  if (n_streams <= 0) return hipSuccess;
-  hipLaunchKernelGGL(logmel::logmel_stream_prep_kernel, dim3((unsigned)n_streams), dim3(256), 0,
-                     stream, ws, row_stride, fresh, meta, n_streams);
-  return hipGetLastError();
 }

@@ -1,0 +1,80 @@
+// The streaming push, step 1 (gfx950): moves each stream's carry (the
+// samples of its next, not yet complete frame) to sit right before the new
+// samples in the stream's workspace row, and appends the new samples
+// (fp32, or int16 PCM converted to s / 32768, exact). The frames are then
+// computed by logmel_tiles_kernel over the per-stream segments, so a
+// streamed frame is bit-for-bit the offline frame of the same samples.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "logmel_launch.h"
+
+namespace logmel {
+
+__device__ __forceinline__ float stream_sample(const float* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float stream_sample(const int16_t* p, int64_t i) {
+  return (float)p[i] * (1.0f / 32768.0f);
+}
+
+// One workgroup per stream. meta layout (int64, n = n_streams):
+//   [0n, 1n)  carry source index in ws (absolute)
+//   [1n, 2n)  carry length (< 400)
+//   [2n, 3n)  offset of the stream's new samples in `fresh`
+//   [3n, 4n)  number of new samples
+//   [4n, 5n)  segment start in ws  (= row base + 400 - carry length)
+//   [5n, 6n)  segment end in ws    (= row base + 400 + new samples)
+//   [6n, 7n+1) output frame offsets
+template <typename In>
+__device__ __forceinline__ void stream_prep_body(float* __restrict__ ws, int64_t row_stride,
+                                                 const In* __restrict__ fresh,
+                                                 const int64_t* __restrict__ meta,
+                                                 int64_t n_streams) {
+  const int64_t j = blockIdx.x;
+  const int t = threadIdx.x;
+  const int64_t base = j * row_stride;
+  const int64_t src = meta[j];
+  const int64_t clen = meta[n_streams + j];
+  const int64_t noff = meta[2 * n_streams + j];
+  const int64_t nlen = meta[3 * n_streams + j];
+  // The carry can overlap its destination: read it all before any write.
+  float c0 = 0.f, c1 = 0.f;
+  if (t < clen) c0 = ws[src + t];
+  if (t + 256 < clen) c1 = ws[src + t + 256];
+  __syncthreads();
+  const int64_t dst = base + 400 - clen;
+  if (t < clen) ws[dst + t] = c0;
+  if (t + 256 < clen) ws[dst + t + 256] = c1;
+  float* row = ws + base + 400;
+  const In* in = fresh + noff;
+  for (int64_t i = t; i < nlen; i += 256) row[i] = stream_sample(in, i);
+}
+
+extern "C" __global__ void __launch_bounds__(256)
+logmel_stream_prep_kernel(float* __restrict__ ws, int64_t row_stride,
+                          const float* __restrict__ fresh, const int64_t* __restrict__ meta,
+                          int64_t n_streams) {
+  stream_prep_body(ws, row_stride, fresh, meta, n_streams);
+}
+
+extern "C" __global__ void __launch_bounds__(256)
+logmel_stream_prep_i16_kernel(float* __restrict__ ws, int64_t row_stride,
+                              const int16_t* __restrict__ fresh, const int64_t* __restrict__ meta,
+                              int64_t n_streams) {
+  stream_prep_body(ws, row_stride, fresh, meta, n_streams);
+}
+
+}  // namespace logmel
+
+hipError_t logmel_launch_stream_prep(float* ws, int64_t row_stride, const void* fresh, int in_i16,
+                                     const int64_t* meta, int64_t n_streams,
+                                     hipStream_t stream) {
+  if (n_streams <= 0) return hipSuccess;
+  if (in_i16)
+    hipLaunchKernelGGL(logmel::logmel_stream_prep_i16_kernel, dim3((unsigned)n_streams), dim3(256),
+                       0, stream, ws, row_stride, static_cast<const int16_t*>(fresh), meta,
+                       n_streams);
+  else
+    hipLaunchKernelGGL(logmel::logmel_stream_prep_kernel, dim3((unsigned)n_streams), dim3(256), 0,
+                       stream, ws, row_stride, static_cast<const float*>(fresh), meta, n_streams);
+  return hipGetLastError();
+}

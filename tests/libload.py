@@ -9,7 +9,12 @@ LIB = os.path.join(ROOT, "log_mel_spectrogram_amd", "liblogmel.so")
 
 def load_binding():
     if not os.path.exists(LIB):
-        from log_mel_spectrogram_amd.build import build
-        build()
+        # build.py by path: importing the package itself needs the library
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "logmel_build", os.path.join(ROOT, "log_mel_spectrogram_amd", "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
     import log_mel_spectrogram_amd as lm
     return lm

@@ -201,3 +201,61 @@ def test_other_clocks_equal_offline(env, push, first, steady):
     assert torch.equal(streamed.reshape(-1, 128), ref), "stream != offline"
     assert lm.logmel_stream_counters(s, 0) == (N, 2998)
     s.close()
+
+
+def test_int16_and_fp16_streams_equal_offline(env):
+    """int16 PCM pushes and fp16 output: the streamed frames equal the offline
+    frames of the same samples and types bit for bit; a stream fed int16 and
+    fp32 pushes of the same values in turn equals the fp32 offline result."""
+    lm, plan, torch = env
+    say("int16 / fp16 streams: 24 streams x 4 s, pushes of 1280 and ragged")
+    dev = torch.device("cuda", 0)
+    n, N = 24, 64000
+    x = torch.stack([S.speech_like(700 + j, N, "cuda") for j in range(n)])
+    s16 = torch.clamp(torch.round(x * 32768.0), -32768, 32767).to(torch.int16)
+    x32 = s16.to(torch.float32) / 32768.0
+    so = np.arange(n + 1, dtype=np.int64) * N
+    fo = lm.logmel_frame_offsets(so)
+    so_d = torch.from_numpy(so).to(dev)
+    fo_d = torch.from_numpy(fo).to(dev)
+    T = int(fo[-1])
+    ref32 = lm.logmel_compute_ex(plan, x32.reshape(-1).contiguous(), so_d, fo_d, T)
+    ref16 = lm.logmel_compute_ex(plan, x32.reshape(-1).contiguous(), so_d, fo_d, T,
+                                 out_dtype=torch.float16)
+    rng = np.random.default_rng(9)
+    for case, (inp, odt, ref) in {"int16 in": (s16, torch.float32, ref32),
+                                  "fp16 out": (x32, torch.float16, ref16),
+                                  "int16 in, fp16 out": (s16, torch.float16, ref16),
+                                  "int16 and fp32 pushes": (None, torch.float32, ref32)}.items():
+        s = lm.logmel_stream_create(plan, n, 2000)
+        got = [[] for _ in range(n)]
+        pos = np.zeros(n, dtype=np.int64)
+        k = 0
+        while (pos < N).any():
+            pl = np.minimum(rng.integers(0, 2001, n) if k % 3 == 2 else np.full(n, 1280), N - pos)
+            src = inp if inp is not None else (s16 if k % 2 == 0 else x32)
+            new = torch.cat([src[j, pos[j]:pos[j] + pl[j]] for j in range(n)]).contiguous()
+            out, f = lm.logmel_stream_push(s, new, pl, out_dtype=odt)
+            for j in range(n):
+                if f[j + 1] > f[j]:
+                    got[j].append(out[f[j]:f[j + 1]])
+            pos += pl
+            k += 1
+        torch.cuda.synchronize()
+        for j in range(n):
+            g = torch.cat(got[j])
+            assert g.dtype == odt
+            assert torch.equal(g, ref[fo[j]:fo[j + 1]]), (case, j)
+        s.close()
+        say(f"{case}: equal to offline")
+
+
+def test_stream_push_ex_rejects_types(env):
+    lm, plan, torch = env
+    s = lm.logmel_stream_create(plan, 2, 100)
+    pl = np.array([0, 0], dtype=np.int64)
+    assert lm._stream_push_ex(s.handle, None, 7, lm._ptr64(pl), None, lm.LOGMEL_F32, None,
+                              None) == lm.LOGMEL_ERR_UNSUPPORTED
+    assert lm._stream_push_ex(s.handle, None, lm.LOGMEL_F32, lm._ptr64(pl), None, 9, None,
+                              None) == lm.LOGMEL_ERR_UNSUPPORTED
+    s.close()
