@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Throughput of the 128-bin log-mel front end on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c4|c3|c1]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c4|c3|c1|p3]
                     [--in-rate R]  (c2 made at R Hz, resampled to 16 kHz in the step)
 
 Prints one JSON line. A step is one logmel_compute over one batch of
@@ -133,6 +133,10 @@ def make_workload(name, device):
     elif name == "c1":
         x, so = S.config1(device=device)
         desc = "1 speech-like clip, 30 s (480000 fp32 samples)"
+    elif name == "p3":
+        # the shape of the transcribe.cpp page's timing: one 11-s clip
+        x, so = S.pack([176000], lambda i, v: S.speech_like(7, 176000, device, out=v), device)
+        desc = "1 speech-like clip, 11 s (176000 fp32 samples, 1098 frames)"
     elif name == "c4":
         x, so = S.config4(device=device)
         desc = ("ragged long batch: 200 speech-like clips, log-uniform 0.5 s..87 min, "
@@ -171,6 +175,8 @@ def bench_offline(args, lm, plan, torch):
         out_rows = total
     set_bytes = (2 if in_i16 else 4) * n_samples + (256 if out_f16 else 512) * out_rows
     n_sets = max(1, min(5, int(math.ceil(1.1e9 / set_bytes)))) if args.workload != "c4" else 1
+    if args.workload == "p3":
+        n_sets = 1   # a latency run: the one clip, resident
     xs = [x] + [x.clone() for _ in range(n_sets - 1)]
     if chunked:
         outs = [torch.empty((n_chunks, lm.CHUNK_FRAMES, 128), dtype=out_dtype, device=dev)
@@ -223,7 +229,10 @@ def bench_offline(args, lm, plan, torch):
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": None,
+        # The only page number for this stage is the transcribe.cpp page's mel
+        # time for 11 s of audio on an Apple M4 Max (best: 43 ms, 256 audio-s/s,
+        # Vulkan): a ratio only for that workload's shape, as context.
+        "vs_baseline": (audio_s / (ms_per_step / 1e3)) / (11.0 / 0.043) if args.workload == "p3" else None,
         "dtype": "f64",
         "data": "synthetic",
         "config": {"workload": desc, "clips": len(so) - 1, "samples": n_samples,
@@ -443,7 +452,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="c2", choices=["c2", "c1", "c4", "c3"])
+    ap.add_argument("--workload", default="c2", choices=["c2", "c1", "c4", "c3", "p3"])
     ap.add_argument("--clock-ms", type=int, default=80, choices=[80, 120, 160],
                     help="audio clock of the streaming workload (c3)")
     ap.add_argument("--in-dtype", default="f32", choices=["f32", "i16"],
@@ -464,7 +473,7 @@ def main():
               "(frames are independent, so several GPUs would each run this same kernel "
               "on their own share of the batch)", file=sys.stderr)
         sys.exit(2)
-    defaults = {"c2": (200, 20), "c1": (500, 50), "c4": (5, 2), "c3": (3, 1)}
+    defaults = {"c2": (200, 20), "c1": (500, 50), "c4": (5, 2), "c3": (3, 1), "p3": (500, 50)}
     if args.in_rate != FS:
         defaults["c2"] = (50, 5)
     if args.steps is None:

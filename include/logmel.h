@@ -217,6 +217,27 @@ int logmel_stream_push_ex(logmel_stream* s, const void* d_new, int sample_type,
                           const int64_t* push_len_host, void* d_out, int out_type,
                           int64_t* out_frame_offsets_host, void* hip_stream);
 
+/* Streams at another input rate (the resampling reading below: Kaiser-
+ * windowed sinc to 16 kHz): in_rate 16000 is logmel_stream_create; other
+ * rates resample every push to 16 kHz on the device before framing.
+ * max_push counts input samples. A stream's frames over all its pushes and
+ * its flush are, bit for bit, the offline frames of logmel_resample of the
+ * concatenated input followed by logmel_compute: each 16 kHz sample is
+ * formed once its whole window has arrived, and the last ones (whose windows
+ * reach past the input) at logmel_stream_flush. UNSUPPORTED for rates the
+ * resampler does not take; snapshot and restore are UNSUPPORTED for such
+ * streams. logmel_stream_counters reports input samples for them. */
+int logmel_stream_create_ex(const logmel_plan* plan, int64_t n_streams, int64_t max_push,
+                            int32_t in_rate, logmel_stream** out);
+
+/* Ends every stream: emits the frames that only the end of the input
+ * completes (for 16 kHz streams none: a partial frame is dropped, as
+ * offline), then resets the streams. d_out and the offsets as for a push;
+ * logmel_stream_frames_for_flush gives the offsets beforehand. */
+int logmel_stream_frames_for_flush(const logmel_stream* s, int64_t* out_frame_offsets_host);
+int logmel_stream_flush(logmel_stream* s, void* d_out, int out_type,
+                        int64_t* out_frame_offsets_host, void* hip_stream);
+
 /* Total samples pushed and frames emitted so far for stream j. */
 int logmel_stream_counters(const logmel_stream* s, int64_t j, int64_t* samples_seen,
                            int64_t* frames_emitted);

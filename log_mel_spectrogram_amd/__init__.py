@@ -75,6 +75,10 @@ _compute_chunked = _sig("logmel_compute_chunked", ctypes.c_int, _p, _p, _p, _p, 
 _compute_ex = _sig("logmel_compute_ex", ctypes.c_int, _p, _p, ctypes.c_int, _p, _p, _p, _i64, _i64,
                    _i64, _p, ctypes.c_int, _p)
 _stream_create = _sig("logmel_stream_create", ctypes.c_int, _p, _i64, _i64, ctypes.POINTER(_p))
+_stream_create_ex = _sig("logmel_stream_create_ex", ctypes.c_int, _p, _i64, _i64, ctypes.c_int32,
+                         ctypes.POINTER(_p))
+_stream_frames_for_flush = _sig("logmel_stream_frames_for_flush", ctypes.c_int, _p, _i64p)
+_stream_flush = _sig("logmel_stream_flush", ctypes.c_int, _p, _p, ctypes.c_int, _i64p, _p)
 _stream_destroy = _sig("logmel_stream_destroy", None, _p)
 _stream_reset = _sig("logmel_stream_reset", ctypes.c_int, _p)
 _stream_frames_for_push = _sig("logmel_stream_frames_for_push", ctypes.c_int, _p, _i64p, _i64p)
@@ -101,7 +105,8 @@ EXPORTED = [
     "logmel_frame_offsets", "logmel_compute", "logmel_chunk_offsets", "logmel_chunk_frames",
     "logmel_compute_chunked", "logmel_compute_ex", "logmel_stream_create",
     "logmel_stream_destroy", "logmel_stream_reset", "logmel_stream_frames_for_push",
-    "logmel_stream_push", "logmel_stream_push_ex", "logmel_stream_counters", "logmel_stream_state_bytes",
+    "logmel_stream_push", "logmel_stream_push_ex", "logmel_stream_counters",
+    "logmel_stream_create_ex", "logmel_stream_frames_for_flush", "logmel_stream_flush", "logmel_stream_state_bytes",
     "logmel_stream_get_state", "logmel_stream_set_state", "logmel_resample_length",
     "logmel_resample_offsets", "logmel_resampler_create", "logmel_resampler_destroy",
     "logmel_resampler_info", "logmel_resample",
@@ -344,14 +349,16 @@ def log_mel(plan: Plan, samples, sample_offsets_host, stream=None):
 class Stream:
     """Owns a logmel_stream handle (n_streams independent streams)."""
 
-    def __init__(self, plan: Plan, n_streams: int, max_push: int):
+    def __init__(self, plan: Plan, n_streams: int, max_push: int, in_rate: int = SAMPLE_RATE):
         h = _p()
-        _check(_stream_create(plan.handle, int(n_streams), int(max_push), ctypes.byref(h)),
-               "logmel_stream_create")
+        _check(_stream_create_ex(plan.handle, int(n_streams), int(max_push), int(in_rate),
+                                 ctypes.byref(h)),
+               "logmel_stream_create_ex")
         self.handle = h
         self.plan = plan
         self.n_streams = int(n_streams)
         self.max_push = int(max_push)
+        self.in_rate = int(in_rate)
         self._destroy = _stream_destroy
 
     def close(self):
@@ -363,8 +370,42 @@ class Stream:
         self.close()
 
 
-def logmel_stream_create(plan: Plan, n_streams: int, max_push: int) -> Stream:
-    return Stream(plan, n_streams, max_push)
+def logmel_stream_create(plan: Plan, n_streams: int, max_push: int,
+                         in_rate: int = SAMPLE_RATE) -> Stream:
+    """n_streams streams taking up to max_push samples per push at in_rate
+    (other rates than 16 kHz are resampled on the device)."""
+    return Stream(plan, n_streams, max_push, in_rate)
+
+
+def logmel_stream_frames_for_flush(s: Stream) -> np.ndarray:
+    fo = np.zeros(s.n_streams + 1, dtype=np.int64)
+    _check(_stream_frames_for_flush(s.handle, _ptr64(fo)), "logmel_stream_frames_for_flush")
+    return fo
+
+
+def logmel_stream_flush(s: Stream, out=None, out_dtype=None, stream=None, device=None):
+    """Ends every stream (emitting what only the end of the input completes)
+    and resets them; returns (out [frames, 128], frame offsets)."""
+    torch = _torch()
+    out_dtype = out_dtype or (out.dtype if out is not None else torch.float32)
+    if out_dtype == torch.float32:
+        st_out = LOGMEL_F32
+    elif out_dtype == torch.float16:
+        st_out = LOGMEL_F16
+    else:
+        raise TypeError(f"output must be float32 or float16, got {out_dtype}")
+    fo = logmel_stream_frames_for_flush(s)
+    total = int(fo[-1])
+    dev = device if device is not None else torch.device("cuda", s.plan.device)
+    if out is None:
+        out = torch.empty((total, N_MELS), dtype=out_dtype, device=dev)
+    if tuple(out.shape) != (total, N_MELS):
+        raise ValueError(f"out must be [{total}, {N_MELS}]")
+    st = _stream_handle(stream, dev)
+    fo2 = np.zeros(s.n_streams + 1, dtype=np.int64)
+    ptr = _dev_ptr(out, out_dtype, "out") if out.numel() else None
+    _check(_stream_flush(s.handle, ptr, st_out, _ptr64(fo2), st), "logmel_stream_flush")
+    return out, fo2
 
 
 def logmel_stream_destroy(s: Stream):

@@ -58,6 +58,110 @@ struct logmel_plan {
   int resident_waves = 0;    // wavefronts of the transform kernel resident at once: one per SIMD
 };
 
+// ---------------------------------------------------------------------------
+// Resampling to 16 kHz: a Kaiser-windowed sinc (the reading and its
+// parameters are stated in logmel.h).
+// ---------------------------------------------------------------------------
+
+namespace {
+
+constexpr int kResZeros = LOGMEL_RESAMPLE_ZEROS;
+constexpr double kResRolloff = 0.96;
+constexpr double kResBeta = 9.0;
+constexpr int32_t kResMinRate = 1000;
+constexpr int32_t kResMaxRate = 384000;
+
+int64_t gcd64(int64_t a, int64_t b) {
+  while (b) {
+    const int64_t t = a % b;
+    a = b;
+    b = t;
+  }
+  return a;
+}
+
+// Modified Bessel function of the first kind, order 0, by its power series
+// sum_k ((x / 2)^k / k!)^2 (all terms positive; converges for any x).
+double bessel_i0(double x) {
+  const double h = 0.5 * x;
+  double term = 1.0, sum = 1.0;
+  for (int k = 1; k < 500; ++k) {
+    term *= (h / k) * (h / k);
+    sum += term;
+    if (term < 1e-17 * sum) break;
+  }
+  return sum;
+}
+
+struct ResGeometry {
+  int64_t L, M;   // 16000 / R = L / M in lowest terms
+  int J;          // taps j = 0 .. 2J cover input samples q - J .. q + J
+  int Tp;         // 2J + 1 rounded up to a multiple of 16 (table row length)
+  double fc, H;   // cutoff (Hz) and half-width (input samples)
+  int G;          // periods of L outputs per block, in groups of 64
+};
+
+ResGeometry res_geometry(int32_t rate) {
+  ResGeometry g;
+  const int64_t d = gcd64(rate, 16000);
+  g.L = 16000 / d;
+  g.M = rate / d;
+  g.fc = kResRolloff * (rate < 16000 ? rate : 16000) / 2.0;
+  g.H = kResZeros * (double)rate / (2.0 * g.fc);
+  g.J = rate == 16000 ? 0 : (int)std::ceil(g.H);
+  g.Tp = (2 * g.J + 1 + 15) / 16 * 16;
+  // A block of 64 G periods needs about 64 G M + Tp staged samples; at
+  // most 1024 (period group, phase) items per block.
+  const int64_t room = kResLdsFloats - g.Tp - 64;
+  int64_t G = room / (64 * g.M);
+  const int64_t item_cap = 1024 / g.L > 1 ? 1024 / g.L : 1;
+  if (G > item_cap) G = item_cap;
+  g.G = (int)(G < 1 ? 0 : G);
+  return g;
+}
+
+// Taps table [L][Tp]: row phi, tap j < 2J + 1 is h(phi / L + J - j); the
+// row's last Tp - 2J - 1 entries are zero.
+std::vector<float> res_taps(int32_t rate, const ResGeometry& g) {
+  const int T = 2 * g.J + 1;
+  std::vector<float> t((size_t)(g.L * g.Tp), 0.0f);
+  if (rate == 16000) {   // no resampling: the output is the input
+    t[0] = 1.0f;
+    return t;
+  }
+  const double i0b = bessel_i0(kResBeta);
+  const double pi = 3.14159265358979323846;
+  for (int64_t phi = 0; phi < g.L; ++phi) {
+    for (int j = 0; j < T; ++j) {
+      const double dd = ((double)phi / (double)g.L + g.J) - j;   // p - k, input samples
+      const double r = dd / g.H;
+      double h = 0.0;
+      if (std::fabs(r) < 1.0) {
+        const double u = 2.0 * g.fc * dd / rate;
+        const double sinc = u == 0.0 ? 1.0 : std::sin(pi * u) / (pi * u);
+        h = (2.0 * g.fc / rate) * sinc * bessel_i0(kResBeta * std::sqrt(1.0 - r * r)) / i0b;
+      }
+      t[(size_t)(phi * g.Tp + j)] = (float)h;
+    }
+  }
+  return t;
+}
+
+// Largest taps table accepted (floats, device memory).
+constexpr int64_t kResMaxTableFloats = int64_t(1) << 24;
+
+bool res_rate_ok(int32_t rate) { return rate >= kResMinRate && rate <= kResMaxRate; }
+
+}  // namespace
+
+struct logmel_resampler {
+  const logmel_plan* plan;
+  int32_t rate;
+  ResGeometry geo;
+  int grid;
+  float* taps = nullptr;   // device [L][2J + 1]
+};
+
 struct logmel_stream {
   const logmel_plan* plan;
   int64_t n;
@@ -72,7 +176,45 @@ struct logmel_stream {
   int slot = 0;
   // host shadow, per stream
   std::vector<int64_t> seen, emitted, carry_len, carry_src;
+
+  // Streams at another input rate: each push is resampled to 16 kHz first,
+  // and the 16 kHz samples go through the part above. Per stream, the input
+  // samples the next outputs' windows still need (at most 2J) are kept as a
+  // carry, in one of two packed input buffers that alternate from push to
+  // push.
+  int32_t in_rate = 16000;
+  logmel_resampler* rs = nullptr;
+  int64_t in_max_push = 0;              // input samples per push and stream
+  int64_t in_stride = 0;                // a stream's room in an input buffer
+  float* in_buf[2] = {nullptr, nullptr};
+  int in_cur = 0;                       // the buffer holding the carries
+  float* res_buf = nullptr;             // one push's 16 kHz samples, packed
+  int64_t* rmeta_dev = nullptr;         // [9n + 1], layout in rs_push
+  int64_t* rmeta_host[kSlots] = {nullptr, nullptr, nullptr, nullptr};
+  hipEvent_t rslot_done[kSlots] = {nullptr, nullptr, nullptr, nullptr};
+  int rslot = 0;
+  std::vector<int64_t> rs_in, rs_out, rcarry_len, rcarry_src;
 };
+
+namespace {
+
+// Outputs of a clip whose whole window lies in its first n_in samples:
+// the n with floor(n M / L) + J <= n_in - 1.
+int64_t res_final(const ResGeometry& g, int64_t n_in) {
+  const int64_t x = n_in - g.J;   // floor(n M / L) < x
+  return x >= 1 ? ((x * g.L - 1) / g.M) + 1 : 0;
+}
+
+// 16 kHz outputs a push of p samples (or, with flush, the end of the stream)
+// completes for stream j.
+int64_t res_new_outputs(const logmel_stream* s, int64_t j, int64_t p, bool flush) {
+  const int64_t n_in = s->rs_in[j] + p;
+  const int64_t end = flush ? (n_in * 16000 + s->in_rate - 1) / s->in_rate
+                            : res_final(s->rs->geo, n_in);
+  return end - s->rs_out[j];
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -335,7 +477,77 @@ void logmel_stream_destroy(logmel_stream* s) {
   }
   if (s->ws) (void)hipFree(s->ws);
   if (s->meta_dev) (void)hipFree(s->meta_dev);
+  for (int i = 0; i < logmel_stream::kSlots; ++i) {
+    if (s->rslot_done[i]) {
+      (void)hipEventSynchronize(s->rslot_done[i]);
+      (void)hipEventDestroy(s->rslot_done[i]);
+    }
+    if (s->rmeta_host[i]) (void)hipHostFree(s->rmeta_host[i]);
+  }
+  for (int i = 0; i < 2; ++i)
+    if (s->in_buf[i]) (void)hipFree(s->in_buf[i]);
+  if (s->res_buf) (void)hipFree(s->res_buf);
+  if (s->rmeta_dev) (void)hipFree(s->rmeta_dev);
+  if (s->rs) logmel_resampler_destroy(s->rs);
   delete s;
+}
+
+int logmel_stream_create_ex(const logmel_plan* plan, int64_t n_streams, int64_t max_push,
+                            int32_t in_rate, logmel_stream** out) {
+  if (in_rate == 16000) return logmel_stream_create(plan, n_streams, max_push, out);
+  if (!plan || !out || n_streams < 1 || max_push < 1) return LOGMEL_ERR_INVALID_ARGUMENT;
+  *out = nullptr;
+  logmel_resampler* r = nullptr;
+  int e = logmel_resampler_create(plan, in_rate, &r);
+  if (e != LOGMEL_OK) return e;
+  const ResGeometry& geo = r->geo;
+  // 16 kHz samples one push can complete: those of its new input, one more
+  // for rounding, and at the end of the stream those of the retained 2J.
+  if (max_push > (INT64_MAX / 16) / geo.L) {
+    logmel_resampler_destroy(r);
+    return LOGMEL_ERR_INPUT_TOO_LONG;
+  }
+  const int64_t by_push = (max_push * geo.L + geo.M - 1) / geo.M + 2;
+  const int64_t by_end = ((2 * geo.J + 2) * geo.L + geo.M - 1) / geo.M + 2;
+  const int64_t max16 = by_push > by_end ? by_push : by_end;
+  logmel_stream* s = nullptr;
+  e = logmel_stream_create(plan, n_streams, max16, &s);
+  if (e != LOGMEL_OK) {
+    logmel_resampler_destroy(r);
+    return e;
+  }
+  s->in_rate = in_rate;
+  s->rs = r;
+  s->in_max_push = max_push;
+  s->in_stride = 2 * (int64_t)geo.J + 2 + max_push;
+  if (s->in_stride > INT64_MAX / n_streams / 4) {
+    logmel_stream_destroy(s);
+    return LOGMEL_ERR_INPUT_TOO_LONG;
+  }
+  DeviceGuard g(plan->cfg.device);
+  if (!g.ok) {
+    logmel_stream_destroy(s);
+    return LOGMEL_ERR_DEVICE;
+  }
+  const size_t rmeta_words = 9 * (size_t)n_streams + 1;
+  bool ok = true;
+  for (int i = 0; ok && i < 2; ++i)
+    ok = hipMalloc(&s->in_buf[i], (size_t)n_streams * s->in_stride * sizeof(float)) == hipSuccess;
+  ok = ok && hipMalloc(&s->res_buf, (size_t)n_streams * max16 * sizeof(float)) == hipSuccess &&
+       hipMalloc(&s->rmeta_dev, rmeta_words * 8) == hipSuccess;
+  for (int i = 0; ok && i < logmel_stream::kSlots; ++i)
+    ok = hipHostMalloc(&s->rmeta_host[i], rmeta_words * 8, hipHostMallocDefault) == hipSuccess &&
+         hipEventCreateWithFlags(&s->rslot_done[i], hipEventDisableTiming) == hipSuccess;
+  if (!ok) {
+    logmel_stream_destroy(s);
+    return LOGMEL_ERR_OUT_OF_MEMORY;
+  }
+  s->rs_in.assign(n_streams, 0);
+  s->rs_out.assign(n_streams, 0);
+  s->rcarry_len.assign(n_streams, 0);
+  s->rcarry_src.assign(n_streams, 0);
+  *out = s;
+  return LOGMEL_OK;
 }
 
 int logmel_stream_reset(logmel_stream* s) {
@@ -346,6 +558,12 @@ int logmel_stream_reset(logmel_stream* s) {
     s->carry_len[j] = 0;
     s->carry_src[j] = j * s->stride + kRing;
   }
+  for (size_t j = 0; j < s->rs_in.size(); ++j) {
+    s->rs_in[j] = 0;
+    s->rs_out[j] = 0;
+    s->rcarry_len[j] = 0;
+    s->rcarry_src[j] = 0;
+  }
   return LOGMEL_OK;
 }
 
@@ -355,7 +573,18 @@ int logmel_stream_frames_for_push(const logmel_stream* s, const int64_t* push_le
   fo[0] = 0;
   for (int64_t j = 0; j < s->n; ++j) {
     if (push_len[j] < 0) return LOGMEL_ERR_INVALID_ARGUMENT;
-    fo[j + 1] = fo[j] + frames_of(s->carry_len[j] + push_len[j]);
+    const int64_t p = s->rs ? res_new_outputs(s, j, push_len[j], false) : push_len[j];
+    fo[j + 1] = fo[j] + frames_of(s->carry_len[j] + p);
+  }
+  return LOGMEL_OK;
+}
+
+int logmel_stream_frames_for_flush(const logmel_stream* s, int64_t* fo) {
+  if (!s || !fo) return LOGMEL_ERR_INVALID_ARGUMENT;
+  fo[0] = 0;
+  for (int64_t j = 0; j < s->n; ++j) {
+    const int64_t p = s->rs ? res_new_outputs(s, j, 0, true) : 0;
+    fo[j + 1] = fo[j] + (s->rs ? frames_of(s->carry_len[j] + p) : 0);
   }
   return LOGMEL_OK;
 }
@@ -366,24 +595,13 @@ int logmel_stream_push(logmel_stream* s, const float* d_new, const int64_t* push
                                hip_stream);
 }
 
-int logmel_stream_push_ex(logmel_stream* s, const void* d_new, int sample_type,
-                          const int64_t* push_len, void* d_out, int out_type, int64_t* fo_out,
-                          void* hip_stream) {
-  if (!s || !push_len) return LOGMEL_ERR_INVALID_ARGUMENT;
-  if (sample_type != LOGMEL_F32 && sample_type != LOGMEL_I16) return LOGMEL_ERR_UNSUPPORTED;
-  if (out_type != LOGMEL_F32 && out_type != LOGMEL_F16) return LOGMEL_ERR_UNSUPPORTED;
-  const int64_t n = s->n;
-  int64_t total_new = 0;
-  for (int64_t j = 0; j < n; ++j) {
-    if (push_len[j] < 0) return LOGMEL_ERR_INVALID_ARGUMENT;
-    if (push_len[j] > s->max_push) return LOGMEL_ERR_INPUT_TOO_LONG;
-    total_new += push_len[j];
-  }
-  if (total_new > 0 && !d_new) return LOGMEL_ERR_INVALID_ARGUMENT;
-  DeviceGuard g(s->plan->cfg.device);
-  if (!g.ok) return LOGMEL_ERR_DEVICE;
-  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+namespace {
 
+// The 16 kHz part of a push: push_len[j] <= max_push new samples per stream
+// (checked by the caller), the device on.
+int lm_push(logmel_stream* s, const void* d_new, int sample_type, const int64_t* push_len,
+            void* d_out, int out_type, int64_t* fo_out, hipStream_t st) {
+  const int64_t n = s->n;
   // Fill the next staging slot once the push that last used it has gone up.
   const int slot = s->slot;
   if (hipEventSynchronize(s->slot_done[slot]) != hipSuccess) return LOGMEL_ERR_DEVICE;
@@ -434,9 +652,125 @@ int logmel_stream_push_ex(logmel_stream* s, const void* d_new, int sample_type,
   return LOGMEL_OK;
 }
 
+// The resampling part of a push (or, with flush, of the end of the
+// streams): builds each stream's segment (carry, then the new samples) in
+// the other input buffer, resamples every output the segment completes, and
+// passes those 16 kHz samples to lm_push. Meta layout (int64, n streams):
+//   [0n) carry index in the carry buffer   [1n) carry length
+//   [2n) offset of the new samples in d_new [3n) number of new samples
+//   [4n) segment start in the new buffer    [5n) buffer index of the clip's sample 0
+//   [6n) segment end                        [7n) number of the first output
+//   [8n, 9n + 1) output offsets
+int rs_push(logmel_stream* s, const void* d_new, int sample_type, const int64_t* push_len,
+            void* d_out, int out_type, int64_t* fo_out, hipStream_t st, bool flush) {
+  const int64_t n = s->n;
+  const ResGeometry& geo = s->rs->geo;
+  const int slot = s->rslot;
+  if (hipEventSynchronize(s->rslot_done[slot]) != hipSuccess) return LOGMEL_ERR_DEVICE;
+  int64_t* m = s->rmeta_host[slot];
+  std::vector<int64_t> k(n);
+  int64_t seg = 0, noff = 0;
+  m[8 * n] = 0;
+  for (int64_t j = 0; j < n; ++j) {
+    const int64_t c = s->rcarry_len[j];
+    const int64_t p = flush ? 0 : push_len[j];
+    m[j] = s->rcarry_src[j];
+    m[n + j] = c;
+    m[2 * n + j] = noff;
+    m[3 * n + j] = p;
+    m[4 * n + j] = seg;
+    m[5 * n + j] = seg - (s->rs_in[j] - c);
+    m[6 * n + j] = seg + c + p;
+    m[7 * n + j] = s->rs_out[j];
+    k[j] = res_new_outputs(s, j, p, flush);
+    if (k[j] < 0 || k[j] > s->max_push) return LOGMEL_ERR_INVALID_ARGUMENT;   // not reached
+    m[8 * n + j + 1] = m[8 * n + j] + k[j];
+    seg += c + p;
+    noff += p;
+  }
+  const int64_t total_k = m[9 * n];
+  const size_t meta_bytes = (9 * (size_t)n + 1) * 8;
+  if (hipMemcpyAsync(s->rmeta_dev, m, meta_bytes, hipMemcpyHostToDevice, st) != hipSuccess ||
+      hipEventRecord(s->rslot_done[slot], st) != hipSuccess)
+    return LOGMEL_ERR_DEVICE;
+  s->rslot = (slot + 1) % logmel_stream::kSlots;
+  float* src = s->in_buf[s->in_cur];
+  float* dst = s->in_buf[1 - s->in_cur];
+  if (logmel_launch_rstream_prep(dst, src, flush ? nullptr : d_new, sample_type == LOGMEL_I16,
+                                 s->rmeta_dev, n, st) != hipSuccess)
+    return LOGMEL_ERR_DEVICE;
+  if (total_k > 0 &&
+      logmel_launch_resample(dst, 0, s->rmeta_dev + 5 * n, s->rmeta_dev + 6 * n,
+                             s->rmeta_dev + 7 * n, s->rmeta_dev + 8 * n, n, total_k, s->res_buf,
+                             s->rs->taps, (int)geo.L, (int)geo.M, geo.J, geo.Tp, geo.G,
+                             s->rs->grid, st) != hipSuccess)
+    return LOGMEL_ERR_DEVICE;
+  const int r = lm_push(s, s->res_buf, LOGMEL_F32, k.data(), d_out, out_type, fo_out, st);
+  if (r != LOGMEL_OK) return r;
+  // Advance the host shadow: keep the input from the first window the next
+  // outputs need.
+  for (int64_t j = 0; j < n; ++j) {
+    const int64_t c = s->rcarry_len[j];
+    const int64_t p = flush ? 0 : push_len[j];
+    const int64_t n_in = s->rs_in[j] + p;
+    const int64_t n_out = s->rs_out[j] + k[j];
+    int64_t a = (n_out * geo.M) / geo.L - geo.J;        // first sample still needed
+    const int64_t kept = s->rs_in[j] - c;                // first sample in the segment
+    if (a < kept) a = kept;
+    if (a > n_in) a = n_in;
+    s->rcarry_src[j] = m[4 * n + j] + (a - kept);
+    s->rcarry_len[j] = n_in - a;
+    s->rs_in[j] = n_in;
+    s->rs_out[j] = n_out;
+  }
+  s->in_cur = 1 - s->in_cur;
+  return LOGMEL_OK;
+}
+
+}  // namespace
+
+int logmel_stream_push_ex(logmel_stream* s, const void* d_new, int sample_type,
+                          const int64_t* push_len, void* d_out, int out_type, int64_t* fo_out,
+                          void* hip_stream) {
+  if (!s || !push_len) return LOGMEL_ERR_INVALID_ARGUMENT;
+  if (sample_type != LOGMEL_F32 && sample_type != LOGMEL_I16) return LOGMEL_ERR_UNSUPPORTED;
+  if (out_type != LOGMEL_F32 && out_type != LOGMEL_F16) return LOGMEL_ERR_UNSUPPORTED;
+  const int64_t n = s->n;
+  const int64_t limit = s->rs ? s->in_max_push : s->max_push;
+  int64_t total_new = 0;
+  for (int64_t j = 0; j < n; ++j) {
+    if (push_len[j] < 0) return LOGMEL_ERR_INVALID_ARGUMENT;
+    if (push_len[j] > limit) return LOGMEL_ERR_INPUT_TOO_LONG;
+    total_new += push_len[j];
+  }
+  if (total_new > 0 && !d_new) return LOGMEL_ERR_INVALID_ARGUMENT;
+  DeviceGuard g(s->plan->cfg.device);
+  if (!g.ok) return LOGMEL_ERR_DEVICE;
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  if (s->rs) return rs_push(s, d_new, sample_type, push_len, d_out, out_type, fo_out, st, false);
+  return lm_push(s, d_new, sample_type, push_len, d_out, out_type, fo_out, st);
+}
+
+int logmel_stream_flush(logmel_stream* s, void* d_out, int out_type, int64_t* fo_out,
+                        void* hip_stream) {
+  if (!s) return LOGMEL_ERR_INVALID_ARGUMENT;
+  if (out_type != LOGMEL_F32 && out_type != LOGMEL_F16) return LOGMEL_ERR_UNSUPPORTED;
+  int r = LOGMEL_OK;
+  if (s->rs) {
+    DeviceGuard g(s->plan->cfg.device);
+    if (!g.ok) return LOGMEL_ERR_DEVICE;
+    r = rs_push(s, nullptr, LOGMEL_F32, nullptr, d_out, out_type, fo_out,
+                static_cast<hipStream_t>(hip_stream), true);
+  } else if (fo_out) {
+    for (int64_t j = 0; j <= s->n; ++j) fo_out[j] = 0;   // partial frames are dropped
+  }
+  if (r != LOGMEL_OK) return r;
+  return logmel_stream_reset(s);
+}
+
 int logmel_stream_counters(const logmel_stream* s, int64_t j, int64_t* seen, int64_t* emitted) {
   if (!s || j < 0 || j >= s->n) return LOGMEL_ERR_INVALID_ARGUMENT;
-  if (seen) *seen = s->seen[j];
+  if (seen) *seen = s->rs ? s->rs_in[j] : s->seen[j];
   if (emitted) *emitted = s->emitted[j];
   return LOGMEL_OK;
 }
@@ -444,11 +778,12 @@ int logmel_stream_counters(const logmel_stream* s, int64_t j, int64_t* seen, int
 static constexpr int64_t kStateWords = 3 * 2 + kRing;  // 3 int64 + 400 fp32, in 4-byte words
 
 int64_t logmel_stream_state_bytes(const logmel_stream* s) {
-  return s ? s->n * kStateWords * 4 : 0;
+  return (s && !s->rs) ? s->n * kStateWords * 4 : 0;
 }
 
 int logmel_stream_get_state(logmel_stream* s, void* state_host, void* hip_stream) {
   if (!s || !state_host) return LOGMEL_ERR_INVALID_ARGUMENT;
+  if (s->rs) return LOGMEL_ERR_UNSUPPORTED;
   DeviceGuard g(s->plan->cfg.device);
   if (!g.ok) return LOGMEL_ERR_DEVICE;
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
@@ -468,6 +803,7 @@ int logmel_stream_get_state(logmel_stream* s, void* state_host, void* hip_stream
 
 int logmel_stream_set_state(logmel_stream* s, const void* state_host, void* hip_stream) {
   if (!s || !state_host) return LOGMEL_ERR_INVALID_ARGUMENT;
+  if (s->rs) return LOGMEL_ERR_UNSUPPORTED;
   const char* b = static_cast<const char*>(state_host);
   for (int64_t j = 0; j < s->n; ++j) {
     int64_t hdr[3];
@@ -500,110 +836,6 @@ int logmel_stream_set_state(logmel_stream* s, const void* state_host, void* hip_
 }
 
 }  // extern "C"
-
-// ---------------------------------------------------------------------------
-// Resampling to 16 kHz: a Kaiser-windowed sinc (the reading and its
-// parameters are stated in logmel.h).
-// ---------------------------------------------------------------------------
-
-namespace {
-
-constexpr int kResZeros = LOGMEL_RESAMPLE_ZEROS;
-constexpr double kResRolloff = 0.96;
-constexpr double kResBeta = 9.0;
-constexpr int32_t kResMinRate = 1000;
-constexpr int32_t kResMaxRate = 384000;
-
-int64_t gcd64(int64_t a, int64_t b) {
-  while (b) {
-    const int64_t t = a % b;
-    a = b;
-    b = t;
-  }
-  return a;
-}
-
-// Modified Bessel function of the first kind, order 0, by its power series
-// sum_k ((x / 2)^k / k!)^2 (all terms positive; converges for any x).
-double bessel_i0(double x) {
-  const double h = 0.5 * x;
-  double term = 1.0, sum = 1.0;
-  for (int k = 1; k < 500; ++k) {
-    term *= (h / k) * (h / k);
-    sum += term;
-    if (term < 1e-17 * sum) break;
-  }
-  return sum;
-}
-
-struct ResGeometry {
-  int64_t L, M;   // 16000 / R = L / M in lowest terms
-  int J;          // taps j = 0 .. 2J cover input samples q - J .. q + J
-  int Tp;         // 2J + 1 rounded up to a multiple of 16 (table row length)
-  double fc, H;   // cutoff (Hz) and half-width (input samples)
-  int G;          // periods of L outputs per block, in groups of 64
-};
-
-ResGeometry res_geometry(int32_t rate) {
-  ResGeometry g;
-  const int64_t d = gcd64(rate, 16000);
-  g.L = 16000 / d;
-  g.M = rate / d;
-  g.fc = kResRolloff * (rate < 16000 ? rate : 16000) / 2.0;
-  g.H = kResZeros * (double)rate / (2.0 * g.fc);
-  g.J = rate == 16000 ? 0 : (int)std::ceil(g.H);
-  g.Tp = (2 * g.J + 1 + 15) / 16 * 16;
-  // A block of 64 G periods needs about 64 G M + Tp staged samples; at
-  // most 1024 (period group, phase) items per block.
-  const int64_t room = kResLdsFloats - g.Tp - 64;
-  int64_t G = room / (64 * g.M);
-  const int64_t item_cap = 1024 / g.L > 1 ? 1024 / g.L : 1;
-  if (G > item_cap) G = item_cap;
-  g.G = (int)(G < 1 ? 0 : G);
-  return g;
-}
-
-// Taps table [L][Tp]: row phi, tap j < 2J + 1 is h(phi / L + J - j); the
-// row's last Tp - 2J - 1 entries are zero.
-std::vector<float> res_taps(int32_t rate, const ResGeometry& g) {
-  const int T = 2 * g.J + 1;
-  std::vector<float> t((size_t)(g.L * g.Tp), 0.0f);
-  if (rate == 16000) {   // no resampling: the output is the input
-    t[0] = 1.0f;
-    return t;
-  }
-  const double i0b = bessel_i0(kResBeta);
-  const double pi = 3.14159265358979323846;
-  for (int64_t phi = 0; phi < g.L; ++phi) {
-    for (int j = 0; j < T; ++j) {
-      const double dd = ((double)phi / (double)g.L + g.J) - j;   // p - k, input samples
-      const double r = dd / g.H;
-      double h = 0.0;
-      if (std::fabs(r) < 1.0) {
-        const double u = 2.0 * g.fc * dd / rate;
-        const double sinc = u == 0.0 ? 1.0 : std::sin(pi * u) / (pi * u);
-        h = (2.0 * g.fc / rate) * sinc * bessel_i0(kResBeta * std::sqrt(1.0 - r * r)) / i0b;
-      }
-      t[(size_t)(phi * g.Tp + j)] = (float)h;
-    }
-  }
-  return t;
-}
-
-// Largest taps table accepted (floats, device memory).
-constexpr int64_t kResMaxTableFloats = int64_t(1) << 24;
-
-bool res_rate_ok(int32_t rate) { return rate >= kResMinRate && rate <= kResMaxRate; }
-
-}  // namespace
-
-struct logmel_resampler {
-  const logmel_plan* plan;
-  int32_t rate;
-  ResGeometry geo;
-  int grid;
-  float* taps = nullptr;   // device [L][2J + 1]
-};
 
 extern "C" {
 
@@ -702,7 +934,8 @@ int logmel_resample(const logmel_resampler* r, const void* d_samples, int sample
       return LOGMEL_ERR_INVALID_ARGUMENT;
   }
   if (logmel_launch_resample(d_samples, sample_type == LOGMEL_I16, d_sample_offsets,
-                             d_out_offsets, n_clips, total_out, d_out, r->taps, (int)r->geo.L,
+                             d_sample_offsets + 1, nullptr, d_out_offsets, n_clips, total_out,
+                             d_out, r->taps, (int)r->geo.L,
                              (int)r->geo.M, r->geo.J, r->geo.Tp, r->geo.G, r->grid, st) !=
       hipSuccess)
     return LOGMEL_ERR_DEVICE;

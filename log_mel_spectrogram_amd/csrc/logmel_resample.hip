@@ -60,22 +60,36 @@ __device__ __forceinline__ int64_t div_by(int64_t a, int L, double inv_L) {
   return q;
 }
 
-// A lane's current clip: its index, output range [o_lo, o_hi) and sample
-// range [lo, hi). A lane's successive outputs usually stay in one clip, so
-// the clip is looked up again only when an output leaves it.
-struct ResClip {
-  int64_t c, o_lo, o_hi, lo, hi;
+// Segment c of the batch: its samples lie at [lo[c], hi[c]) of x, sample 0
+// of its clip at lo[c] (zero before lo and from hi on), and its outputs,
+// [out_off[c], out_off[c + 1]) of y, are the clip's outputs nfirst[c],
+// nfirst[c] + 1, ... (nfirst null: from 0). An offline batch passes its
+// sample offsets as lo (and, shifted by one, as hi); a stream passes the
+// segment of each stream's retained and new samples.
+struct ResSegs {
+  const int64_t* __restrict__ lo;
+  const int64_t* __restrict__ hi;
+  const int64_t* __restrict__ nfirst;
+  const int64_t* __restrict__ out_off;
+  int64_t n;
 };
 
-__device__ __forceinline__ ResClip res_clip(int64_t g, const int64_t* __restrict__ in_off,
-                                            const int64_t* __restrict__ out_off,
-                                            int64_t n_clips) {
+// A lane's current segment: its index, output range [o_lo, o_hi), first
+// output number nf and sample range [lo, hi). A lane's successive outputs
+// usually stay in one segment, so it is looked up again only when an output
+// leaves it.
+struct ResClip {
+  int64_t c, o_lo, o_hi, nf, lo, hi;
+};
+
+__device__ __forceinline__ ResClip res_clip(int64_t g, const ResSegs& sg) {
   ResClip r;
-  r.c = last_le(out_off, n_clips, g);
-  r.o_lo = out_off[r.c];
-  r.o_hi = out_off[r.c + 1];
-  r.lo = in_off[r.c];
-  r.hi = in_off[r.c + 1];
+  r.c = last_le(sg.out_off, sg.n, g);
+  r.o_lo = sg.out_off[r.c];
+  r.o_hi = sg.out_off[r.c + 1];
+  r.nf = sg.nfirst ? sg.nfirst[r.c] : 0;
+  r.lo = sg.lo[r.c];
+  r.hi = sg.hi[r.c];
   return r;
 }
 
@@ -92,7 +106,7 @@ __device__ __forceinline__ ResSrc res_pos(int64_t g, const ResClip& cl, int L, i
   s.c = cl.c;
   s.lo = cl.lo;
   s.hi = cl.hi;
-  const int64_t nm = (g - cl.o_lo) * M;
+  const int64_t nm = (cl.nf + g - cl.o_lo) * M;
   const int64_t q = div_by(nm, L, inv_L);
   s.phi = (int)(nm - q * L);
   s.k0 = cl.lo + q - J;
@@ -117,16 +131,18 @@ __device__ __forceinline__ int64_t wave_last_le(const int64_t* __restrict__ a, i
   return c0;
 }
 
-__device__ __forceinline__ int64_t wave_k0(int64_t g, const int64_t* __restrict__ in_off,
-                                           const int64_t* __restrict__ out_off, int64_t n_clips,
-                                           int L, int M, int J, double inv_L, int lane) {
-  const int64_t c = wave_last_le(out_off, n_clips, g, lane);
-  const int64_t nm = (g - out_off[c]) * M;
-  return in_off[c] + div_by(nm, L, inv_L) - J;
+__device__ __forceinline__ int64_t wave_k0(int64_t g, const ResSegs& sg, int L, int M, int J,
+                                           double inv_L, int lane) {
+  const int64_t c = wave_last_le(sg.out_off, sg.n, g, lane);
+  const int64_t nm = ((sg.nfirst ? sg.nfirst[c] : 0) + g - sg.out_off[c]) * M;
+  return sg.lo[c] + div_by(nm, L, inv_L) - J;
 }
 
 // One output alone, with its own row of taps; samples outside [lo, hi) are
 // zero; from the staged span when it holds the window, else from memory.
+// The sums run in the order of the shared-tap loop (odd taps of whole
+// 16-tap chunks in a second sum), so a whole window gives the same bits on
+// either path.
 template <typename In>
 __device__ __forceinline__ float res_one(const ResSrc& s, const float* __restrict__ taps, int Tp,
                                          int T, const float* span, int64_t s0, int span_len,
@@ -134,14 +150,16 @@ __device__ __forceinline__ float res_one(const ResSrc& s, const float* __restric
   const float* tp = taps + (int64_t)s.phi * Tp;
   const int jlo = (int)max((int64_t)0, s.lo - s.k0);
   const int jhi = (int)min((int64_t)T, s.hi - s.k0);
+  const int whole = (T / kResChunk) * kResChunk;
   const int64_t off = s.k0 - s0;
-  float a = 0.0f;
-  if (off + jlo >= 0 && off + jhi <= span_len) {
-    for (int j = jlo; j < jhi; ++j) a = __builtin_fmaf(tp[j], span[off + j], a);
-  } else {
-    for (int j = jlo; j < jhi; ++j) a = __builtin_fmaf(tp[j], res_sample(x, s.k0 + j), a);
+  const bool staged = off + jlo >= 0 && off + jhi <= span_len;
+  float a0 = 0.0f, a1 = 0.0f;
+  for (int j = jlo; j < jhi; ++j) {
+    const float v = staged ? span[off + j] : res_sample(x, s.k0 + j);
+    if (j < whole && (j & 1)) a1 = __builtin_fmaf(tp[j], v, a1);
+    else a0 = __builtin_fmaf(tp[j], v, a0);
   }
-  return a;
+  return a0 + a1;
 }
 
 // 16 taps (scalar registers) and 16 samples (vector registers) of a chunk.
@@ -178,9 +196,7 @@ __device__ __forceinline__ void res_fma(const ResChunk& c, float& a0, float& a1)
 
 template <typename In>
 __device__ __forceinline__ void resample_body(const In* __restrict__ x,
-                                              const int64_t* __restrict__ in_off,
-                                              const int64_t* __restrict__ out_off,
-                                              int64_t n_clips, int64_t total_out,
+                                              const ResSegs sg, int64_t total_out,
                                               float* __restrict__ y,
                                               const float* __restrict__ taps, int L, int M, int J,
                                               int Tp, int G, float* span, int64_t* bounds) {
@@ -190,7 +206,7 @@ __device__ __forceinline__ void resample_body(const In* __restrict__ x,
   const int n_waves = blockDim.x >> 6;
   const int T = 2 * J + 1;
   const double inv_L = 1.0 / L;
-  const int64_t total_in = in_off[n_clips];
+  const int64_t total_in = sg.hi[sg.n - 1];   // the last segment ends the buffer
   const int64_t per_block = (int64_t)64 * G * L;
   const int items = G * L;
 
@@ -201,8 +217,8 @@ __device__ __forceinline__ void resample_body(const In* __restrict__ x,
     const int64_t g_last = min(g0 + per_block, total_out) - 1;
     __syncthreads();                          // the previous block's span is consumed
     if (wave == 0) {
-      const int64_t k_first = wave_k0(g0, in_off, out_off, n_clips, L, M, J, inv_L, lane);
-      const int64_t k_last = wave_k0(g_last, in_off, out_off, n_clips, L, M, J, inv_L, lane);
+      const int64_t k_first = wave_k0(g0, sg, L, M, J, inv_L, lane);
+      const int64_t k_last = wave_k0(g_last, sg, L, M, J, inv_L, lane);
       if (lane == 0) {
         bounds[0] = k_first;
         bounds[1] = k_last + Tp;
@@ -217,7 +233,7 @@ __device__ __forceinline__ void resample_body(const In* __restrict__ x,
     }
     __syncthreads();
 
-    ResClip cl{-1, 0, -1, 0, 0};
+    ResClip cl{-1, 0, -1, 0, 0, 0};
     // items it = wave, wave + n_waves, ... as (period group gi, phase r)
     // with it = gi L + r, stepped without a division
     int gi = wave / L, r = wave - (wave / L) * L;
@@ -237,7 +253,7 @@ __device__ __forceinline__ void resample_body(const In* __restrict__ x,
       bool ok = false;
       int64_t off = 0;
       if (active) {
-        if (!(cl.o_lo <= g && g < cl.o_hi)) cl = res_clip(g, in_off, out_off, n_clips);
+        if (!(cl.o_lo <= g && g < cl.o_hi)) cl = res_clip(g, sg);
         s = res_pos(g, cl, L, M, J, inv_L);
         off = s.k0 - s0;
         ok = s.k0 >= s.lo && s.k0 + T <= s.hi && off >= 0 && off + Tp <= span_len;
@@ -296,14 +312,15 @@ __device__ __forceinline__ void resample_body(const In* __restrict__ x,
 
 #define LOGMEL_RESAMPLE_KERNEL(NAME, IN)                                                         \
   extern "C" __global__ void __launch_bounds__(1024)                                             \
-  NAME(const IN* __restrict__ x, const int64_t* __restrict__ in_off,                             \
-       const int64_t* __restrict__ out_off, int64_t n_clips, int64_t total_out,                   \
+  NAME(const IN* __restrict__ x, const int64_t* __restrict__ seg_lo,                            \
+       const int64_t* __restrict__ seg_hi, const int64_t* __restrict__ nfirst,                  \
+       const int64_t* __restrict__ out_off, int64_t n_segs, int64_t total_out,                  \
        float* __restrict__ y, const float* __restrict__ taps, int L, int M, int J, int Tp,       \
        int G) {                                                                                  \
     __shared__ float span[kResLdsFloats];                                                        \
     __shared__ int64_t bounds[2];                                                                \
-    resample_body<IN>(x, in_off, out_off, n_clips, total_out, y, taps, L, M, J, Tp, G, span,     \
-                      bounds);                                                                   \
+    const ResSegs sg{seg_lo, seg_hi, nfirst, out_off, n_segs};                                   \
+    resample_body<IN>(x, sg, total_out, y, taps, L, M, J, Tp, G, span, bounds);                 \
   }
 
 LOGMEL_RESAMPLE_KERNEL(logmel_resample_kernel, float)
@@ -311,21 +328,22 @@ LOGMEL_RESAMPLE_KERNEL(logmel_resample_i16_kernel, int16_t)
 
 }  // namespace logmel
 
-hipError_t logmel_launch_resample(const void* x, int in_i16, const int64_t* in_off,
-                                  const int64_t* out_off, int64_t n_clips, int64_t total_out,
+hipError_t logmel_launch_resample(const void* x, int in_i16, const int64_t* seg_lo,
+                                  const int64_t* seg_hi, const int64_t* nfirst,
+                                  const int64_t* out_off, int64_t n_segs, int64_t total_out,
                                   float* y, const float* taps, int L, int M, int J, int Tp, int G,
                                   int grid, hipStream_t stream) {
-  if (total_out <= 0) return hipSuccess;
+  if (total_out <= 0 || n_segs <= 0) return hipSuccess;
   const int64_t per_block = (int64_t)64 * G * L;
   const int64_t blocks = (total_out + per_block - 1) / per_block;
   const int g = (int)(blocks < grid ? blocks : grid);
   if (in_i16)
     hipLaunchKernelGGL(logmel::logmel_resample_i16_kernel, dim3(g), dim3(1024), 0, stream,
-                       static_cast<const int16_t*>(x), in_off, out_off, n_clips, total_out, y,
-                       taps, L, M, J, Tp, G);
+                       static_cast<const int16_t*>(x), seg_lo, seg_hi, nfirst, out_off, n_segs,
+                       total_out, y, taps, L, M, J, Tp, G);
   else
     hipLaunchKernelGGL(logmel::logmel_resample_kernel, dim3(g), dim3(1024), 0, stream,
-                       static_cast<const float*>(x), in_off, out_off, n_clips, total_out, y,
-                       taps, L, M, J, Tp, G);
+                       static_cast<const float*>(x), seg_lo, seg_hi, nfirst, out_off, n_segs,
+                       total_out, y, taps, L, M, J, Tp, G);
   return hipGetLastError();
 }

@@ -7,11 +7,24 @@
 // (one 1024-thread workgroup per compute unit).
 static constexpr int kResLdsFloats = 38400;   // 150 KB of the 160 KB
 
-// Clip i's samples [in_off[i], in_off[i + 1]) of x (fp32, or int16 PCM with
-// in_i16) give outputs [out_off[i], out_off[i + 1]) of y; taps is the device
-// table [L][Tp] (rows of 2J + 1 taps zero-padded to Tp, a multiple of 16);
-// blocks of 64 G periods of L outputs; grid: workgroups resident at once.
-hipError_t logmel_launch_resample(const void* x, int in_i16, const int64_t* in_off,
-                                  const int64_t* out_off, int64_t n_clips, int64_t total_out,
+// Segment i's samples are [seg_lo[i], seg_hi[i]) of x (fp32, or int16 PCM
+// with in_i16), its clip's sample 0 at seg_lo[i]; its outputs
+// [out_off[i], out_off[i + 1]) of y are the clip's outputs nfirst[i],
+// nfirst[i] + 1, ... (nfirst null: from 0). The last segment ends x. An
+// offline batch passes its sample offsets as seg_lo and, one further, as
+// seg_hi. taps is the device table [L][Tp] (rows of 2J + 1 taps zero-padded
+// to Tp, a multiple of 16); blocks of 64 G periods of L outputs; grid:
+// workgroups resident at once.
+hipError_t logmel_launch_resample(const void* x, int in_i16, const int64_t* seg_lo,
+                                  const int64_t* seg_hi, const int64_t* nfirst,
+                                  const int64_t* out_off, int64_t n_segs, int64_t total_out,
                                   float* y, const float* taps, int L, int M, int J, int Tp, int G,
                                   int grid, hipStream_t stream);
+
+// A resampling stream's push, step 1: segment j of dst = src[carry index,
+// + carry length) followed by the new samples of stream j (fp32, or int16
+// PCM with in_i16; fresh may be null when there are none); meta as in the
+// host's rs_push.
+hipError_t logmel_launch_rstream_prep(float* dst, const float* src, const void* fresh, int in_i16,
+                                      const int64_t* meta, int64_t n_streams,
+                                      hipStream_t stream);

@@ -1,4 +1,7 @@
-// The streaming push, step 1 (gfx950): moves each stream's carry (the
+// The streaming push, step 1 (gfx950), and the same for streams that are
+// resampled to 16 kHz first (logmel_rstream_prep_kernel, below).
+//
+// logmel_stream_prep_kernel moves each stream's carry (the
 // samples of its next, not yet complete frame) to sit right before the new
 // samples in the stream's workspace row, and appends the new samples
 // (fp32, or int16 PCM converted to s / 32768, exact). The frames are then
@@ -8,6 +11,7 @@
 #include <stdint.h>
 
 #include "logmel_launch.h"
+#include "logmel_resample_launch.h"
 
 namespace logmel {
 
@@ -63,7 +67,58 @@ logmel_stream_prep_i16_kernel(float* __restrict__ ws, int64_t row_stride,
   stream_prep_body(ws, row_stride, fresh, meta, n_streams);
 }
 
+// A resampling stream's push, step 1: one workgroup per stream builds its
+// segment in dst: the retained input samples (from the previous push's
+// buffer src), then the new ones (fp32, or int16 PCM as s / 32768). Meta
+// layout as in the host's rs_push: [0n) carry index in src, [1n) carry
+// length, [2n) offset of the new samples, [3n) their number, [4n) segment
+// start in dst.
+template <typename In>
+__device__ __forceinline__ void rstream_prep_body(float* __restrict__ dst,
+                                                  const float* __restrict__ src,
+                                                  const In* __restrict__ fresh,
+                                                  const int64_t* __restrict__ meta,
+                                                  int64_t n_streams) {
+  const int64_t j = blockIdx.x;
+  const int t = threadIdx.x;
+  const int64_t csrc = meta[j];
+  const int64_t clen = meta[n_streams + j];
+  const int64_t noff = meta[2 * n_streams + j];
+  const int64_t nlen = meta[3 * n_streams + j];
+  float* seg = dst + meta[4 * n_streams + j];
+  for (int64_t i = t; i < clen; i += 256) seg[i] = src[csrc + i];
+  for (int64_t i = t; i < nlen; i += 256) seg[clen + i] = stream_sample(fresh + noff, i);
+}
+
+extern "C" __global__ void __launch_bounds__(256)
+logmel_rstream_prep_kernel(float* __restrict__ dst, const float* __restrict__ src,
+                           const float* __restrict__ fresh, const int64_t* __restrict__ meta,
+                           int64_t n_streams) {
+  rstream_prep_body(dst, src, fresh, meta, n_streams);
+}
+
+extern "C" __global__ void __launch_bounds__(256)
+logmel_rstream_prep_i16_kernel(float* __restrict__ dst, const float* __restrict__ src,
+                               const int16_t* __restrict__ fresh,
+                               const int64_t* __restrict__ meta, int64_t n_streams) {
+  rstream_prep_body(dst, src, fresh, meta, n_streams);
+}
+
 }  // namespace logmel
+
+hipError_t logmel_launch_rstream_prep(float* dst, const float* src, const void* fresh, int in_i16,
+                                      const int64_t* meta, int64_t n_streams,
+                                      hipStream_t stream) {
+  if (n_streams <= 0) return hipSuccess;
+  if (in_i16)
+    hipLaunchKernelGGL(logmel::logmel_rstream_prep_i16_kernel, dim3((unsigned)n_streams),
+                       dim3(256), 0, stream, dst, src, static_cast<const int16_t*>(fresh), meta,
+                       n_streams);
+  else
+    hipLaunchKernelGGL(logmel::logmel_rstream_prep_kernel, dim3((unsigned)n_streams), dim3(256),
+                       0, stream, dst, src, static_cast<const float*>(fresh), meta, n_streams);
+  return hipGetLastError();
+}
 
 hipError_t logmel_launch_stream_prep(float* ws, int64_t row_stride, const void* fresh, int in_i16,
                                      const int64_t* meta, int64_t n_streams,

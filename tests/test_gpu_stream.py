@@ -259,3 +259,88 @@ def test_stream_push_ex_rejects_types(env):
     assert lm._stream_push_ex(s.handle, None, lm.LOGMEL_F32, lm._ptr64(pl), None, 9, None,
                               None) == lm.LOGMEL_ERR_UNSUPPORTED
     s.close()
+
+
+def resampled_streams_case(env, rate, n, seconds, seed, in_dtype="f32", out_dtype="f32"):
+    """Streams at `rate`: ragged pushes around 80 ms, then a flush; each
+    stream's frames equal, bit for bit, logmel_resample of the whole input
+    followed by logmel_compute."""
+    lm, plan, torch = env
+    dev = torch.device("cuda", 0)
+    rng = np.random.default_rng(seed)
+    lens = [int(rng.integers(int(0.2 * rate), int(seconds * rate))) for _ in range(n)]
+    lens[0] = 0
+    lens[1] = 37
+    clips = [S.speech_like(900 + j, max(L, 1), "cuda", fs=rate)[:L] for j, L in enumerate(lens)]
+    if in_dtype == "i16":
+        clips = [torch.clamp(torch.round(c * 32768.0), -32768, 32767).to(torch.int16) for c in clips]
+    odt = torch.float16 if out_dtype == "f16" else torch.float32
+    so = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    packed = torch.cat(clips).contiguous() if sum(lens) else torch.zeros(0, device=dev)
+    r = lm.logmel_resampler_create(plan, rate)
+    y, oo = lm.resample(r, packed, so)
+    fo = lm.logmel_frame_offsets(oo)
+    ref = lm.logmel_compute_ex(plan, y, torch.from_numpy(oo).to(dev), torch.from_numpy(fo).to(dev),
+                               int(fo[-1]), out_dtype=odt)
+    push = rate * 80 // 1000
+    s = lm.logmel_stream_create(plan, n, push + push // 2, in_rate=rate)
+    got = [[] for _ in range(n)]
+    pos = np.zeros(n, dtype=np.int64)
+    k = 0
+    while (pos < np.array(lens)).any():
+        pl = np.full(n, push) if k % 3 else rng.integers(0, push + push // 2 + 1, n)
+        pl = np.minimum(pl, np.array(lens) - pos)
+        new = torch.cat([clips[j][pos[j]:pos[j] + pl[j]] for j in range(n)]).contiguous()
+        fo_pred = lm.logmel_stream_frames_for_push(s, pl)
+        out, f = lm.logmel_stream_push(s, new, pl, out_dtype=odt)
+        assert np.array_equal(f, fo_pred)
+        for j in range(n):
+            if f[j + 1] > f[j]:
+                got[j].append(out[f[j]:f[j + 1]])
+        pos += pl
+        k += 1
+    out, f = lm.logmel_stream_flush(s, out_dtype=odt)
+    for j in range(n):
+        if f[j + 1] > f[j]:
+            got[j].append(out[f[j]:f[j + 1]])
+    torch.cuda.synchronize()
+    for j in range(n):
+        g = torch.cat(got[j]) if got[j] else torch.zeros((0, 128), dtype=odt, device=dev)
+        assert g.shape[0] == fo[j + 1] - fo[j], (rate, j, g.shape[0], fo[j + 1] - fo[j])
+        assert torch.equal(g, ref[fo[j]:fo[j + 1]]), (rate, j)
+    # after the flush the streams start again from nothing
+    assert lm.logmel_stream_counters(s, 2) == (0, 0)
+    s.close()
+    return k
+
+
+@pytest.mark.parametrize("rate", [48000, 44100, 8000, 22050])
+def test_resampling_streams_equal_offline(env, rate):
+    say(f"resampling streams at {rate} Hz")
+    pushes = resampled_streams_case(env, rate, 10, 3.0, rate)
+    say(f"{rate} Hz: {pushes} pushes and a flush equal offline")
+
+
+def test_resampling_streams_int16_fp16(env):
+    say("resampling streams at 48 kHz, int16 in, fp16 out")
+    resampled_streams_case(env, 48000, 6, 2.0, 5, in_dtype="i16", out_dtype="f16")
+
+
+def test_resampling_stream_limits(env):
+    lm, plan, torch = env
+    s = lm.logmel_stream_create(plan, 2, 1000, in_rate=48000)
+    assert lm.logmel_stream_state_bytes(s) == 0
+    with pytest.raises(lm.LogmelError) as e:
+        lm.logmel_stream_push(s, torch.zeros(2002, device="cuda"), [1001, 1001])
+    assert e.value.status == lm.LOGMEL_ERR_INPUT_TOO_LONG
+    assert lm._stream_get_state(s.handle, lm._p(1), None) == lm.LOGMEL_ERR_UNSUPPORTED
+    s.close()
+    with pytest.raises(lm.LogmelError):
+        lm.logmel_stream_create(plan, 2, 1000, in_rate=44101)
+    # a 16 kHz stream's flush emits nothing and resets it
+    s = lm.logmel_stream_create(plan, 3, 1280)
+    lm.logmel_stream_push(s, torch.zeros(3 * 1000, device="cuda"), [1000] * 3)
+    out, f = lm.logmel_stream_flush(s)
+    assert out.shape[0] == 0 and list(f) == [0, 0, 0, 0]
+    assert lm.logmel_stream_counters(s, 0) == (0, 0)
+    s.close()
