@@ -7,8 +7,9 @@
 //   The flattened frame space [0, total_frames) is cut into tiles of 32
 //   consecutive frames, one frame per lane pair (role 0: even samples, role
 //   1: odd samples; see logmel_frame.h). A persistent grid of one wavefront
-//   per SIMD walks the tiles; a wavefront locates and loads its next tile
-//   while it finishes the current one. A tile may straddle clips: each pair
+//   per SIMD walks the tiles, each wavefront a contiguous run of them; a
+//   wavefront locates and loads its next tile while it finishes the current
+//   one. A tile may straddle clips: each pair
 //   finds its clip from the int64 frame offsets. A tile inside one clip reads
 //   its 5360-sample span once, coalesced, and shares it through LDS; a tile
 //   across clips stages the spans of its clips' runs of frames in LDS the
@@ -85,16 +86,40 @@ struct RowMap {
   int64_t unit;
 };
 
+// The clip that holds a tile's first frame, kept in wave-uniform registers:
+// its frames [lo, hi) of the flattened frame space, its samples' range and
+// its output row base. A following tile whose 32 frames all lie in [lo, hi)
+// is located from these alone, with no memory access.
+struct ClipCache {
+  int64_t lo, hi, ss, se, rb;
+};
+
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t h = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)h << 32) | l);
+}
+
 __device__ __forceinline__ TileSrc locate_tile(int64_t tile, int lane,
                                                const int64_t* __restrict__ seg_start,
                                                const int64_t* __restrict__ seg_end,
                                                const int64_t* __restrict__ frame_off,
                                                RowMap rows, int64_t n_clips,
-                                               int64_t total_frames) {
+                                               int64_t total_frames, ClipCache& cc) {
   TileSrc t;
   const int64_t g0 = tile * kTile;
   t.g = g0 + (lane >> 1);
   t.in_range = t.g < total_frames;
+  if (cc.lo <= g0 && g0 + kTile <= cc.hi && g0 + kTile <= total_frames) {
+    // all 32 frames in the cached clip (so all inside the batch)
+    const int64_t f = t.g - cc.lo;
+    t.s = cc.ss + 160 * f;
+    t.row = cc.rb * rows.unit + f;
+    t.valid = t.s + 400 <= cc.se;
+    t.s0 = cc.ss + 160 * (g0 - cc.lo);
+    t.fast = t.s0 + 160 * (kTile - 1) + 400 <= cc.se;
+    return t;
+  }
   const int64_t gq = t.in_range ? t.g : total_frames - 1;   // lookup key for idle lanes
 
   // Clip of the tile's first frame (wave-uniform): the last c with
@@ -147,6 +172,12 @@ __device__ __forceinline__ TileSrc locate_tile(int64_t tile, int lane,
   const int64_t f = gq - fo_c;
   t.s = ss_c + 160 * f;
   t.row = rb_c * rows.unit + f;
+  // lane 0's clip is the first frame's: cache it (hi from the next boundary)
+  cc.lo = uniform64(fo_c);
+  cc.hi = uniform64(c == c0 ? B : fo_c);
+  cc.ss = uniform64(ss_c);
+  cc.se = uniform64(se_c);
+  cc.rb = uniform64(rb_c);
   // A frame is only computed if all its 400 samples lie inside its clip.
   t.valid = t.in_range && f >= 0 && (t.s + 400 <= se_c);
   t.fast = __all(t.valid && c == __shfl(c, 0));
@@ -433,14 +464,19 @@ __device__ __forceinline__ void tiles_body(const In* __restrict__ samples,
   const int fl = lane >> 1;
   const int64_t n_tiles = (total_frames + kTile - 1) / kTile;
 
-  // Each wavefront takes tiles blockIdx.x, + gridDim.x, ... While it computes
-  // one tile it locates the next and loads that tile's span into registers
+  // Wavefront w takes a contiguous run of tiles (the first n_tiles % grid
+  // wavefronts one more), so that consecutive tiles usually share a clip and
+  // are located from the cached clip without a lookup. While it computes one
+  // tile it locates the next and loads that tile's span into registers
   // (between the transform and the filterbank, where the fewest registers
   // are live), so the loads' latency hides behind the filterbank and the log.
-  int64_t tile = blockIdx.x;
-  if (tile >= n_tiles) return;
+  const int64_t per = n_tiles / gridDim.x, extra = n_tiles % gridDim.x;
+  int64_t tile = blockIdx.x * per + min((int64_t)blockIdx.x, extra);
+  const int64_t tile_end = tile + per + ((int64_t)blockIdx.x < extra ? 1 : 0);
+  if (tile >= tile_end) return;
+  ClipCache cc{0, 0, 0, 0, 0};
   TileSrc cur = locate_tile(tile, lane, seg_start, seg_end, frame_off, rows, n_clips,
-                            total_frames);
+                            total_frames, cc);
   if (role == 0) row_lds[0][fl] = cur.row;
   typename SpanOf<In>::type span;
   if (cur.fast) load_span(samples, cur.s0, lane, span);
@@ -505,11 +541,12 @@ __device__ __forceinline__ void tiles_body(const In* __restrict__ samples,
     float P[101];
     pair_power(v, tables + kTabWindow, tables + kTabRot800, role ? -1.0 : 1.0, P);
 
-    const int64_t next = tile + gridDim.x;
-    const bool more = next < n_tiles;
+    const int64_t next = tile + 1;
+    const bool more = next < tile_end;
     TileSrc nxt = cur;
     if (more) {
-      nxt = locate_tile(next, lane, seg_start, seg_end, frame_off, rows, n_clips, total_frames);
+      nxt = locate_tile(next, lane, seg_start, seg_end, frame_off, rows, n_clips, total_frames,
+                        cc);
       if (role == 0) row_lds[(it + 1) & 1][fl] = nxt.row;
     }
     // Loaded on every path (from the plan's zero pad when there is no span
