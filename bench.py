@@ -113,6 +113,18 @@ def cpu_baseline(clips, seconds):
         t0 = time.perf_counter()
         pool.map(_oracle_worker, [(c, reps) for c in clips])
         dt = time.perf_counter() - t0
+    # one core, in this process, for about 2 s
+    from oracle import logmel_clip
+    done, k = 0.0, 0
+    t1 = time.perf_counter()
+    while True:
+        c = clips[k % len(clips)]
+        logmel_clip(c)
+        done += c.size / FS
+        k += 1
+        if time.perf_counter() - t1 > 2.0:
+            break
+    dt1 = time.perf_counter() - t1
     return {
         "value": audio_per_pass * reps / dt,
         "unit": "audio-seconds/s",
@@ -120,7 +132,42 @@ def cpu_baseline(clips, seconds):
         "kind": "oracle",
         "sample": f"{len(clips)} clips of the workload ({audio_per_pass:.0f} audio-s), "
                   f"{reps} passes, {dt:.1f} s wall",
+        "one_core_value": done / dt1,
+        "one_core_sample": f"{k} clips, {dt1:.1f} s",
+        "cpu_model": _cpu_model(),
     }
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def copy_bandwidth(torch, dev, nbytes=1 << 30, reps=5):
+    """Device-to-device copy of nbytes (read + write) timed with HIP events:
+    the bandwidth a plain streaming kernel reaches on this GPU, in GB/s."""
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1.0)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) / 1e3)
+    del a, b
+    torch.cuda.empty_cache()
+    return 2 * nbytes / sorted(ts)[len(ts) // 2] / 1e9
 
 
 # ---------------------------------------------------------------- workloads
@@ -213,6 +260,10 @@ def bench_offline(args, lm, plan, torch):
     wall = time.perf_counter() - t0
     kern_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     kern_avg_s = sum(kern_ms) / len(kern_ms) / 1e3
+    kern_sorted = sorted(kern_ms)
+    kern_med_s = kern_sorted[len(kern_sorted) // 2] / 1e3
+    kern_min_s = kern_sorted[0] / 1e3
+    copy_gbs = copy_bandwidth(torch, dev) if args.workload != "p3" else None
     algo_bytes = set_bytes + 8 * 2 * (len(so))
     ms_per_step = wall / args.steps * 1e3
     audio_s = n_samples / FS
@@ -248,10 +299,16 @@ def bench_offline(args, lm, plan, torch):
                                    (0, 1): "logmel_tiles_f16out_kernel",
                                    (1, 1): "logmel_tiles_i16_f16out_kernel"}[(in_i16, out_f16)]),
                      "kernel_avg_us": kern_avg_s * 1e6,
+                     "kernel_median_us": kern_med_s * 1e6,
+                     "kernel_min_us": kern_min_s * 1e6,
                      "algorithmic_flops_per_launch": FLOPS_PER_FRAME * total,
                      "algorithmic_bytes_per_launch": algo_bytes,
                      "hbm_achieved_gbs": achieved_gbs,
-                     "hbm_frac": achieved_gbs / HBM_PEAK_GBS},
+                     "hbm_frac": achieved_gbs / HBM_PEAK_GBS,
+                     # a 1 GiB device-to-device copy in the same run: what a
+                     # plain streaming kernel reaches here
+                     "copy_gbs": copy_gbs,
+                     "hbm_frac_of_copy": achieved_gbs / copy_gbs if copy_gbs else None},
     }
     clips_host = None
     if not args.no_cpu_baseline:

@@ -98,7 +98,11 @@ struct ResGeometry {
   int J;          // taps j = 0 .. 2J cover input samples q - J .. q + J
   int Tp;         // 2J + 1 rounded up to a multiple of 16 (table row length)
   double fc, H;   // cutoff (Hz) and half-width (input samples)
-  int G;          // periods of L outputs per block, in groups of 64
+  int G;          // lane groups of 64 per block
+  int NB;         // consecutive outputs per lane on the shared path: 4, 3, 2 or 1
+  int Q;          // outputs between neighbouring lanes' first outputs: L, or NB when L divides NB
+  int TpX;        // row length of the shared path's table: the largest union of NB windows,
+                  // rounded up to a multiple of 16
 };
 
 ResGeometry res_geometry(int32_t rate) {
@@ -110,11 +114,24 @@ ResGeometry res_geometry(int32_t rate) {
   g.H = kResZeros * (double)rate / (2.0 * g.fc);
   g.J = rate == 16000 ? 0 : (int)std::ceil(g.H);
   g.Tp = (2 * g.J + 1 + 15) / 16 * 16;
-  // A block of 64 G periods needs about 64 G M + Tp staged samples; at
-  // most 1024 (period group, phase) items per block.
-  const int64_t room = kResLdsFloats - g.Tp - 64;
-  int64_t G = room / (64 * g.M);
-  const int64_t item_cap = 1024 / g.L > 1 ? 1024 / g.L : 1;
+  // (16 kHz input is the identity: one output per lane, each reading only its own sample)
+  // (integer ratios with M odd: 3, so that the lanes' windows, 3 M apart,
+  // fall on different LDS banks)
+  g.NB = g.J == 0                             ? 1
+         : (g.L == 1 && g.M % 2 == 1)         ? 3
+         : (g.L % 4 == 0 || 4 % g.L == 0)     ? 4
+         : (g.L % 2 == 0)                     ? 2
+                                              : 1;
+  g.Q = g.L % g.NB == 0 ? (int)g.L : g.NB;
+  // first phase phi's union of NB windows: 2J + 1 + floor((phi + (NB - 1) M) / L)
+  const int64_t d_max = (g.L - 1 + (int64_t)(g.NB - 1) * g.M) / g.L;
+  g.TpX = (int)((2 * g.J + 1 + d_max + 15) / 16 * 16);
+  // A block of 64 G lanes needs about 64 G Q M / L + TpX staged samples; at
+  // most 1024 (lane group, output block) items per block.
+  const int64_t room = kResLdsFloats - g.TpX - 64;
+  int64_t G = room / (64 * (g.Q * g.M / g.L));
+  const int64_t per_group = g.Q / g.NB;
+  const int64_t item_cap = 1024 / per_group > 1 ? 1024 / per_group : 1;
   if (G > item_cap) G = item_cap;
   g.G = (int)(G < 1 ? 0 : G);
   return g;
@@ -147,6 +164,23 @@ std::vector<float> res_taps(int32_t rate, const ResGeometry& g) {
   return t;
 }
 
+// The shared path's table [L][TpX][NB]: for first phase phi, entry [s][a] is
+// the tap of output a after it (phase (phi + a M) mod L) for the union's
+// sample s, i.e. that output's row shifted right by its window's offset
+// floor((phi + a M) / L); zeros elsewhere.
+std::vector<float> res_taps_blk(const ResGeometry& g, const std::vector<float>& t) {
+  const int T = 2 * g.J + 1;
+  std::vector<float> b((size_t)(g.L * g.NB * g.TpX), 0.0f);
+  for (int64_t phi = 0; phi < g.L; ++phi)
+    for (int a = 0; a < g.NB; ++a) {
+      const int64_t pa = (phi + a * g.M) % g.L;
+      const int64_t d = (phi + a * g.M) / g.L;
+      for (int j = 0; j < T; ++j)
+        b[(size_t)((phi * g.TpX + d + j) * g.NB + a)] = t[(size_t)(pa * g.Tp + j)];
+    }
+  return b;
+}
+
 // Largest taps table accepted (floats, device memory).
 constexpr int64_t kResMaxTableFloats = int64_t(1) << 24;
 
@@ -159,7 +193,8 @@ struct logmel_resampler {
   int32_t rate;
   ResGeometry geo;
   int grid;
-  float* taps = nullptr;   // device [L][2J + 1]
+  float* taps = nullptr;       // device [L][Tp], then the shared path's [L][TpX][NB]
+  float* taps_blk = nullptr;   // inside the taps allocation
 };
 
 struct logmel_stream {
@@ -702,8 +737,8 @@ int rs_push(logmel_stream* s, const void* d_new, int sample_type, const int64_t*
   if (total_k > 0 &&
       logmel_launch_resample(dst, 0, s->rmeta_dev + 5 * n, s->rmeta_dev + 6 * n,
                              s->rmeta_dev + 7 * n, s->rmeta_dev + 8 * n, n, total_k, s->res_buf,
-                             s->rs->taps, (int)geo.L, (int)geo.M, geo.J, geo.Tp, geo.G,
-                             s->rs->grid, st) != hipSuccess)
+                             s->rs->taps, s->rs->taps_blk, (int)geo.L, (int)geo.M, geo.J, geo.Tp,
+                             geo.TpX, geo.NB, geo.Q, geo.G, s->rs->grid, st) != hipSuccess)
     return LOGMEL_ERR_DEVICE;
   const int r = lm_push(s, s->res_buf, LOGMEL_F32, k.data(), d_out, out_type, fo_out, st);
   if (r != LOGMEL_OK) return r;
@@ -866,9 +901,12 @@ int logmel_resampler_create(const logmel_plan* plan, int32_t in_rate, logmel_res
   *out = nullptr;
   if (!res_rate_ok(in_rate)) return LOGMEL_ERR_UNSUPPORTED;
   const ResGeometry geo = res_geometry(in_rate);
-  if (geo.G < 1 || geo.L * geo.Tp > kResMaxTableFloats)
-    return LOGMEL_ERR_UNSUPPORTED;   // 64 input periods beyond LDS, or too many phases
-  const std::vector<float> taps = res_taps(in_rate, geo);
+  if (geo.G < 1 || geo.L * (geo.Tp + geo.NB * geo.TpX) > kResMaxTableFloats)
+    return LOGMEL_ERR_UNSUPPORTED;   // 64 lanes' inputs beyond LDS, or too many phases
+  std::vector<float> taps = res_taps(in_rate, geo);
+  const std::vector<float> blk = res_taps_blk(geo, taps);
+  const size_t plain = taps.size();
+  taps.insert(taps.end(), blk.begin(), blk.end());
   logmel_resampler* r = new (std::nothrow) logmel_resampler;
   if (!r) return LOGMEL_ERR_OUT_OF_MEMORY;
   r->plan = plan;
@@ -890,6 +928,7 @@ int logmel_resampler_create(const logmel_plan* plan, int32_t in_rate, logmel_res
     delete r;
     return LOGMEL_ERR_DEVICE;
   }
+  r->taps_blk = r->taps + plain;
   *out = r;
   return LOGMEL_OK;
 }
@@ -935,8 +974,8 @@ int logmel_resample(const logmel_resampler* r, const void* d_samples, int sample
   }
   if (logmel_launch_resample(d_samples, sample_type == LOGMEL_I16, d_sample_offsets,
                              d_sample_offsets + 1, nullptr, d_out_offsets, n_clips, total_out,
-                             d_out, r->taps, (int)r->geo.L,
-                             (int)r->geo.M, r->geo.J, r->geo.Tp, r->geo.G, r->grid, st) !=
+                             d_out, r->taps, r->taps_blk, (int)r->geo.L, (int)r->geo.M, r->geo.J,
+                             r->geo.Tp, r->geo.TpX, r->geo.NB, r->geo.Q, r->geo.G, r->grid, st) !=
       hipSuccess)
     return LOGMEL_ERR_DEVICE;
   return LOGMEL_OK;

@@ -8,23 +8,31 @@
 // logmel_api.cpp.
 //
 // logmel_resample_kernel: a persistent grid of one 1024-thread workgroup per
-// compute unit. The outputs of the packed batch are cut into blocks of
-// 64 G periods of L outputs each (a period's outputs have the L different
-// phases; inside one clip, output r of every period has the same phase). A
-// workgroup stages the input samples a block's windows cover in LDS (one
-// coalesced pass; int16 PCM is converted to s / 32768 on the way), then its
-// 16 wavefronts take the block's (period group, phase) items in turn: lane l
-// of a wavefront forms output r of period 64 g + l. All lanes of an item
-// share their taps, which the wavefront reads with scalar loads straight
-// into scalar registers; each lane's window starts M samples after its left
-// neighbour's, so with M odd the 64 lanes' LDS reads of one tap fall on 64
-// different banks. Per multiply-add: one LDS read.
+// compute unit. Each lane forms NB consecutive outputs (NB = 4 for every
+// common rate but the integer ratios with M odd, 48 kHz among them, where it
+// is 3), reading each sample of their windows' union from LDS once and
+// multiplying it into the NB sums. Lane l of item (gi, b) takes outputs
+// g0 + (64 gi + l) Q + NB b + a, a < NB, where Q = L when NB divides L (a
+// lane's outputs are NB of one period's L) and Q = NB when L divides NB
+// (integer ratios: a lane's outputs are NB / L whole periods); either way
+// all lanes of an item inside one clip have the same first phase, hence the
+// same NB tap rows and the same window offsets. The outputs of the packed
+// batch are cut into blocks of 64 G lanes; a workgroup stages the input
+// samples a block's windows cover in LDS (coalesced, sixteen loads in flight
+// per thread; int16 PCM converted to s / 32768 on the way), then its 16
+// wavefronts take the block's items in turn. The taps of an item come from
+// the shared path's table, NB rows per first phase, each shifted right by
+// its window's offset and zero elsewhere, read with scalar loads into scalar
+// registers; lanes' windows start Q M / L samples apart, so when that is odd
+// the 64 lanes' LDS reads of one sample fall on 64 different banks.
+// Per NB multiply-adds: one LDS read.
 // Clips are packed back to back, so a block's windows cover one contiguous
-// range of the batch even when the block spans clips. A lane whose window
-// crosses its clip's edge or lies beyond the staged span (blocks of many
-// tiny clips) forms its output alone, masked to its clip, with its own row
-// of taps; lanes of one item in different clips (different phases) take one
-// pass of the shared-tap loop per phase.
+// range of the batch even when the block spans clips. A lane whose NB
+// outputs are not all in one clip, or whose windows' union crosses its
+// clip's edge or lies beyond the staged span (blocks of many tiny clips),
+// forms each output alone, masked to its clip, with its own row of taps;
+// lanes of one item in different clips (different first phases) take one
+// pass of the shared loop per phase.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -32,7 +40,6 @@
 
 namespace logmel {
 
-static constexpr int kResChunk = 16;   // taps per unrolled step
 
 __device__ __forceinline__ float res_sample(const float* p, int64_t k) { return p[k]; }
 __device__ __forceinline__ float res_sample(const int16_t* p, int64_t k) {
@@ -138,11 +145,12 @@ __device__ __forceinline__ int64_t wave_k0(int64_t g, const ResSegs& sg, int L, 
   return sg.lo[c] + div_by(nm, L, inv_L) - J;
 }
 
-// One output alone, with its own row of taps; samples outside [lo, hi) are
-// zero; from the staged span when it holds the window, else from memory.
-// The sums run in the order of the shared-tap loop (odd taps of whole
-// 16-tap chunks in a second sum), so a whole window gives the same bits on
-// either path.
+// One output alone, with its own row of taps: the plain sum, in tap order,
+// of the window's samples inside [lo, hi) times their taps; from the staged
+// span when it holds the window, else from memory. The shared path below
+// adds the same products in the same order (plus products with zero taps,
+// which leave every nonzero sum unchanged), so an output gets the same
+// value on either path.
 template <typename In>
 __device__ __forceinline__ float res_one(const ResSrc& s, const float* __restrict__ taps, int Tp,
                                          int T, const float* span, int64_t s0, int span_len,
@@ -150,56 +158,87 @@ __device__ __forceinline__ float res_one(const ResSrc& s, const float* __restric
   const float* tp = taps + (int64_t)s.phi * Tp;
   const int jlo = (int)max((int64_t)0, s.lo - s.k0);
   const int jhi = (int)min((int64_t)T, s.hi - s.k0);
-  const int whole = (T / kResChunk) * kResChunk;
   const int64_t off = s.k0 - s0;
   const bool staged = off + jlo >= 0 && off + jhi <= span_len;
-  float a0 = 0.0f, a1 = 0.0f;
+  float a = 0.0f;
   for (int j = jlo; j < jhi; ++j) {
     const float v = staged ? span[off + j] : res_sample(x, s.k0 + j);
-    if (j < whole && (j & 1)) a1 = __builtin_fmaf(tp[j], v, a1);
-    else a0 = __builtin_fmaf(tp[j], v, a0);
+    a = __builtin_fmaf(tp[j], v, a);
   }
-  return a0 + a1;
+  return a;
 }
 
-// 16 taps (scalar registers) and 16 samples (vector registers) of a chunk.
-struct ResChunk {
-  float t[kResChunk];
-  float v[kResChunk];
+// A chunk of CH samples (vector registers) and, for each of the NB outputs,
+// CH taps (scalar registers).
+// 16 bytes at a 4-byte aligned address (global memory allows this).
+struct __attribute__((packed, aligned(4))) f4u {
+  float x, y, z, w;
 };
 
+template <int NB, int CH>
+struct ResChunk {
+  float t[NB][CH];
+  float v[CH];
+};
+
+// The chunk's NB x CH taps are consecutive in the table (sample-major), one
+// or two scalar loads.
+template <int NB, int CH>
 __device__ __forceinline__ void res_load(const __attribute__((address_space(4))) float* trow,
-                                         const float* sp, int ch, ResChunk& c) {
+                                         const float* sp, int ch, ResChunk<NB, CH>& c) {
 #pragma unroll
-  for (int j = 0; j < kResChunk; ++j) {
-    c.t[j] = trow[ch * kResChunk + j];
-    c.v[j] = sp[ch * kResChunk + j];
-  }
+  for (int j = 0; j < CH; ++j) c.v[j] = sp[ch * CH + j];
+#pragma unroll
+  for (int j = 0; j < CH; ++j)
+#pragma unroll
+    for (int a = 0; a < NB; ++a) c.t[a][j] = trow[(ch * CH + j) * NB + a];
 }
 
 // Ties every value of a chunk to this point, so that its loads are all
 // issued before and waited here, in one wait.
-__device__ __forceinline__ void res_wait(ResChunk& c) {
+template <int NB, int CH>
+__device__ __forceinline__ void res_wait(ResChunk<NB, CH>& c) {
 #pragma unroll
-  for (int j = 0; j < kResChunk; j += 4)
-    asm volatile("" : "+s"(c.t[j]), "+s"(c.t[j + 1]), "+s"(c.t[j + 2]), "+s"(c.t[j + 3]),
-                      "+v"(c.v[j]), "+v"(c.v[j + 1]), "+v"(c.v[j + 2]), "+v"(c.v[j + 3]));
+  for (int j = 0; j < CH; ++j) asm volatile("" : "+v"(c.v[j]));
+#pragma unroll
+  for (int a = 0; a < NB; ++a)
+#pragma unroll
+    for (int j = 0; j < CH; ++j) asm volatile("" : "+s"(c.t[a][j]));
 }
 
-__device__ __forceinline__ void res_fma(const ResChunk& c, float& a0, float& a1) {
+template <int NB, int CH>
+__device__ __forceinline__ void res_fma(const ResChunk<NB, CH>& c, float (&acc)[NB]) {
 #pragma unroll
-  for (int j = 0; j < kResChunk; j += 2) {
-    a0 = __builtin_fmaf(c.t[j], c.v[j], a0);
-    a1 = __builtin_fmaf(c.t[j + 1], c.v[j + 1], a1);
-  }
+  for (int j = 0; j < CH; ++j)
+#pragma unroll
+    for (int a = 0; a < NB; ++a) acc[a] = __builtin_fmaf(c.t[a][j], c.v[j], acc[a]);
 }
 
-template <typename In>
+// Output g's clip and source (its segment looked up again only when g leaves
+// the cached one).
+__device__ __forceinline__ ResSrc res_at(int64_t g, ResClip& cl, const ResSegs& sg, int L, int M,
+                                         int J, double inv_L) {
+  if (!(cl.o_lo <= g && g < cl.o_hi)) cl = res_clip(g, sg);
+  return res_pos(g, cl, L, M, J, inv_L);
+}
+
+// NB consecutive outputs per lane. Lane l of item (gi, b) forms outputs
+// g0 + (64 gi + l) Q + NB b + a, a < NB (Q = L when NB divides L, else NB,
+// which L divides), so all lanes of an item in one clip have the same first
+// phase phi, and their outputs' windows start at offsets
+// d_a = floor((phi + a M) / L) from the first's: the union of the NB windows
+// is U = 2J + 1 + d_{NB-1} samples. taps_blk holds, for every first phase,
+// TpX groups of NB taps: group s, tap a is output a's tap for the union's
+// sample s (output a's row shifted right by d_a, zeros elsewhere), so each
+// staged sample is read once and multiplied into the NB sums.
+template <int NB, int CH, typename In>
 __device__ __forceinline__ void resample_body(const In* __restrict__ x,
                                               const ResSegs sg, int64_t total_out,
                                               float* __restrict__ y,
-                                              const float* __restrict__ taps, int L, int M, int J,
-                                              int Tp, int G, float* span, int64_t* bounds) {
+                                              const float* __restrict__ taps,
+                                              const float* __restrict__ taps_blk, int L, int M,
+                                              int J, int Tp, int TpX, int Ur, int Q, int G,
+                                              float* span, int64_t* bounds) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -207,13 +246,14 @@ __device__ __forceinline__ void resample_body(const In* __restrict__ x,
   const int T = 2 * J + 1;
   const double inv_L = 1.0 / L;
   const int64_t total_in = sg.hi[sg.n - 1];   // the last segment ends the buffer
-  const int64_t per_block = (int64_t)64 * G * L;
-  const int items = G * L;
+  const int64_t per_block = (int64_t)64 * G * Q;
+  const int nb_per = Q / NB;                  // output blocks per lane stride
+  const int items = G * nb_per;
 
   for (int64_t g0 = (int64_t)blockIdx.x * per_block; g0 < total_out;
        g0 += (int64_t)gridDim.x * per_block) {
     // The block's windows run from its first output's first sample to its
-    // last output's last (window starts never decrease along the outputs).
+    // last output's (window starts never decrease along the outputs).
     const int64_t g_last = min(g0 + per_block, total_out) - 1;
     __syncthreads();                          // the previous block's span is consumed
     if (wave == 0) {
@@ -221,46 +261,57 @@ __device__ __forceinline__ void resample_body(const In* __restrict__ x,
       const int64_t k_last = wave_k0(g_last, sg, L, M, J, inv_L, lane);
       if (lane == 0) {
         bounds[0] = k_first;
-        bounds[1] = k_last + Tp;
+        bounds[1] = k_last + TpX;
       }
     }
     __syncthreads();
     const int64_t s0 = bounds[0];
     const int span_len = (int)min(max(bounds[1] - s0, (int64_t)0), (int64_t)kResLdsFloats);
-    for (int i = tid; i < span_len; i += blockDim.x) {
-      const int64_t k = s0 + i;
-      span[i] = (k >= 0 && k < total_in) ? res_sample(x, k) : 0.0f;
+    // coalesced, sixteen loads in flight per thread before the first store
+    for (int i0 = 0; i0 < span_len; i0 += 16 * 1024) {
+      float v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int i = i0 + u * 1024 + tid;
+        const int64_t k = s0 + i;
+        v[u] = (i < span_len && k >= 0 && k < total_in) ? res_sample(x, k) : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int i = i0 + u * 1024 + tid;
+        if (i < span_len) span[i] = v[u];
+      }
     }
     __syncthreads();
 
     ResClip cl{-1, 0, -1, 0, 0, 0};
-    // items it = wave, wave + n_waves, ... as (period group gi, phase r)
-    // with it = gi L + r, stepped without a division
-    int gi = wave / L, r = wave - (wave / L) * L;
-    const int step_q = n_waves / L, step_r = n_waves - (n_waves / L) * L;
+    // items it = wave, wave + n_waves, ... as (lane group gi, output block b)
+    // with it = gi nb_per + b, stepped without a division
+    int gi = wave / nb_per, b = wave - (wave / nb_per) * nb_per;
+    const int step_q = n_waves / nb_per, step_r = n_waves - (n_waves / nb_per) * nb_per;
     for (int it = wave; it < items; it += n_waves) {
       if (it != wave) {
         gi += step_q;
-        r += step_r;
-        if (r >= L) {
-          r -= L;
+        b += step_r;
+        if (b >= nb_per) {
+          b -= nb_per;
           ++gi;
         }
       }
-      const int64_t g = g0 + (int64_t)(gi * 64 + lane) * L + r;
+      const int64_t g = g0 + (int64_t)(gi * 64 + lane) * Q + NB * b;
       const bool active = g < total_out;
       ResSrc s{};
       bool ok = false;
       int64_t off = 0;
       if (active) {
-        if (!(cl.o_lo <= g && g < cl.o_hi)) cl = res_clip(g, sg);
-        s = res_pos(g, cl, L, M, J, inv_L);
+        s = res_at(g, cl, sg, L, M, J, inv_L);
         off = s.k0 - s0;
-        ok = s.k0 >= s.lo && s.k0 + T <= s.hi && off >= 0 && off + Tp <= span_len;
+        ok = g + NB <= cl.o_hi && s.k0 >= s.lo && s.k0 + Ur <= s.hi && off >= 0 &&
+             off + Ur <= span_len;
       }
-      // The lanes with a whole window, one phase at a time (one pass unless
-      // the item's outputs lie in several clips): the first waiting lane's
-      // phase, shared by the lanes that have it.
+      // The lanes whose NB windows are whole, one first phase at a time (one
+      // pass unless the item's outputs lie in several clips): the first
+      // waiting lane's phase, shared by the lanes that have it.
       uint64_t waiting = __ballot(ok);
       while (waiting) {
         const int lead = __builtin_ctzll(waiting);
@@ -268,82 +319,130 @@ __device__ __forceinline__ void resample_body(const In* __restrict__ x,
         const bool mine = ok && s.phi == phi_w;
         waiting &= ~__ballot(mine);
         if (mine) {
-          // The lanes here all have phase phi_w: the row address is uniform
-          // (taken with readfirstlane, so that it stays scalar), read through
-          // the constant address space, so the taps load with scalar loads
-          // into scalar registers.
+          // The row block's address is uniform (taken with readfirstlane, so
+          // that it stays scalar) and read through the constant address
+          // space: the taps load with scalar loads into scalar registers.
           const int pu = __builtin_amdgcn_readfirstlane(s.phi);
           const __attribute__((address_space(4))) float* trow =
-              (const __attribute__((address_space(4))) float*)(taps + (int64_t)pu * Tp);
+              (const __attribute__((address_space(4))) float*)(taps_blk +
+                                                                (int64_t)pu * NB * TpX);
           const float* sp = span + off;
-          float a0 = 0.0f, a1 = 0.0f;
-          const int full = T / kResChunk;
-          // Software pipeline over chunks of 16 taps, two buffers: the next
-          // chunk's taps (scalar loads) and samples (LDS reads) are issued
-          // before this chunk's multiply-adds and waited after them (scalar
-          // loads return out of order, so one wait covers both kinds).
-          ResChunk A, B;
-          res_load(trow, sp, 0, A);
-          res_wait(A);
-          int ch = 0;
-          for (; ch + 2 <= full; ch += 2) {
-            res_load(trow, sp, ch + 1, B);
-            asm volatile("" ::: "memory");
-            res_fma(A, a0, a1);
-            res_wait(B);
-            res_load(trow, sp, min(ch + 2, full - 1), A);
-            asm volatile("" ::: "memory");
-            res_fma(B, a0, a1);
-            res_wait(A);
-          }
-          if (ch < full) res_fma(A, a0, a1);
-          // the last chunk: samples past the window's T taps are not read
-          const int base = full * kResChunk;
+          float acc[NB];
 #pragma unroll
-          for (int j = 0; j < kResChunk; ++j)
-            if (base + j < T) a0 = __builtin_fmaf(trow[base + j], sp[base + j], a0);
-          y[g] = a0 + a1;
+          for (int a = 0; a < NB; ++a) acc[a] = 0.0f;
+          const int full = Ur / CH;
+          // Two chunks per step: both chunks' taps (scalar loads) and samples
+          // (LDS reads) are issued, then waited for once; the wavefronts on
+          // the other SIMDs' slots cover the wait.
+          ResChunk<NB, CH> A, B, C, D;
+          int ch = 0;
+          for (; ch + 4 <= full; ch += 4) {
+            res_load(trow, sp, ch, A);
+            res_load(trow, sp, ch + 1, B);
+            res_load(trow, sp, ch + 2, C);
+            res_load(trow, sp, ch + 3, D);
+            res_wait(A);
+            res_wait(B);
+            res_wait(C);
+            res_wait(D);
+            res_fma(A, acc);
+            res_fma(B, acc);
+            res_fma(C, acc);
+            res_fma(D, acc);
+          }
+          for (; ch + 2 <= full; ch += 2) {
+            res_load(trow, sp, ch, A);
+            res_load(trow, sp, ch + 1, B);
+            res_wait(A);
+            res_wait(B);
+            res_fma(A, acc);
+            res_fma(B, acc);
+          }
+          if (ch < full) {
+            res_load(trow, sp, ch, A);
+            res_wait(A);
+            res_fma(A, acc);
+          }
+          if (NB == 4) {
+            *reinterpret_cast<f4u*>(y + g) = f4u{acc[0], acc[1], acc[2], acc[3]};
+          } else {
+#pragma unroll
+            for (int a = 0; a < NB; ++a) y[g + a] = acc[a];
+          }
         }
       }
-      if (active && !ok) y[g] = res_one(s, taps, Tp, T, span, s0, span_len, x);
+      if (active && !ok) {
+        // each output alone (its own segment, phase and window)
+        for (int a = 0; a < NB; ++a) {
+          const int64_t ga = g + a;
+          if (ga < total_out) {
+            const ResSrc sa = res_at(ga, cl, sg, L, M, J, inv_L);
+            y[ga] = res_one(sa, taps, Tp, T, span, s0, span_len, x);
+          }
+        }
+      }
     }
   }
 }
 
-#define LOGMEL_RESAMPLE_KERNEL(NAME, IN)                                                         \
+#define LOGMEL_RESAMPLE_KERNEL(NAME, IN, NB, CH)                                                 \
   extern "C" __global__ void __launch_bounds__(1024)                                             \
   NAME(const IN* __restrict__ x, const int64_t* __restrict__ seg_lo,                            \
        const int64_t* __restrict__ seg_hi, const int64_t* __restrict__ nfirst,                  \
        const int64_t* __restrict__ out_off, int64_t n_segs, int64_t total_out,                  \
-       float* __restrict__ y, const float* __restrict__ taps, int L, int M, int J, int Tp,       \
+       float* __restrict__ y, const float* __restrict__ taps,                                   \
+       const float* __restrict__ taps_blk, int L, int M, int J, int Tp, int TpX, int Ur, int Q,  \
        int G) {                                                                                  \
     __shared__ float span[kResLdsFloats];                                                        \
     __shared__ int64_t bounds[2];                                                                \
     const ResSegs sg{seg_lo, seg_hi, nfirst, out_off, n_segs};                                   \
-    resample_body<IN>(x, sg, total_out, y, taps, L, M, J, Tp, G, span, bounds);                 \
+    resample_body<NB, CH, IN>(x, sg, total_out, y, taps, taps_blk, L, M, J, Tp, TpX, Ur, Q, G,   \
+                              span, bounds);                                                     \
   }
 
-LOGMEL_RESAMPLE_KERNEL(logmel_resample_kernel, float)
-LOGMEL_RESAMPLE_KERNEL(logmel_resample_i16_kernel, int16_t)
+LOGMEL_RESAMPLE_KERNEL(logmel_resample_kernel, float, 4, 4)
+LOGMEL_RESAMPLE_KERNEL(logmel_resample_i16_kernel, int16_t, 4, 4)
+LOGMEL_RESAMPLE_KERNEL(logmel_resample3_kernel, float, 3, 4)
+LOGMEL_RESAMPLE_KERNEL(logmel_resample3_i16_kernel, int16_t, 3, 4)
+LOGMEL_RESAMPLE_KERNEL(logmel_resample2_kernel, float, 2, 8)
+LOGMEL_RESAMPLE_KERNEL(logmel_resample2_i16_kernel, int16_t, 2, 8)
+LOGMEL_RESAMPLE_KERNEL(logmel_resample1_kernel, float, 1, 16)
+LOGMEL_RESAMPLE_KERNEL(logmel_resample1_i16_kernel, int16_t, 1, 16)
 
 }  // namespace logmel
 
 hipError_t logmel_launch_resample(const void* x, int in_i16, const int64_t* seg_lo,
                                   const int64_t* seg_hi, const int64_t* nfirst,
                                   const int64_t* out_off, int64_t n_segs, int64_t total_out,
-                                  float* y, const float* taps, int L, int M, int J, int Tp, int G,
-                                  int grid, hipStream_t stream) {
+                                  float* y, const float* taps, const float* taps_blk, int L, int M,
+                                  int J, int Tp, int TpX, int NB, int Q, int G, int grid,
+                                  hipStream_t stream) {
   if (total_out <= 0 || n_segs <= 0) return hipSuccess;
-  const int64_t per_block = (int64_t)64 * G * L;
+  const int64_t per_block = (int64_t)64 * G * Q;
+  // every lane of the shared path reads Ur samples: the largest union of NB
+  // windows rounded up to its chunk (taps beyond a phase's own union are zero)
+  const int CH = NB == 3 ? 4 : 16 / NB;
+  const int64_t d_max = (L - 1 + (int64_t)(NB - 1) * M) / L;
+  const int Ur = (int)((2 * J + 1 + d_max + CH - 1) / CH * CH);
   const int64_t blocks = (total_out + per_block - 1) / per_block;
   const int g = (int)(blocks < grid ? blocks : grid);
-  if (in_i16)
-    hipLaunchKernelGGL(logmel::logmel_resample_i16_kernel, dim3(g), dim3(1024), 0, stream,
-                       static_cast<const int16_t*>(x), seg_lo, seg_hi, nfirst, out_off, n_segs,
-                       total_out, y, taps, L, M, J, Tp, G);
-  else
-    hipLaunchKernelGGL(logmel::logmel_resample_kernel, dim3(g), dim3(1024), 0, stream,
-                       static_cast<const float*>(x), seg_lo, seg_hi, nfirst, out_off, n_segs,
-                       total_out, y, taps, L, M, J, Tp, G);
+#define LOGMEL_RES_LAUNCH(K, IN)                                                                \
+  hipLaunchKernelGGL(logmel::K, dim3(g), dim3(1024), 0, stream, static_cast<const IN*>(x), seg_lo, \
+                     seg_hi, nfirst, out_off, n_segs, total_out, y, taps, taps_blk, L, M, J, Tp,  \
+                     TpX, Ur, Q, G)
+  if (NB == 4) {
+    if (in_i16) LOGMEL_RES_LAUNCH(logmel_resample_i16_kernel, int16_t);
+    else LOGMEL_RES_LAUNCH(logmel_resample_kernel, float);
+  } else if (NB == 3) {
+    if (in_i16) LOGMEL_RES_LAUNCH(logmel_resample3_i16_kernel, int16_t);
+    else LOGMEL_RES_LAUNCH(logmel_resample3_kernel, float);
+  } else if (NB == 2) {
+    if (in_i16) LOGMEL_RES_LAUNCH(logmel_resample2_i16_kernel, int16_t);
+    else LOGMEL_RES_LAUNCH(logmel_resample2_kernel, float);
+  } else {
+    if (in_i16) LOGMEL_RES_LAUNCH(logmel_resample1_i16_kernel, int16_t);
+    else LOGMEL_RES_LAUNCH(logmel_resample1_kernel, float);
+  }
+#undef LOGMEL_RES_LAUNCH
   return hipGetLastError();
 }

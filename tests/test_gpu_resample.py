@@ -21,7 +21,8 @@ from tests.parity import assert_parity
 pytestmark = pytest.mark.gpu
 
 U = 2.0 ** -24
-RATES = [8000, 11025, 12000, 22050, 24000, 32000, 44100, 48000, 88200, 96000, 176400, 192000]
+RATES = [4800, 8000, 9600, 11025, 12000, 22050, 24000, 32000, 44100, 48000, 88200, 96000, 176400,
+         192000]
 
 
 def say(msg):
