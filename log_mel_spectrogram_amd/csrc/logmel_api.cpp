@@ -207,6 +207,7 @@ struct logmel_stream {
   // pinned staging ring for the per-push metadata
   static constexpr int kSlots = 4;
   int64_t* meta_host[kSlots] = {nullptr, nullptr, nullptr, nullptr};
+  int64_t* meta_host_dev[kSlots] = {nullptr, nullptr, nullptr, nullptr};   // their device addresses
   hipEvent_t slot_done[kSlots] = {nullptr, nullptr, nullptr, nullptr};
   int slot = 0;
   // host shadow, per stream
@@ -226,6 +227,7 @@ struct logmel_stream {
   float* res_buf = nullptr;             // one push's 16 kHz samples, packed
   int64_t* rmeta_dev = nullptr;         // [9n + 1], layout in rs_push
   int64_t* rmeta_host[kSlots] = {nullptr, nullptr, nullptr, nullptr};
+  int64_t* rmeta_host_dev[kSlots] = {nullptr, nullptr, nullptr, nullptr};
   hipEvent_t rslot_done[kSlots] = {nullptr, nullptr, nullptr, nullptr};
   int rslot = 0;
   std::vector<int64_t> rs_in, rs_out, rcarry_len, rcarry_src;
@@ -486,6 +488,8 @@ int logmel_stream_create(const logmel_plan* plan, int64_t n_streams, int64_t max
             hipMalloc(&s->meta_dev, meta_words * 8) == hipSuccess;
   for (int i = 0; ok && i < logmel_stream::kSlots; ++i)
     ok = hipHostMalloc(&s->meta_host[i], meta_words * 8, hipHostMallocDefault) == hipSuccess &&
+         hipHostGetDevicePointer(reinterpret_cast<void**>(&s->meta_host_dev[i]), s->meta_host[i],
+                                 0) == hipSuccess &&
          hipEventCreateWithFlags(&s->slot_done[i], hipEventDisableTiming) == hipSuccess;
   if (!ok) {
     logmel_stream_destroy(s);
@@ -572,6 +576,8 @@ int logmel_stream_create_ex(const logmel_plan* plan, int64_t n_streams, int64_t 
        hipMalloc(&s->rmeta_dev, rmeta_words * 8) == hipSuccess;
   for (int i = 0; ok && i < logmel_stream::kSlots; ++i)
     ok = hipHostMalloc(&s->rmeta_host[i], rmeta_words * 8, hipHostMallocDefault) == hipSuccess &&
+         hipHostGetDevicePointer(reinterpret_cast<void**>(&s->rmeta_host_dev[i]),
+                                 s->rmeta_host[i], 0) == hipSuccess &&
          hipEventCreateWithFlags(&s->rslot_done[i], hipEventDisableTiming) == hipSuccess;
   if (!ok) {
     logmel_stream_destroy(s);
@@ -660,14 +666,13 @@ int lm_push(logmel_stream* s, const void* d_new, int sample_type, const int64_t*
   const int64_t total_frames = fo[n];
   if (total_frames > INT64_MAX / kMels) return LOGMEL_ERR_INPUT_TOO_LONG;
   if (total_frames > 0 && !d_out) return LOGMEL_ERR_INVALID_ARGUMENT;
-  const size_t meta_bytes = (7 * (size_t)n + 1) * 8;
-  if (hipMemcpyAsync(s->meta_dev, m, meta_bytes, hipMemcpyHostToDevice, st) != hipSuccess ||
+  // The prep kernel reads the slot in place (no copy engine in the push's
+  // path) and hands the transform kernel its offsets in meta_dev.
+  if (logmel_launch_stream_prep(s->ws, s->stride, d_new, sample_type == LOGMEL_I16,
+                                s->meta_host_dev[slot], s->meta_dev, n, st) != hipSuccess ||
       hipEventRecord(s->slot_done[slot], st) != hipSuccess)
     return LOGMEL_ERR_DEVICE;
   s->slot = (slot + 1) % logmel_stream::kSlots;
-  if (logmel_launch_stream_prep(s->ws, s->stride, d_new, sample_type == LOGMEL_I16, s->meta_dev,
-                                n, st) != hipSuccess)
-    return LOGMEL_ERR_DEVICE;
   if (logmel_launch_tiles(s->plan->tables, s->ws, 0, s->meta_dev + 4 * n, s->meta_dev + 5 * n,
                           s->meta_dev + 6 * n, n, total_frames, d_out, out_type == LOGMEL_F16,
                           s->meta_dev + 6 * n, 1, total_frames, s->plan->resident_waves, st) !=
@@ -724,16 +729,15 @@ int rs_push(logmel_stream* s, const void* d_new, int sample_type, const int64_t*
     noff += p;
   }
   const int64_t total_k = m[9 * n];
-  const size_t meta_bytes = (9 * (size_t)n + 1) * 8;
-  if (hipMemcpyAsync(s->rmeta_dev, m, meta_bytes, hipMemcpyHostToDevice, st) != hipSuccess ||
+  float* src = s->in_buf[s->in_cur];
+  float* dst = s->in_buf[1 - s->in_cur];
+  // The prep kernel reads the slot in place and hands the resampling kernel
+  // its segment arrays in rmeta_dev.
+  if (logmel_launch_rstream_prep(dst, src, flush ? nullptr : d_new, sample_type == LOGMEL_I16,
+                                 s->rmeta_host_dev[slot], s->rmeta_dev, n, st) != hipSuccess ||
       hipEventRecord(s->rslot_done[slot], st) != hipSuccess)
     return LOGMEL_ERR_DEVICE;
   s->rslot = (slot + 1) % logmel_stream::kSlots;
-  float* src = s->in_buf[s->in_cur];
-  float* dst = s->in_buf[1 - s->in_cur];
-  if (logmel_launch_rstream_prep(dst, src, flush ? nullptr : d_new, sample_type == LOGMEL_I16,
-                                 s->rmeta_dev, n, st) != hipSuccess)
-    return LOGMEL_ERR_DEVICE;
   if (total_k > 0 &&
       logmel_launch_resample(dst, 0, s->rmeta_dev + 5 * n, s->rmeta_dev + 6 * n,
                              s->rmeta_dev + 7 * n, s->rmeta_dev + 8 * n, n, total_k, s->res_buf,

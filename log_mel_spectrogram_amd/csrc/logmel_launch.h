@@ -29,8 +29,10 @@ hipError_t logmel_launch_chunk_pad(void* out, int out_f16, const int64_t* frame_
                                    const int64_t* chunk_off, int64_t n_clips, int64_t out_rows,
                                    hipStream_t stream);
 
-// fresh: fp32, or int16 PCM (s / 32768) with in_i16.
+// fresh: fp32, or int16 PCM (s / 32768) with in_i16. meta: the host's
+// staging slot (pinned host memory, its device-side address); the kernel
+// copies what the transform kernel reads into meta_dev.
 hipError_t logmel_launch_stream_prep(float* ws, int64_t row_stride, const void* fresh, int in_i16,
-                                     const int64_t* meta, int64_t n_streams,
+                                     const int64_t* meta, int64_t* meta_dev, int64_t n_streams,
                                      hipStream_t stream);
 
