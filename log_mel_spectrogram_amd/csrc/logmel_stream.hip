@@ -44,8 +44,11 @@ __device__ __forceinline__ void stream_prep_body(float* __restrict__ ws, int64_t
   const int64_t clen = meta[n_streams + j];
   const int64_t noff = meta[2 * n_streams + j];
   const int64_t nlen = meta[3 * n_streams + j];
-  if (t < 3) meta_dev[(4 + t) * n_streams + j + (t == 2)] = meta[(4 + t) * n_streams + j + (t == 2)];
-  if (j == 0 && t == 3) meta_dev[6 * n_streams] = meta[6 * n_streams];
+  // the transform kernel's inputs: segment start and end, frame offsets
+  if (t == 0) meta_dev[4 * n_streams + j] = meta[4 * n_streams + j];
+  if (t == 1) meta_dev[5 * n_streams + j] = meta[5 * n_streams + j];
+  if (t == 2) meta_dev[6 * n_streams + j + 1] = meta[6 * n_streams + j + 1];
+  if (t == 3 && j == 0) meta_dev[6 * n_streams] = meta[6 * n_streams];
   // The carry can overlap its destination, and the new samples land where
   // the old ones were: read the carry and the first new samples before any
   // write.
@@ -108,8 +111,13 @@ __device__ __forceinline__ void rstream_prep_body(float* __restrict__ dst,
   const int64_t clen = meta[n_streams + j];
   const int64_t noff = meta[2 * n_streams + j];
   const int64_t nlen = meta[3 * n_streams + j];
-  if (t < 4) meta_dev[(5 + t) * n_streams + j + (t == 3)] = meta[(5 + t) * n_streams + j + (t == 3)];
-  if (j == 0 && t == 4) meta_dev[8 * n_streams] = meta[8 * n_streams];
+  // the resampling kernel's inputs: segment origin, end, first output
+  // number and output offsets
+  if (t == 0) meta_dev[5 * n_streams + j] = meta[5 * n_streams + j];
+  if (t == 1) meta_dev[6 * n_streams + j] = meta[6 * n_streams + j];
+  if (t == 2) meta_dev[7 * n_streams + j] = meta[7 * n_streams + j];
+  if (t == 3) meta_dev[8 * n_streams + j + 1] = meta[8 * n_streams + j + 1];
+  if (t == 4 && j == 0) meta_dev[8 * n_streams] = meta[8 * n_streams];
   float* seg = dst + meta[4 * n_streams + j];
   for (int64_t i = t; i < clen; i += 256) seg[i] = src[csrc + i];
   for (int64_t i = t; i < nlen; i += 256) seg[clen + i] = stream_sample(fresh + noff, i);
