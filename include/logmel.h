@@ -265,7 +265,11 @@ int logmel_stream_set_state(logmel_stream* s, const void* state_host, void* hip_
  * H = 24 R / (2 fc) input samples (24 zero crossings each side). A clip of
  * N samples gives ceil(16000 N / R) outputs. At R = 16000 the output is the
  * input. The taps are computed in fp64 and rounded to fp32; each output is
- * an fp32 dot product of at most 2 ceil(H) + 1 terms.
+ * an fp32 dot product of at most 2 ceil(H) + 1 terms, summed in tap order
+ * (the kernel forms a few consecutive outputs per lane over the union of
+ * their windows, with zero taps outside each output's own window, so a
+ * non-finite sample also reaches outputs whose window ends a few samples
+ * before it, within its clip).
  * --------------------------------------------------------------------------- */
 #define LOGMEL_RESAMPLE_ZEROS 24
 
@@ -279,8 +283,9 @@ int64_t logmel_resample_length(int64_t n_samples, int32_t in_rate);
 int logmel_resample_offsets(int32_t in_rate, const int64_t* sample_offsets_host, int64_t n_clips,
                             int64_t* out_offsets_host);
 
-/* A resampler for one input rate: owns the device taps table ([L][2J + 1]
- * fp32 with 16000 / R = L / M in lowest terms). UNSUPPORTED for rates outside
+/* A resampler for one input rate: owns the device taps tables (fp32, [L]
+ * rows of 2J + 1 taps with 16000 / R = L / M in lowest terms, and the same
+ * taps arranged per group of consecutive outputs). UNSUPPORTED for rates outside
  * [1000, 384000] and for rates with so many phases that the table does not
  * fit the kernel's LDS (it holds every common rate: 8000, 11025, 12000,
  * 16000, 22050, 24000, 32000, 44100, 48000, 88200, 96000, 176400, 192000). */
