@@ -96,13 +96,10 @@ double bessel_i0(double x) {
 struct ResGeometry {
   int64_t L, M;   // 16000 / R = L / M in lowest terms
   int J;          // taps j = 0 .. 2J cover input samples q - J .. q + J
-  int Tp;         // 2J + 1 rounded up to a multiple of 16 (table row length)
+  int Tp;         // 2J + 1 rounded up to a multiple of 16 (host table row length)
   double fc, H;   // cutoff (Hz) and half-width (input samples)
-  int G;          // lane groups of 64 per block
-  int NB;         // consecutive outputs per lane on the shared path: 4, 3, 2 or 1
-  int Q;          // outputs between neighbouring lanes' first outputs: L, or NB when L divides NB
-  int TpX;        // row length of the shared path's table: the largest union of NB windows,
-                  // rounded up to a multiple of 16
+  RsmGeometry k;  // the matrix-core kernel's geometry; k.NT == 0: unsupported
+  std::vector<int> gbase;   // per column group, floor(16 g M / L)
 };
 
 ResGeometry res_geometry(int32_t rate) {
@@ -114,26 +111,37 @@ ResGeometry res_geometry(int32_t rate) {
   g.H = kResZeros * (double)rate / (2.0 * g.fc);
   g.J = rate == 16000 ? 0 : (int)std::ceil(g.H);
   g.Tp = (2 * g.J + 1 + 15) / 16 * 16;
-  // (16 kHz input is the identity: one output per lane, each reading only its own sample)
-  // (integer ratios with M odd: 3, so that the lanes' windows, 3 M apart,
-  // fall on different LDS banks)
-  g.NB = g.J == 0                             ? 1
-         : (g.L == 1 && g.M % 2 == 1)         ? 3
-         : (g.L % 4 == 0 || 4 % g.L == 0)     ? 4
-         : (g.L % 2 == 0)                     ? 2
-                                              : 1;
-  g.Q = g.L % g.NB == 0 ? (int)g.L : g.NB;
-  // first phase phi's union of NB windows: 2J + 1 + floor((phi + (NB - 1) M) / L)
-  const int64_t d_max = (g.L - 1 + (int64_t)(g.NB - 1) * g.M) / g.L;
-  g.TpX = (int)((2 * g.J + 1 + d_max + 15) / 16 * 16);
-  // A block of 64 G lanes needs about 64 G Q M / L + TpX staged samples; at
-  // most 1024 (lane group, output block) items per block.
-  const int64_t room = kResLdsFloats - g.TpX - 64;
-  int64_t G = room / (64 * (g.Q * g.M / g.L));
-  const int64_t per_group = g.Q / g.NB;
-  const int64_t item_cap = 1024 / per_group > 1 ? 1024 / per_group : 1;
-  if (G > item_cap) G = item_cap;
-  g.G = (int)(G < 1 ? 0 : G);
+  RsmGeometry& k = g.k;
+  k = RsmGeometry{0, 0, 0, 0, 0, 1, g.J, 0, 0};
+  // super-periods of S = lcm(L, 16) outputs, S M / L input samples apart
+  const int64_t S = g.L / gcd64(g.L, 16) * 16;
+  const int64_t S_in = S / g.L * g.M;
+  const int64_t C = S / 16;
+  if (S > (1 << 20) || S_in > kRsmLdsMax) return g;   // too many phases, or too sparse
+  g.gbase.resize((size_t)C);
+  int64_t dmax = 0;
+  for (int64_t gm = 0; gm < C; ++gm) {
+    g.gbase[(size_t)gm] = (int)((16 * gm * g.M) / g.L);
+    const int64_t dd = ((16 * gm + 15) * g.M) / g.L - g.gbase[(size_t)gm];
+    if (dd > dmax) dmax = dd;
+  }
+  // K / 4 MFMA steps cover 2J + 1 + dmax samples, padded to whole chunks of 8 steps
+  const int64_t KS = ((2 * g.J + 1 + dmax + 3) / 4 + 7) / 8 * 8;
+  const int64_t base_max = g.gbase.back();
+  auto span_of = [&](int64_t nt) { return (16 * nt - 1) * S_in + base_max + 4 * KS; };
+  int64_t NT = 1;
+  if (span_of(1) > kRsmLdsMax) return g;
+  while (NT < 8 && span_of(2 * NT) <= kRsmLdsSmall) NT *= 2;   // 1, 2, 4 or 8 row blocks
+  k.S = (int)S;
+  k.S_in = (int)S_in;
+  k.C = (int)C;
+  k.KS = (int)KS;
+  k.NT = (int)NT;
+  // two row blocks per item share one read of the taps, when that still
+  // leaves an item for each of the four wavefronts
+  k.RB = NT % 2 == 0 && C * NT / 2 >= 4 ? 2 : 1;
+  k.span = (int)span_of(NT);
+  k.TB = NT * 16 * S;
   return g;
 }
 
@@ -164,19 +172,24 @@ std::vector<float> res_taps(int32_t rate, const ResGeometry& g) {
   return t;
 }
 
-// The shared path's table [L][TpX][NB]: for first phase phi, entry [s][a] is
-// the tap of output a after it (phase (phi + a M) mod L) for the union's
-// sample s, i.e. that output's row shifted right by its window's offset
-// floor((phi + a M) / L); zeros elsewhere.
-std::vector<float> res_taps_blk(const ResGeometry& g, const std::vector<float>& t) {
+// The matrix cores' B operand, [C][KS][64]: for column group g and step s,
+// lane l holds W_g[4 s + l / 16][l % 16], where W_g[k][c] is the tap of
+// output r = 16 g + c (phase r M mod L) for sample k of the group's window,
+// i.e. its row shifted right by floor(r M / L) - floor(16 g M / L), zeros
+// elsewhere.
+std::vector<float> res_btab(const ResGeometry& g, const std::vector<float>& t) {
+  const RsmGeometry& k = g.k;
   const int T = 2 * g.J + 1;
-  std::vector<float> b((size_t)(g.L * g.NB * g.TpX), 0.0f);
-  for (int64_t phi = 0; phi < g.L; ++phi)
-    for (int a = 0; a < g.NB; ++a) {
-      const int64_t pa = (phi + a * g.M) % g.L;
-      const int64_t d = (phi + a * g.M) / g.L;
-      for (int j = 0; j < T; ++j)
-        b[(size_t)((phi * g.TpX + d + j) * g.NB + a)] = t[(size_t)(pa * g.Tp + j)];
+  std::vector<float> b((size_t)k.C * k.KS * 64, 0.0f);
+  for (int64_t gm = 0; gm < k.C; ++gm)
+    for (int c = 0; c < 16; ++c) {
+      const int64_t r = 16 * gm + c;
+      const int64_t phi = (r * g.M) % g.L;
+      const int64_t d = (r * g.M) / g.L - g.gbase[(size_t)gm];
+      for (int j = 0; j < T; ++j) {
+        const int64_t kk = d + j;   // sample of the window
+        b[(size_t)((gm * k.KS + kk / 4) * 64 + (kk % 4) * 16 + c)] = t[(size_t)(phi * g.Tp + j)];
+      }
     }
   return b;
 }
@@ -192,9 +205,8 @@ struct logmel_resampler {
   const logmel_plan* plan;
   int32_t rate;
   ResGeometry geo;
-  int grid;
-  float* taps = nullptr;       // device [L][Tp], then the shared path's [L][TpX][NB]
-  float* taps_blk = nullptr;   // inside the taps allocation
+  float* btab = nullptr;   // device: the B operand [C][KS][64], then gbase [C] int32
+  int* gbase = nullptr;    // inside the btab allocation
 };
 
 struct logmel_stream {
@@ -741,8 +753,7 @@ int rs_push(logmel_stream* s, const void* d_new, int sample_type, const int64_t*
   if (total_k > 0 &&
       logmel_launch_resample(dst, 0, s->rmeta_dev + 5 * n, s->rmeta_dev + 6 * n,
                              s->rmeta_dev + 7 * n, s->rmeta_dev + 8 * n, n, total_k, s->res_buf,
-                             s->rs->taps, s->rs->taps_blk, (int)geo.L, (int)geo.M, geo.J, geo.Tp,
-                             geo.TpX, geo.NB, geo.Q, geo.G, s->rs->grid, st) != hipSuccess)
+                             s->rs->btab, s->rs->gbase, geo.k, st) != hipSuccess)
     return LOGMEL_ERR_DEVICE;
   const int r = lm_push(s, s->res_buf, LOGMEL_F32, k.data(), d_out, out_type, fo_out, st);
   if (r != LOGMEL_OK) return r;
@@ -905,43 +916,43 @@ int logmel_resampler_create(const logmel_plan* plan, int32_t in_rate, logmel_res
   *out = nullptr;
   if (!res_rate_ok(in_rate)) return LOGMEL_ERR_UNSUPPORTED;
   const ResGeometry geo = res_geometry(in_rate);
-  if (geo.G < 1 || geo.L * (geo.Tp + geo.NB * geo.TpX) > kResMaxTableFloats)
-    return LOGMEL_ERR_UNSUPPORTED;   // 64 lanes' inputs beyond LDS, or too many phases
-  std::vector<float> taps = res_taps(in_rate, geo);
-  const std::vector<float> blk = res_taps_blk(geo, taps);
-  const size_t plain = taps.size();
-  taps.insert(taps.end(), blk.begin(), blk.end());
+  if (geo.k.NT < 1 || (int64_t)geo.k.C * geo.k.KS * 64 + geo.k.C > kResMaxTableFloats ||
+      geo.L * geo.Tp > kResMaxTableFloats)
+    return LOGMEL_ERR_UNSUPPORTED;   // a tile's input beyond LDS, or too many phases
+  const std::vector<float> taps = res_taps(in_rate, geo);
+  const std::vector<float> btab = res_btab(geo, taps);
   logmel_resampler* r = new (std::nothrow) logmel_resampler;
   if (!r) return LOGMEL_ERR_OUT_OF_MEMORY;
   r->plan = plan;
   r->rate = in_rate;
   r->geo = geo;
-  r->grid = plan->resident_waves / 4;   // one workgroup per compute unit
   DeviceGuard g(plan->cfg.device);
   if (!g.ok) {
     delete r;
     return LOGMEL_ERR_DEVICE;
   }
-  if (hipMalloc(&r->taps, taps.size() * sizeof(float)) != hipSuccess) {
+  const size_t bbytes = btab.size() * sizeof(float);
+  const size_t gbytes = geo.gbase.size() * sizeof(int);
+  if (hipMalloc(&r->btab, bbytes + gbytes) != hipSuccess) {
     delete r;
     return LOGMEL_ERR_OUT_OF_MEMORY;
   }
-  if (hipMemcpy(r->taps, taps.data(), taps.size() * sizeof(float), hipMemcpyHostToDevice) !=
-      hipSuccess) {
-    (void)hipFree(r->taps);
+  r->gbase = reinterpret_cast<int*>(reinterpret_cast<char*>(r->btab) + bbytes);
+  if (hipMemcpy(r->btab, btab.data(), bbytes, hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(r->gbase, geo.gbase.data(), gbytes, hipMemcpyHostToDevice) != hipSuccess) {
+    (void)hipFree(r->btab);
     delete r;
     return LOGMEL_ERR_DEVICE;
   }
-  r->taps_blk = r->taps + plain;
   *out = r;
   return LOGMEL_OK;
 }
 
 void logmel_resampler_destroy(logmel_resampler* r) {
   if (!r) return;
-  if (r->taps) {
+  if (r->btab) {
     DeviceGuard g(r->plan->cfg.device);
-    (void)hipFree(r->taps);
+    (void)hipFree(r->btab);
   }
   delete r;
 }
@@ -978,8 +989,7 @@ int logmel_resample(const logmel_resampler* r, const void* d_samples, int sample
   }
   if (logmel_launch_resample(d_samples, sample_type == LOGMEL_I16, d_sample_offsets,
                              d_sample_offsets + 1, nullptr, d_out_offsets, n_clips, total_out,
-                             d_out, r->taps, r->taps_blk, (int)r->geo.L, (int)r->geo.M, r->geo.J,
-                             r->geo.Tp, r->geo.TpX, r->geo.NB, r->geo.Q, r->geo.G, r->grid, st) !=
+                             d_out, r->btab, r->gbase, r->geo.k, st) !=
       hipSuccess)
     return LOGMEL_ERR_DEVICE;
   return LOGMEL_OK;

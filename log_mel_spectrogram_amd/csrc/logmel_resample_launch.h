@@ -3,27 +3,36 @@
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
-// Resampling to 16 kHz: LDS floats of one workgroup's staged input span
-// (one 1024-thread workgroup per compute unit).
-static constexpr int kResLdsFloats = 38400;   // 150 KB of the 160 KB
+// Resampling to 16 kHz on the matrix cores (see logmel_resample.hip): the
+// geometry of one input rate. Super-periods of S outputs start S_in input
+// samples apart; C column groups of 16 outputs; KS MFMA steps of 4 samples
+// per output (a multiple of 8); tiles of NT x 16 super-periods, TB outputs,
+// worked in items of RB row blocks (RB divides NT);
+// span: LDS floats one tile stages; J: the half-width in input samples.
+struct RsmGeometry {
+  int S, S_in, C, KS, NT, RB, J, span;
+  int64_t TB;
+};
+
+// Largest LDS span a resampling workgroup may stage (floats), and the span
+// below which two or more workgroups share a compute unit.
+static constexpr int kRsmLdsMax = 38400;
+static constexpr int kRsmLdsSmall = 14336;
 
 // Segment i's samples are [seg_lo[i], seg_hi[i]) of x (fp32, or int16 PCM
-// with in_i16), its clip's sample 0 at seg_lo[i]; its outputs
-// [out_off[i], out_off[i + 1]) of y are the clip's outputs nfirst[i],
-// nfirst[i] + 1, ... (nfirst null: from 0). The last segment ends x. An
-// offline batch passes its sample offsets as seg_lo and, one further, as
-// seg_hi. taps is the device table [L][Tp] (rows of 2J + 1 taps zero-padded
-// to Tp, a multiple of 16); taps_blk the table [L][TpX][NB] of the shared
-// path (for each first phase, the NB outputs' rows shifted by their windows'
-// offsets, interleaved sample by sample);
-// NB in {1, 2, 3, 4} outputs per lane, lanes Q outputs apart; blocks of 64 G
-// lanes; grid: workgroups resident at once.
+// with in_i16), its clip's sample 0 at seg_lo[i]; samples before
+// max(seg_lo[i], seg_hi[i - 1]) and from seg_hi[i] on read as zero; its
+// outputs [out_off[i], out_off[i + 1]) of y are the clip's outputs
+// nfirst[i], nfirst[i] + 1, ... (nfirst null: from 0). The last segment
+// ends x. An offline batch passes its sample offsets as seg_lo and, one
+// further, as seg_hi. btab: [C][KS][64] fp32 (the B operand per column
+// group and step, in the MFMA's lane layout); gbase: [C] int32, the window
+// offset floor(16 g M / L) of column group g.
 hipError_t logmel_launch_resample(const void* x, int in_i16, const int64_t* seg_lo,
                                   const int64_t* seg_hi, const int64_t* nfirst,
                                   const int64_t* out_off, int64_t n_segs, int64_t total_out,
-                                  float* y, const float* taps, const float* taps_blk, int L, int M,
-                                  int J, int Tp, int TpX, int NB, int Q, int G, int grid,
-                                  hipStream_t stream);
+                                  float* y, const float* btab, const int* gbase,
+                                  const RsmGeometry& geo, hipStream_t stream);
 
 // A resampling stream's push, step 1: segment j of dst = src[carry index,
 // + carry length) followed by the new samples of stream j (fp32, or int16
