@@ -50,12 +50,18 @@ FLOPS_PER_FRAME = 8228 + 788
 FS = 16000
 
 
-def kernel_source_hash():
+TILES_SOURCES = ("logmel_kernels.hip", "logmel_frame.h", "logmel_launch.h", "gen_tables.py")
+# the resampler's counters also depend on its geometry and taps, built in
+# the C-ABI layer
+RESAMPLE_SOURCES = ("logmel_resample.hip", "logmel_resample_launch.h", "logmel_api.cpp")
+
+
+def kernel_source_hash(files=TILES_SOURCES):
     """Hash of the kernel sources with comments and blank space removed, so
     that a comment edit does not invalidate a counter summary."""
     import re
     h = hashlib.sha256()
-    for f in ("logmel_kernels.hip", "logmel_frame.h", "logmel_launch.h", "gen_tables.py"):
+    for f in files:
         with open(os.path.join(ROOT, "log_mel_spectrogram_amd", "csrc", f)) as fh:
             text = fh.read()
         if f.endswith(".py"):
@@ -68,17 +74,18 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if
-    it was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"logmel_tiles_{workload}_pmc.md")
+def measured_traffic(profile, files=TILES_SOURCES):
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    profiles/<profile>_pmc.md, if it was taken on the current kernel source;
+    else None."""
+    path = os.path.join(ROOT, "profiles", f"{profile}_pmc.md")
     if not os.path.exists(path):
         return None
     rec = None
     for line in open(path):
         if line.startswith("TRAFFIC_JSON "):
             rec = json.loads(line[len("TRAFFIC_JSON "):])
-    if not rec or rec.get("kernel_source_hash") != kernel_source_hash():
+    if not rec or rec.get("kernel_source_hash") != kernel_source_hash(files):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -269,7 +276,7 @@ def bench_offline(args, lm, plan, torch):
     audio_s = n_samples / FS
     achieved_gbs = algo_bytes / kern_avg_s / 1e9
     achieved_tflops = FLOPS_PER_FRAME * total / kern_avg_s / 1e12
-    traffic = measured_traffic(args.workload) if not (chunked or general) else None
+    traffic = measured_traffic(f"logmel_tiles_{args.workload}") if not (chunked or general) else None
     rec = {
         "metric": "audio-seconds/sec of 128-bin log-mel on 1 MI355X + % of HBM roofline",
         "value": audio_s / (ms_per_step / 1e3),
@@ -401,9 +408,13 @@ def bench_resampled(args, lm, plan, torch):
         "frames_per_s": total / (ms_per_step / 1e3),
         "resample_kernel_avg_us": rs_s * 1e6,
         "logmel_kernel_avg_us": lm_s * 1e6,
-        "roofline": {"bound": "alu", "achieved": rs_tflops, "peak": FP32_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": rs_tflops / FP32_PEAK_TFLOPS, "traffic": None,
-                     "kernel": "logmel_resample_kernel", "kernel_avg_us": rs_s * 1e6,
+        "roofline": {"bound": "mfma", "achieved": rs_tflops, "peak": FP32_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": rs_tflops / FP32_PEAK_TFLOPS,
+                     "traffic": measured_traffic("logmel_resample_c2_44k", RESAMPLE_SOURCES)
+                     if rate == 44100 else None,
+                     "kernel": "logmel_resample (its instance for this rate: "
+                               "logmel_resample2_wide_kernel at 44.1 kHz)",
+                     "kernel_avg_us": rs_s * 1e6,
                      "algorithmic_flops_per_launch": rs_flops,
                      "algorithmic_bytes_per_launch": rs_bytes,
                      "hbm_achieved_gbs": rs_bytes / rs_s / 1e9,

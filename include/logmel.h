@@ -265,11 +265,13 @@ int logmel_stream_set_state(logmel_stream* s, const void* state_host, void* hip_
  * H = 24 R / (2 fc) input samples (24 zero crossings each side). A clip of
  * N samples gives ceil(16000 N / R) outputs. At R = 16000 the output is the
  * input. The taps are computed in fp64 and rounded to fp32; each output is
- * an fp32 dot product of at most 2 ceil(H) + 1 terms, summed in tap order
- * (the kernel forms a few consecutive outputs per lane over the union of
- * their windows, with zero taps outside each output's own window, so a
- * non-finite sample also reaches outputs whose window ends a few samples
- * before it, within its clip).
+ * an fp32 dot product of its 2 ceil(H) + 1 terms, accumulated in fp32 on the
+ * matrix cores four products per step (the kernel forms 16 consecutive
+ * outputs at once over the union of their windows, with zero taps outside
+ * each output's own window; an output gets the same value whichever call
+ * forms it, but a non-finite sample also reaches the outputs of its group of
+ * 16 whose union holds it, up to 4 ceil((2J + 1 + spread) / 4) - 2J - 1
+ * samples beyond their own windows (53 at 44.1 kHz), within its clip).
  * --------------------------------------------------------------------------- */
 #define LOGMEL_RESAMPLE_ZEROS 24
 
@@ -283,12 +285,13 @@ int64_t logmel_resample_length(int64_t n_samples, int32_t in_rate);
 int logmel_resample_offsets(int32_t in_rate, const int64_t* sample_offsets_host, int64_t n_clips,
                             int64_t* out_offsets_host);
 
-/* A resampler for one input rate: owns the device taps tables (fp32, [L]
- * rows of 2J + 1 taps with 16000 / R = L / M in lowest terms, and the same
- * taps arranged per group of consecutive outputs). UNSUPPORTED for rates outside
- * [1000, 384000] and for rates with so many phases that the table does not
- * fit the kernel's LDS (it holds every common rate: 8000, 11025, 12000,
- * 16000, 22050, 24000, 32000, 44100, 48000, 88200, 96000, 176400, 192000). */
+/* A resampler for one input rate: owns the device taps table (fp32: the
+ * 2J + 1 taps of each of the L phases, 16000 / R = L / M in lowest terms,
+ * arranged per group of 16 consecutive outputs as the matrix cores read
+ * them). UNSUPPORTED for rates outside [1000, 384000] and for rates with so
+ * many phases, or samples so far apart, that a tile's input does not fit the
+ * kernel's LDS (it holds every common rate: 8000, 11025, 12000, 16000,
+ * 22050, 24000, 32000, 44100, 48000, 88200, 96000, 176400, 192000). */
 typedef struct logmel_resampler logmel_resampler;
 int logmel_resampler_create(const logmel_plan* plan, int32_t in_rate, logmel_resampler** out);
 void logmel_resampler_destroy(logmel_resampler* r);

@@ -25,7 +25,10 @@
 // call's range falls in window b (a clip's first tile at its first output,
 // the others at their start), so every tile is formed once and clips of any
 // length need no lookup table. A tile's input (zero outside the clip's
-// available samples) is staged in LDS; the 4 wavefronts take its NT x C
+// available samples) is staged in LDS, 8 samples per thread in flight, or 32
+// for spans of 8192 floats or more (the *_wide_* instances: fewer round trips
+// where the span is long, fewer registers where it is short); the 4
+// wavefronts take its NT x C
 // items (row block, column group) in turn, each K / 4 MFMAs with A read from
 // LDS and B from the table, in chunks of 8 steps whose loads are issued one
 // chunk ahead. Outputs outside the call's range are formed and dropped.
@@ -107,7 +110,7 @@ __device__ __forceinline__ void rsm_mma(const RsmChunk<NT>& c, rsm_f4 (&acc)[NT]
       acc[rb] = __builtin_amdgcn_mfma_f32_16x16x4f32(c.a[rb][s], c.b[s], acc[rb], 0, 0, 0);
 }
 
-template <int RB, typename In>
+template <int RB, int STG, typename In>
 __device__ __forceinline__ void rsm_body(const In* __restrict__ x, const int64_t* __restrict__ seg_lo,
                                          const int64_t* __restrict__ seg_hi,
                                          const int64_t* __restrict__ nfirst,
@@ -144,18 +147,40 @@ __device__ __forceinline__ void rsm_body(const In* __restrict__ x, const int64_t
       const int64_t sp0 = jt * geo.NT * 16;
       const int64_t k0 = lo + sp0 * geo.S_in - geo.J;   // buffer index of staged value 0
       __syncthreads();                                   // the previous tile's items are done
-      for (int i0 = 0; i0 < geo.span; i0 += 8 * kRsmThreads) {
-        float v[8];
+      if constexpr (STG == 8) {
+        for (int i0 = 0; i0 < geo.span; i0 += 8 * kRsmThreads) {
+          float v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int i = i0 + u * kRsmThreads + tid;
-          const int64_t k = k0 + i;
-          v[u] = (i < geo.span && k >= avail_lo && k < avail_hi) ? res_sample(x, k) : 0.0f;
+          for (int u = 0; u < 8; ++u) {
+            const int i = i0 + u * kRsmThreads + tid;
+            const int64_t k = k0 + i;
+            v[u] = (i < geo.span && k >= avail_lo && k < avail_hi) ? res_sample(x, k) : 0.0f;
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int i = i0 + u * kRsmThreads + tid;
+            if (i < geo.span) xs[i] = v[u];
+          }
         }
+      } else {
+        // STG samples per thread in flight: loads clamped into the available
+        // staged indexes [ia, ib), the rest written as zero
+        const int ia = (int)min(max(avail_lo - k0, (int64_t)0), (int64_t)geo.span);
+        const int ib = (int)min(max(avail_hi - k0, (int64_t)ia), (int64_t)geo.span);
+        for (int i0 = 0; i0 < geo.span; i0 += STG * kRsmThreads) {
+          float v[STG];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int i = i0 + u * kRsmThreads + tid;
-          if (i < geo.span) xs[i] = v[u];
+          for (int u = 0; u < STG; ++u) {
+            const int i = i0 + u * kRsmThreads + tid;
+            v[u] = (ia < ib && i0 + u * kRsmThreads < geo.span)
+                       ? res_sample(x, k0 + min(max(i, ia), ib - 1))
+                       : 0.0f;
+          }
+#pragma unroll
+          for (int u = 0; u < STG; ++u) {
+            const int i = i0 + u * kRsmThreads + tid;
+            if (i < geo.span) xs[i] = (i >= ia && i < ib) ? v[u] : 0.0f;
+          }
         }
       }
       __syncthreads();
@@ -198,7 +223,7 @@ __device__ __forceinline__ void rsm_body(const In* __restrict__ x, const int64_t
   }
 }
 
-#define LOGMEL_RESAMPLE_KERNEL(NAME, IN, RB)                                                     \
+#define LOGMEL_RESAMPLE_KERNEL(NAME, IN, RB, STG)                                                \
   extern "C" __global__ void __launch_bounds__(kRsmThreads)                                      \
   NAME(const IN* __restrict__ x, const int64_t* __restrict__ seg_lo,                            \
        const int64_t* __restrict__ seg_hi, const int64_t* __restrict__ nfirst,                  \
@@ -206,14 +231,18 @@ __device__ __forceinline__ void rsm_body(const In* __restrict__ x, const int64_t
        float* __restrict__ y, const float* __restrict__ btab, const int* __restrict__ gbase,     \
        RsmGeometry geo) {                                                                        \
     extern __shared__ float xs[];                                                                \
-    rsm_body<RB, IN>(x, seg_lo, seg_hi, nfirst, out_off, n_segs, total_out, y, btab, gbase, geo, \
+    rsm_body<RB, STG, IN>(x, seg_lo, seg_hi, nfirst, out_off, n_segs, total_out, y, btab, gbase, geo, \
                      xs);                                                                        \
   }
 
-LOGMEL_RESAMPLE_KERNEL(logmel_resample_kernel, float, 1)
-LOGMEL_RESAMPLE_KERNEL(logmel_resample_i16_kernel, int16_t, 1)
-LOGMEL_RESAMPLE_KERNEL(logmel_resample2_kernel, float, 2)
-LOGMEL_RESAMPLE_KERNEL(logmel_resample2_i16_kernel, int16_t, 2)
+LOGMEL_RESAMPLE_KERNEL(logmel_resample_kernel, float, 1, 8)
+LOGMEL_RESAMPLE_KERNEL(logmel_resample_i16_kernel, int16_t, 1, 8)
+LOGMEL_RESAMPLE_KERNEL(logmel_resample2_kernel, float, 2, 8)
+LOGMEL_RESAMPLE_KERNEL(logmel_resample2_i16_kernel, int16_t, 2, 8)
+LOGMEL_RESAMPLE_KERNEL(logmel_resample_wide_kernel, float, 1, 32)
+LOGMEL_RESAMPLE_KERNEL(logmel_resample_wide_i16_kernel, int16_t, 1, 32)
+LOGMEL_RESAMPLE_KERNEL(logmel_resample2_wide_kernel, float, 2, 32)
+LOGMEL_RESAMPLE_KERNEL(logmel_resample2_wide_i16_kernel, int16_t, 2, 32)
 
 }  // namespace logmel
 
@@ -230,12 +259,25 @@ hipError_t logmel_launch_resample(const void* x, int in_i16, const int64_t* seg_
   hipLaunchKernelGGL(logmel::K, dim3((unsigned)blocks), dim3(logmel::kRsmThreads), lds, stream,  \
                      static_cast<const IN*>(x), seg_lo, seg_hi, nfirst, out_off, n_segs,         \
                      total_out, y, btab, gbase, geo)
+  // large spans: 32 staged samples per thread in flight, else 8 (fewer
+  // registers, more workgroups per compute unit)
+  const bool wide = geo.span >= 32 * logmel::kRsmThreads;
   if (geo.RB == 2) {
-    if (in_i16) LOGMEL_RSM(logmel_resample2_i16_kernel, int16_t);
-    else LOGMEL_RSM(logmel_resample2_kernel, float);
+    if (wide) {
+      if (in_i16) LOGMEL_RSM(logmel_resample2_wide_i16_kernel, int16_t);
+      else LOGMEL_RSM(logmel_resample2_wide_kernel, float);
+    } else {
+      if (in_i16) LOGMEL_RSM(logmel_resample2_i16_kernel, int16_t);
+      else LOGMEL_RSM(logmel_resample2_kernel, float);
+    }
   } else {
-    if (in_i16) LOGMEL_RSM(logmel_resample_i16_kernel, int16_t);
-    else LOGMEL_RSM(logmel_resample_kernel, float);
+    if (wide) {
+      if (in_i16) LOGMEL_RSM(logmel_resample_wide_i16_kernel, int16_t);
+      else LOGMEL_RSM(logmel_resample_wide_kernel, float);
+    } else {
+      if (in_i16) LOGMEL_RSM(logmel_resample_i16_kernel, int16_t);
+      else LOGMEL_RSM(logmel_resample_kernel, float);
+    }
   }
 #undef LOGMEL_RSM
   return hipGetLastError();
