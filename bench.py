@@ -413,7 +413,7 @@ def bench_resampled(args, lm, plan, torch):
                      "traffic": measured_traffic("logmel_resample_c2_44k", RESAMPLE_SOURCES)
                      if rate == 44100 else None,
                      "kernel": "logmel_resample (its instance for this rate: "
-                               "logmel_resample2_wide_kernel at 44.1 kHz)",
+                               "logmel_resample2_wide_8w_kernel at 44.1 kHz)",
                      "kernel_avg_us": rs_s * 1e6,
                      "algorithmic_flops_per_launch": rs_flops,
                      "algorithmic_bytes_per_launch": rs_bytes,

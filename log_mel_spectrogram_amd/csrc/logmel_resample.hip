@@ -28,7 +28,8 @@
 // available samples) is staged in LDS, 8 samples per thread in flight, or 32
 // for spans of 8192 floats or more (the *_wide_* instances: fewer round trips
 // where the span is long, fewer registers where it is short); the 4
-// wavefronts take its NT x C
+// wavefronts (8 in the *_8w_* instances, for tiles of 8 items or more) take
+// its NT x C
 // items (row block, column group) in turn, each K / 4 MFMAs with A read from
 // LDS and B from the table, in chunks of 8 steps whose loads are issued one
 // chunk ahead. Outputs outside the call's range are formed and dropped.
@@ -43,7 +44,6 @@
 
 namespace logmel {
 
-static constexpr int kRsmThreads = 256;   // 4 wavefronts
 static constexpr int kRsmChunk = 8;       // MFMA steps per chunk (K / 4 is padded to a multiple)
 
 typedef float rsm_f4 __attribute__((ext_vector_type(4)));
@@ -110,7 +110,7 @@ __device__ __forceinline__ void rsm_mma(const RsmChunk<NT>& c, rsm_f4 (&acc)[NT]
       acc[rb] = __builtin_amdgcn_mfma_f32_16x16x4f32(c.a[rb][s], c.b[s], acc[rb], 0, 0, 0);
 }
 
-template <int RB, int STG, typename In>
+template <int RB, int STG, int NTH, typename In>
 __device__ __forceinline__ void rsm_body(const In* __restrict__ x, const int64_t* __restrict__ seg_lo,
                                          const int64_t* __restrict__ seg_hi,
                                          const int64_t* __restrict__ nfirst,
@@ -148,17 +148,17 @@ __device__ __forceinline__ void rsm_body(const In* __restrict__ x, const int64_t
       const int64_t k0 = lo + sp0 * geo.S_in - geo.J;   // buffer index of staged value 0
       __syncthreads();                                   // the previous tile's items are done
       if constexpr (STG == 8) {
-        for (int i0 = 0; i0 < geo.span; i0 += 8 * kRsmThreads) {
+        for (int i0 = 0; i0 < geo.span; i0 += 8 * NTH) {
           float v[8];
 #pragma unroll
           for (int u = 0; u < 8; ++u) {
-            const int i = i0 + u * kRsmThreads + tid;
+            const int i = i0 + u * NTH + tid;
             const int64_t k = k0 + i;
             v[u] = (i < geo.span && k >= avail_lo && k < avail_hi) ? res_sample(x, k) : 0.0f;
           }
 #pragma unroll
           for (int u = 0; u < 8; ++u) {
-            const int i = i0 + u * kRsmThreads + tid;
+            const int i = i0 + u * NTH + tid;
             if (i < geo.span) xs[i] = v[u];
           }
         }
@@ -167,18 +167,18 @@ __device__ __forceinline__ void rsm_body(const In* __restrict__ x, const int64_t
         // staged indexes [ia, ib), the rest written as zero
         const int ia = (int)min(max(avail_lo - k0, (int64_t)0), (int64_t)geo.span);
         const int ib = (int)min(max(avail_hi - k0, (int64_t)ia), (int64_t)geo.span);
-        for (int i0 = 0; i0 < geo.span; i0 += STG * kRsmThreads) {
+        for (int i0 = 0; i0 < geo.span; i0 += STG * NTH) {
           float v[STG];
 #pragma unroll
           for (int u = 0; u < STG; ++u) {
-            const int i = i0 + u * kRsmThreads + tid;
-            v[u] = (ia < ib && i0 + u * kRsmThreads < geo.span)
+            const int i = i0 + u * NTH + tid;
+            v[u] = (ia < ib && i0 + u * NTH < geo.span)
                        ? res_sample(x, k0 + min(max(i, ia), ib - 1))
                        : 0.0f;
           }
 #pragma unroll
           for (int u = 0; u < STG; ++u) {
-            const int i = i0 + u * kRsmThreads + tid;
+            const int i = i0 + u * NTH + tid;
             if (i < geo.span) xs[i] = (i >= ia && i < ib) ? v[u] : 0.0f;
           }
         }
@@ -186,7 +186,7 @@ __device__ __forceinline__ void rsm_body(const In* __restrict__ x, const int64_t
       __syncthreads();
       // items (column group, RB row blocks), the RB blocks with one read of the taps
       const int groups = geo.NT / RB;
-      for (int it = wave; it < geo.C * groups; it += kRsmThreads / 64) {
+      for (int it = wave; it < geo.C * groups; it += NTH / 64) {
         const int gm = it / groups, rg = it - gm * groups;
         const int a0 = (rg * RB * 16 + row) * geo.S_in + gbase[gm] + kk;
         const int row_stride = 16 * geo.S_in;
@@ -223,26 +223,34 @@ __device__ __forceinline__ void rsm_body(const In* __restrict__ x, const int64_t
   }
 }
 
-#define LOGMEL_RESAMPLE_KERNEL(NAME, IN, RB, STG)                                                \
-  extern "C" __global__ void __launch_bounds__(kRsmThreads)                                      \
+#define LOGMEL_RESAMPLE_KERNEL(NAME, IN, RB, STG, NTH)                                           \
+  extern "C" __global__ void __launch_bounds__(NTH)                                              \
   NAME(const IN* __restrict__ x, const int64_t* __restrict__ seg_lo,                            \
        const int64_t* __restrict__ seg_hi, const int64_t* __restrict__ nfirst,                  \
        const int64_t* __restrict__ out_off, int64_t n_segs, int64_t total_out,                  \
        float* __restrict__ y, const float* __restrict__ btab, const int* __restrict__ gbase,     \
        RsmGeometry geo) {                                                                        \
     extern __shared__ float xs[];                                                                \
-    rsm_body<RB, STG, IN>(x, seg_lo, seg_hi, nfirst, out_off, n_segs, total_out, y, btab, gbase, geo, \
+    rsm_body<RB, STG, NTH, IN>(x, seg_lo, seg_hi, nfirst, out_off, n_segs, total_out, y, btab, gbase, geo, \
                      xs);                                                                        \
   }
 
-LOGMEL_RESAMPLE_KERNEL(logmel_resample_kernel, float, 1, 8)
-LOGMEL_RESAMPLE_KERNEL(logmel_resample_i16_kernel, int16_t, 1, 8)
-LOGMEL_RESAMPLE_KERNEL(logmel_resample2_kernel, float, 2, 8)
-LOGMEL_RESAMPLE_KERNEL(logmel_resample2_i16_kernel, int16_t, 2, 8)
-LOGMEL_RESAMPLE_KERNEL(logmel_resample_wide_kernel, float, 1, 32)
-LOGMEL_RESAMPLE_KERNEL(logmel_resample_wide_i16_kernel, int16_t, 1, 32)
-LOGMEL_RESAMPLE_KERNEL(logmel_resample2_wide_kernel, float, 2, 32)
-LOGMEL_RESAMPLE_KERNEL(logmel_resample2_wide_i16_kernel, int16_t, 2, 32)
+LOGMEL_RESAMPLE_KERNEL(logmel_resample_kernel, float, 1, 8, 256)
+LOGMEL_RESAMPLE_KERNEL(logmel_resample_8w_kernel, float, 1, 8, 512)
+LOGMEL_RESAMPLE_KERNEL(logmel_resample_i16_kernel, int16_t, 1, 8, 256)
+LOGMEL_RESAMPLE_KERNEL(logmel_resample_i16_8w_kernel, int16_t, 1, 8, 512)
+LOGMEL_RESAMPLE_KERNEL(logmel_resample2_kernel, float, 2, 8, 256)
+LOGMEL_RESAMPLE_KERNEL(logmel_resample2_8w_kernel, float, 2, 8, 512)
+LOGMEL_RESAMPLE_KERNEL(logmel_resample2_i16_kernel, int16_t, 2, 8, 256)
+LOGMEL_RESAMPLE_KERNEL(logmel_resample2_i16_8w_kernel, int16_t, 2, 8, 512)
+LOGMEL_RESAMPLE_KERNEL(logmel_resample_wide_kernel, float, 1, 32, 256)
+LOGMEL_RESAMPLE_KERNEL(logmel_resample_wide_8w_kernel, float, 1, 32, 512)
+LOGMEL_RESAMPLE_KERNEL(logmel_resample_wide_i16_kernel, int16_t, 1, 32, 256)
+LOGMEL_RESAMPLE_KERNEL(logmel_resample_wide_i16_8w_kernel, int16_t, 1, 32, 512)
+LOGMEL_RESAMPLE_KERNEL(logmel_resample2_wide_kernel, float, 2, 32, 256)
+LOGMEL_RESAMPLE_KERNEL(logmel_resample2_wide_8w_kernel, float, 2, 32, 512)
+LOGMEL_RESAMPLE_KERNEL(logmel_resample2_wide_i16_kernel, int16_t, 2, 32, 256)
+LOGMEL_RESAMPLE_KERNEL(logmel_resample2_wide_i16_8w_kernel, int16_t, 2, 32, 512)
 
 }  // namespace logmel
 
@@ -256,29 +264,36 @@ hipError_t logmel_launch_resample(const void* x, int in_i16, const int64_t* seg_
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   const size_t lds = (size_t)geo.span * sizeof(float);
 #define LOGMEL_RSM(K, IN)                                                                        \
-  hipLaunchKernelGGL(logmel::K, dim3((unsigned)blocks), dim3(logmel::kRsmThreads), lds, stream,  \
+  hipLaunchKernelGGL(logmel::K, dim3((unsigned)blocks), dim3(threads), lds, stream,         \
                      static_cast<const IN*>(x), seg_lo, seg_hi, nfirst, out_off, n_segs,         \
                      total_out, y, btab, gbase, geo)
   // large spans: 32 staged samples per thread in flight, else 8 (fewer
-  // registers, more workgroups per compute unit)
-  const bool wide = geo.span >= 32 * logmel::kRsmThreads;
+  // registers, more workgroups per compute unit); 8 wavefronts per
+  // workgroup when a tile has 8 items or more, else 4
+  const bool wide = geo.span >= 32 * 256;
+  const bool w8 = (int64_t)geo.C * (geo.NT / geo.RB) >= 8;
+  const int threads = w8 ? 512 : 256;
+#define LOGMEL_RSM_PICK(K, K8, IN) \
+  if (w8) LOGMEL_RSM(K8, IN);       \
+  else LOGMEL_RSM(K, IN)
   if (geo.RB == 2) {
     if (wide) {
-      if (in_i16) LOGMEL_RSM(logmel_resample2_wide_i16_kernel, int16_t);
-      else LOGMEL_RSM(logmel_resample2_wide_kernel, float);
+      if (in_i16) { LOGMEL_RSM_PICK(logmel_resample2_wide_i16_kernel, logmel_resample2_wide_i16_8w_kernel, int16_t); }
+      else { LOGMEL_RSM_PICK(logmel_resample2_wide_kernel, logmel_resample2_wide_8w_kernel, float); }
     } else {
-      if (in_i16) LOGMEL_RSM(logmel_resample2_i16_kernel, int16_t);
-      else LOGMEL_RSM(logmel_resample2_kernel, float);
+      if (in_i16) { LOGMEL_RSM_PICK(logmel_resample2_i16_kernel, logmel_resample2_i16_8w_kernel, int16_t); }
+      else { LOGMEL_RSM_PICK(logmel_resample2_kernel, logmel_resample2_8w_kernel, float); }
     }
   } else {
     if (wide) {
-      if (in_i16) LOGMEL_RSM(logmel_resample_wide_i16_kernel, int16_t);
-      else LOGMEL_RSM(logmel_resample_wide_kernel, float);
+      if (in_i16) { LOGMEL_RSM_PICK(logmel_resample_wide_i16_kernel, logmel_resample_wide_i16_8w_kernel, int16_t); }
+      else { LOGMEL_RSM_PICK(logmel_resample_wide_kernel, logmel_resample_wide_8w_kernel, float); }
     } else {
-      if (in_i16) LOGMEL_RSM(logmel_resample_i16_kernel, int16_t);
-      else LOGMEL_RSM(logmel_resample_kernel, float);
+      if (in_i16) { LOGMEL_RSM_PICK(logmel_resample_i16_kernel, logmel_resample_i16_8w_kernel, int16_t); }
+      else { LOGMEL_RSM_PICK(logmel_resample_kernel, logmel_resample_8w_kernel, float); }
     }
   }
+#undef LOGMEL_RSM_PICK
 #undef LOGMEL_RSM
   return hipGetLastError();
 }
