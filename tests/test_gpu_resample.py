@@ -1,10 +1,13 @@
 """Resampling to 16 kHz on the GPU against the fp64 oracle.
 
-The kernel forms each output as an fp32 dot product of at most T taps
-(T = 2 ceil(H) + 1) with fp32 taps; the standard bound for such a sum is
+The kernel forms each output as an fp32 dot product of its T taps
+(T = 2 ceil(H) + 1) with fp32 taps, accumulated on the matrix cores four
+products per step in fp32 (the other products of a step have zero taps and
+add exactly nothing); the standard bound for such a sum is
 |y - y_exact| <= (T + 2) u sum_k |x_k h_k| with u = 2^-24 (taps rounded
-once, T - 1 additions and the final combination of four partial sums). The
-test allows (T + 4) u a[n], a[n] being the oracle's sum of |x_k h_k|.
+once, each product and each addition of a nonzero term rounded at most
+once). The test allows (T + 4) u a[n], a[n] being the oracle's sum of
+|x_k h_k|.
 int16 input must give the fp32 result of s / 32768 bit for bit, 16 kHz input
 must come back unchanged, and the resampled batch must feed the log-mel path
 (checked against the oracle's log-mel of the same buffer)."""
@@ -92,14 +95,17 @@ def test_resample_parity(env, rate):
 def test_resample_16k_is_identity_and_int16_bitwise(env):
     lm, plan, torch = env
     dev = torch.device("cuda", 0)
-    say("16 kHz identity; int16 == fp32 at 44.1 and 48 kHz")
+    say("16 kHz identity; int16 == fp32 at 44.1, 48, 11.025, 9.6 and 176.4 kHz")
     x, so = batch_at(16000, 7)
     r = lm.logmel_resampler_create(plan, 16000)
     y, oo = lm.resample(r, torch.from_numpy(x).to(dev), so)
     torch.cuda.synchronize()
     assert np.array_equal(oo, so)
     assert np.array_equal(y.cpu().numpy(), x)
-    for rate in (44100, 48000, 11025):
+    # every staging form and workgroup shape the kernel picks: 44.1 and 11.025 kHz
+    # wide staging, 8 wavefronts; 48 kHz narrow, 4; 9.6 kHz narrow, 8; 176.4 kHz
+    # wide, one row block per item
+    for rate in (44100, 48000, 11025, 9600, 176400):
         x, so = batch_at(rate, rate + 1)
         s16 = np.clip(np.round(x.astype(np.float64) * 32768), -32768, 32767).astype(np.int16)
         x32 = s16.astype(np.float32) / np.float32(32768.0)
