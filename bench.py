@@ -445,19 +445,25 @@ def bench_resampled(args, lm, plan, torch):
 def bench_stream(args, lm, plan, torch):
     """One step = every 30 s stream of 512 pushed through in pushes of the
     audio clock (80 ms: 375 pushes of 1280 samples; 120 ms: 250 of 1920;
-    160 ms: 187 of 2560 and one of 1280)."""
+    160 ms: 187 of 2560 and one of 1280). With --in-rate R the streams are
+    made at R Hz, pushed in pushes of the clock at R Hz, resampled on the
+    device, and each step ends with a flush."""
     import logmel_synth as S
     import numpy as np
     dev = torch.device("cuda", 0)
-    n, N = 512, 480000
-    P = args.clock_ms * FS // 1000
-    streams = S.config3_streams(device=dev)
+    rate = args.in_rate
+    n, N = 512, 30 * rate
+    P = args.clock_ms * rate // 1000
+    streams = (S.config3_streams(device=dev) if rate == FS
+               else S.config3_streams_at(rate, device=dev))
     lens = [min(P, N - a) for a in range(0, N, P)]
     pushes = len(lens)
     chunks = [streams[:, a:a + L].contiguous().reshape(-1) for a, L in zip(range(0, N, P), lens)]
-    s = lm.logmel_stream_create(plan, n, P)
+    s = lm.logmel_stream_create(plan, n, P, rate)
     pls = [np.full(n, L, dtype=np.int64) for L in lens]
-    out = torch.empty((n * (P // 160 + 1), 128), dtype=torch.float32, device=dev)
+    out = torch.empty((n * (args.clock_ms * FS // 1000 // 160 + 2), 128), dtype=torch.float32,
+                      device=dev)
+    flush_out = torch.empty((n * 4, 128), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def one_pass():
@@ -465,6 +471,9 @@ def bench_stream(args, lm, plan, torch):
         for c in range(pushes):
             fo = lm.logmel_stream_frames_for_push(s, pls[c])
             lm.logmel_stream_push(s, chunks[c], pls[c], out=out[:int(fo[-1])], stream=stream)
+        if rate != FS:
+            fo = lm.logmel_stream_frames_for_flush(s)
+            lm.logmel_stream_flush(s, out=flush_out[:int(fo[-1])], stream=stream)
 
     for _ in range(args.warmup):
         one_pass()
@@ -475,7 +484,7 @@ def bench_stream(args, lm, plan, torch):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall / args.steps * 1e3
-    audio_s = n * N / FS
+    audio_s = n * N / rate
     frames = n * 2998
     rec = {
         "metric": "audio-seconds/sec of 128-bin log-mel on 1 MI355X + % of HBM roofline",
@@ -485,8 +494,11 @@ def bench_stream(args, lm, plan, torch):
         "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f64", "data": "synthetic",
         "config": {"workload": f"streaming: 512 streams x 30 s in pushes of {P} samples "
-                               f"({args.clock_ms} ms audio clock, {pushes} pushes)",
-                   "streams": n, "pushes": pushes, "push_samples": P},
+                               f"({args.clock_ms} ms audio clock, {pushes} pushes)"
+                               + ("" if rate == FS else
+                                  f" made at {rate} Hz, resampled to 16 kHz in each push, "
+                                  "then a flush"),
+                   "streams": n, "pushes": pushes, "push_samples": P, "in_rate": rate},
         "frames_per_s": frames / (ms_per_step / 1e3),
         "push_latency_us": ms_per_step * 1e3 / pushes,
     }
@@ -558,10 +570,10 @@ def main():
     if args.counter_pass:
         counter_pass(args, lm, plan, torch)
         return
-    if args.in_rate != FS:
-        if args.workload != "c2":
-            print("bench.py: --in-rate applies to the c2 workload", file=sys.stderr)
-            sys.exit(2)
+    if args.in_rate != FS and args.workload not in ("c2", "c3"):
+        print("bench.py: --in-rate applies to the c2 and c3 workloads", file=sys.stderr)
+        sys.exit(2)
+    if args.in_rate != FS and args.workload == "c2":
         print(json.dumps(bench_resampled(args, lm, plan, torch)), flush=True)
         return
     if args.workload == "c3":

@@ -496,10 +496,11 @@ int logmel_stream_create(const logmel_plan* plan, int64_t n_streams, int64_t max
   s->max_push = max_push;
   s->stride = stride;
   const size_t meta_words = 7 * (size_t)n_streams + 1;
+  const size_t slot_words = kStreamMetaRec * (size_t)n_streams;
   bool ok = hipMalloc(&s->ws, (size_t)n_streams * stride * sizeof(float)) == hipSuccess &&
             hipMalloc(&s->meta_dev, meta_words * 8) == hipSuccess;
   for (int i = 0; ok && i < logmel_stream::kSlots; ++i)
-    ok = hipHostMalloc(&s->meta_host[i], meta_words * 8, hipHostMallocDefault) == hipSuccess &&
+    ok = hipHostMalloc(&s->meta_host[i], slot_words * 8, hipHostMallocDefault) == hipSuccess &&
          hipHostGetDevicePointer(reinterpret_cast<void**>(&s->meta_host_dev[i]), s->meta_host[i],
                                  0) == hipSuccess &&
          hipEventCreateWithFlags(&s->slot_done[i], hipEventDisableTiming) == hipSuccess;
@@ -587,7 +588,8 @@ int logmel_stream_create_ex(const logmel_plan* plan, int64_t n_streams, int64_t 
   ok = ok && hipMalloc(&s->res_buf, (size_t)n_streams * max16 * sizeof(float)) == hipSuccess &&
        hipMalloc(&s->rmeta_dev, rmeta_words * 8) == hipSuccess;
   for (int i = 0; ok && i < logmel_stream::kSlots; ++i)
-    ok = hipHostMalloc(&s->rmeta_host[i], rmeta_words * 8, hipHostMallocDefault) == hipSuccess &&
+    ok = hipHostMalloc(&s->rmeta_host[i], kRStreamMetaRec * (size_t)n_streams * 8,
+                       hipHostMallocDefault) == hipSuccess &&
          hipHostGetDevicePointer(reinterpret_cast<void**>(&s->rmeta_host_dev[i]),
                                  s->rmeta_host[i], 0) == hipSuccess &&
          hipEventCreateWithFlags(&s->rslot_done[i], hipEventDisableTiming) == hipSuccess;
@@ -658,21 +660,27 @@ int lm_push(logmel_stream* s, const void* d_new, int sample_type, const int64_t*
   // Fill the next staging slot once the push that last used it has gone up.
   const int slot = s->slot;
   if (hipEventSynchronize(s->slot_done[slot]) != hipSuccess) return LOGMEL_ERR_DEVICE;
+  // One record of kStreamMetaRec words per stream (a stream's fields in one
+  // line of the pinned slot, read by its prep workgroup in one load):
+  // carry index, carry length, offset and number of new samples, segment
+  // start and end in the workspace, frame offset after the stream.
   int64_t* m = s->meta_host[slot];
   int64_t off = 0;
-  int64_t* fo = m + 6 * n;
+  std::vector<int64_t> fo(n + 1);
   fo[0] = 0;
   for (int64_t j = 0; j < n; ++j) {
     const int64_t c = s->carry_len[j];
     const int64_t p = push_len[j];
     const int64_t base = j * s->stride;
-    m[j] = s->carry_src[j];
-    m[n + j] = c;
-    m[2 * n + j] = off;
-    m[3 * n + j] = p;
-    m[4 * n + j] = base + kRing - c;
-    m[5 * n + j] = base + kRing + p;
+    int64_t* r = m + j * kStreamMetaRec;
     fo[j + 1] = fo[j] + frames_of(c + p);
+    r[0] = s->carry_src[j];
+    r[1] = c;
+    r[2] = off;
+    r[3] = p;
+    r[4] = base + kRing - c;
+    r[5] = base + kRing + p;
+    r[6] = fo[j + 1];
     off += p;
   }
   const int64_t total_frames = fo[n];
@@ -700,19 +708,20 @@ int lm_push(logmel_stream* s, const void* d_new, int sample_type, const int64_t*
     s->seen[j] += p;
     s->emitted[j] += F;
   }
-  if (fo_out) std::memcpy(fo_out, fo, (n + 1) * sizeof(int64_t));
+  if (fo_out) std::memcpy(fo_out, fo.data(), (n + 1) * sizeof(int64_t));
   return LOGMEL_OK;
 }
 
 // The resampling part of a push (or, with flush, of the end of the
 // streams): builds each stream's segment (carry, then the new samples) in
 // the other input buffer, resamples every output the segment completes, and
-// passes those 16 kHz samples to lm_push. Meta layout (int64, n streams):
-//   [0n) carry index in the carry buffer   [1n) carry length
-//   [2n) offset of the new samples in d_new [3n) number of new samples
-//   [4n) segment start in the new buffer    [5n) buffer index of the clip's sample 0
-//   [6n) segment end                        [7n) number of the first output
-//   [8n, 9n + 1) output offsets
+// passes those 16 kHz samples to lm_push. Slot layout: one record of
+// kRStreamMetaRec int64 per stream (one line of the pinned slot):
+//   0 carry index in the carry buffer    1 carry length
+//   2 offset of the new samples in d_new  3 number of new samples
+//   4 segment start in the new buffer     5 buffer index of the clip's sample 0
+//   6 segment end                         7 number of the first output
+//   8 output offset after the stream
 int rs_push(logmel_stream* s, const void* d_new, int sample_type, const int64_t* push_len,
             void* d_out, int out_type, int64_t* fo_out, hipStream_t st, bool flush) {
   const int64_t n = s->n;
@@ -721,26 +730,26 @@ int rs_push(logmel_stream* s, const void* d_new, int sample_type, const int64_t*
   if (hipEventSynchronize(s->rslot_done[slot]) != hipSuccess) return LOGMEL_ERR_DEVICE;
   int64_t* m = s->rmeta_host[slot];
   std::vector<int64_t> k(n);
-  int64_t seg = 0, noff = 0;
-  m[8 * n] = 0;
+  int64_t seg = 0, noff = 0, total_k = 0;
   for (int64_t j = 0; j < n; ++j) {
     const int64_t c = s->rcarry_len[j];
     const int64_t p = flush ? 0 : push_len[j];
-    m[j] = s->rcarry_src[j];
-    m[n + j] = c;
-    m[2 * n + j] = noff;
-    m[3 * n + j] = p;
-    m[4 * n + j] = seg;
-    m[5 * n + j] = seg - (s->rs_in[j] - c);
-    m[6 * n + j] = seg + c + p;
-    m[7 * n + j] = s->rs_out[j];
+    int64_t* r = m + j * kRStreamMetaRec;
     k[j] = res_new_outputs(s, j, p, flush);
     if (k[j] < 0 || k[j] > s->max_push) return LOGMEL_ERR_INVALID_ARGUMENT;   // not reached
-    m[8 * n + j + 1] = m[8 * n + j] + k[j];
+    total_k += k[j];
+    r[0] = s->rcarry_src[j];
+    r[1] = c;
+    r[2] = noff;
+    r[3] = p;
+    r[4] = seg;
+    r[5] = seg - (s->rs_in[j] - c);
+    r[6] = seg + c + p;
+    r[7] = s->rs_out[j];
+    r[8] = total_k;
     seg += c + p;
     noff += p;
   }
-  const int64_t total_k = m[9 * n];
   float* src = s->in_buf[s->in_cur];
   float* dst = s->in_buf[1 - s->in_cur];
   // The prep kernel reads the slot in place and hands the resampling kernel
@@ -768,7 +777,7 @@ int rs_push(logmel_stream* s, const void* d_new, int sample_type, const int64_t*
     const int64_t kept = s->rs_in[j] - c;                // first sample in the segment
     if (a < kept) a = kept;
     if (a > n_in) a = n_in;
-    s->rcarry_src[j] = m[4 * n + j] + (a - kept);
+    s->rcarry_src[j] = m[j * kRStreamMetaRec + 4] + (a - kept);   // segment start + offset
     s->rcarry_len[j] = n_in - a;
     s->rs_in[j] = n_in;
     s->rs_out[j] = n_out;

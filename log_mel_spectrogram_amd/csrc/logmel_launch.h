@@ -29,9 +29,14 @@ hipError_t logmel_launch_chunk_pad(void* out, int out_f16, const int64_t* frame_
                                    const int64_t* chunk_off, int64_t n_clips, int64_t out_rows,
                                    hipStream_t stream);
 
+// Words per stream in a push's staging slot (one record per stream, so a
+// stream's fields share one line of the pinned slot).
+static constexpr int kStreamMetaRec = 8;
+
 // fresh: fp32, or int16 PCM (s / 32768) with in_i16. meta: the host's
-// staging slot (pinned host memory, its device-side address); the kernel
-// copies what the transform kernel reads into meta_dev.
+// staging slot (pinned host memory, its device-side address; records as in
+// logmel_stream.hip); the kernel copies what the transform kernel reads into
+// meta_dev ([4n, 7n + 1): segment starts, ends, frame offsets).
 hipError_t logmel_launch_stream_prep(float* ws, int64_t row_stride, const void* fresh, int in_i16,
                                      const int64_t* meta, int64_t* meta_dev, int64_t n_streams,
                                      hipStream_t stream);

@@ -21,10 +21,10 @@
 // Work: tiles of NT x 16 super-periods of one clip (aligned to the clip's own
 // output grid, so an output always sits at the same place of the same tile
 // whichever call forms it). The packed outputs are cut into windows of one
-// tile's size TB; workgroup b forms the tiles whose first output in the
-// call's range falls in window b (a clip's first tile at its first output,
-// the others at their start), so every tile is formed once and clips of any
-// length need no lookup table. A tile's input (zero outside the clip's
+// tile's size TB (down to TB / 8 for calls of few windows); workgroup b
+// forms the tiles whose first output in the call's range falls in window b
+// (a clip's first tile at its first output, the others at their start), so
+// every tile is formed once and clips of any length need no lookup table. A tile's input (zero outside the clip's
 // available samples) is staged in LDS, 8 samples per thread in flight, or 32
 // for spans of 8192 floats or more (the *_wide_* instances: fewer round trips
 // where the span is long, fewer registers where it is short); the 4
@@ -118,12 +118,12 @@ __device__ __forceinline__ void rsm_body(const In* __restrict__ x, const int64_t
                                          int64_t total_out, float* __restrict__ y,
                                          const float* __restrict__ btab,
                                          const int* __restrict__ gbase, const RsmGeometry geo,
-                                         float* xs) {
+                                         int64_t win, float* xs) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int64_t TB = geo.TB;
-  const int64_t w0 = (int64_t)blockIdx.x * TB, w1 = w0 + TB;
+  const int64_t w0 = (int64_t)blockIdx.x * win, w1 = w0 + win;
   if (w0 >= total_out) return;
   const int chunks = geo.KS / kRsmChunk;
   const int row = lane & 15, kk = lane >> 4;
@@ -229,10 +229,10 @@ __device__ __forceinline__ void rsm_body(const In* __restrict__ x, const int64_t
        const int64_t* __restrict__ seg_hi, const int64_t* __restrict__ nfirst,                  \
        const int64_t* __restrict__ out_off, int64_t n_segs, int64_t total_out,                  \
        float* __restrict__ y, const float* __restrict__ btab, const int* __restrict__ gbase,     \
-       RsmGeometry geo) {                                                                        \
+       RsmGeometry geo, int64_t win) {                                                           \
     extern __shared__ float xs[];                                                                \
     rsm_body<RB, STG, NTH, IN>(x, seg_lo, seg_hi, nfirst, out_off, n_segs, total_out, y, btab, gbase, geo, \
-                     xs);                                                                        \
+                     win, xs);                                                                        \
   }
 
 LOGMEL_RESAMPLE_KERNEL(logmel_resample_kernel, float, 1, 8, 256)
@@ -260,13 +260,18 @@ hipError_t logmel_launch_resample(const void* x, int in_i16, const int64_t* seg_
                                   float* y, const float* btab, const int* gbase,
                                   const RsmGeometry& geo, hipStream_t stream) {
   if (total_out <= 0 || n_segs <= 0) return hipSuccess;
-  const int64_t blocks = (total_out + geo.TB - 1) / geo.TB;
+  // windows of one tile's size; a call of few windows (a stream's push,
+  // whose segment edges cut many partial tiles) halves them, down to TB / 8,
+  // so that its tiles run in parallel workgroups
+  int64_t win = geo.TB;
+  for (int h = 0; h < 3 && win % 2 == 0 && (total_out + win - 1) / win < 2048; ++h) win /= 2;
+  const int64_t blocks = (total_out + win - 1) / win;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   const size_t lds = (size_t)geo.span * sizeof(float);
 #define LOGMEL_RSM(K, IN)                                                                        \
   hipLaunchKernelGGL(logmel::K, dim3((unsigned)blocks), dim3(threads), lds, stream,         \
                      static_cast<const IN*>(x), seg_lo, seg_hi, nfirst, out_off, n_segs,         \
-                     total_out, y, btab, gbase, geo)
+                     total_out, y, btab, gbase, geo, win)
   // large spans: 32 staged samples per thread in flight, else 8 (fewer
   // registers, more workgroups per compute unit); 8 wavefronts per
   // workgroup when a tile has 8 items or more, else 4

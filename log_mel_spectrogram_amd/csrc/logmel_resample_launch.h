@@ -34,12 +34,16 @@ hipError_t logmel_launch_resample(const void* x, int in_i16, const int64_t* seg_
                                   float* y, const float* btab, const int* gbase,
                                   const RsmGeometry& geo, hipStream_t stream);
 
+// Words per stream in a resampling push's staging slot (one 128-byte line).
+static constexpr int kRStreamMetaRec = 16;
+
 // A resampling stream's push, step 1: segment j of dst = src[carry index,
 // + carry length) followed by the new samples of stream j (fp32, or int16
-// PCM with in_i16; fresh may be null when there are none); meta as in the
-// host's rs_push: its staging slot (pinned host memory, its device-side
-// address), of which the kernel copies the resampling kernel's part into
-// meta_dev.
+// PCM with in_i16; fresh may be null when there are none); meta: the host's
+// staging slot (pinned host memory, its device-side address; records as in
+// logmel_stream.hip), of which the kernel copies the resampling kernel's
+// part into meta_dev ([5n, 9n + 1): clip origins, segment ends, first
+// outputs, output offsets).
 hipError_t logmel_launch_rstream_prep(float* dst, const float* src, const void* fresh, int in_i16,
                                       const int64_t* meta, int64_t* meta_dev, int64_t n_streams,
                                       hipStream_t stream);

@@ -20,17 +20,20 @@ __device__ __forceinline__ float stream_sample(const int16_t* p, int64_t i) {
   return (float)p[i] * (1.0f / 32768.0f);
 }
 
-// One workgroup per stream. meta (int64, n = n_streams) is the host's
-// staging slot, read by the device in place (pinned host memory):
-//   [0n, 1n)  carry source index in ws (absolute)
-//   [1n, 2n)  carry length (< 400)
-//   [2n, 3n)  offset of the stream's new samples in `fresh`
-//   [3n, 4n)  number of new samples
-//   [4n, 5n)  segment start in ws  (= row base + 400 - carry length)
-//   [5n, 6n)  segment end in ws    (= row base + 400 + new samples)
-//   [6n, 7n+1) output frame offsets
-// The kernel copies [4n, 7n + 1) into meta_dev, where the transform kernel
-// that follows reads them.
+// One workgroup per stream. meta is the host's staging slot, read by the
+// device in place (pinned host memory), one record of kStreamMetaRec int64
+// per stream, so that a workgroup's fields come in one line (n records
+// field by field would cost each workgroup a host-memory read per field):
+//   0  carry source index in ws (absolute)
+//   1  carry length (< 400)
+//   2  offset of the stream's new samples in `fresh`
+//   3  number of new samples
+//   4  segment start in ws  (= row base + 400 - carry length)
+//   5  segment end in ws    (= row base + 400 + new samples)
+//   6  output frame offset after the stream
+// The kernel copies fields 4, 5 and 6 into meta_dev ([4n, 5n), [5n, 6n),
+// [6n + 1, 7n + 1), with 0 at 6n), where the transform kernel that follows
+// reads them.
 template <typename In>
 __device__ __forceinline__ void stream_prep_body(float* __restrict__ ws, int64_t row_stride,
                                                  const In* __restrict__ fresh,
@@ -40,15 +43,16 @@ __device__ __forceinline__ void stream_prep_body(float* __restrict__ ws, int64_t
   const int64_t j = blockIdx.x;
   const int t = threadIdx.x;
   const int64_t base = j * row_stride;
-  const int64_t src = meta[j];
-  const int64_t clen = meta[n_streams + j];
-  const int64_t noff = meta[2 * n_streams + j];
-  const int64_t nlen = meta[3 * n_streams + j];
+  const int64_t* rec = meta + j * kStreamMetaRec;
+  const int64_t src = rec[0];
+  const int64_t clen = rec[1];
+  const int64_t noff = rec[2];
+  const int64_t nlen = rec[3];
   // the transform kernel's inputs: segment start and end, frame offsets
-  if (t == 0) meta_dev[4 * n_streams + j] = meta[4 * n_streams + j];
-  if (t == 1) meta_dev[5 * n_streams + j] = meta[5 * n_streams + j];
-  if (t == 2) meta_dev[6 * n_streams + j + 1] = meta[6 * n_streams + j + 1];
-  if (t == 3 && j == 0) meta_dev[6 * n_streams] = meta[6 * n_streams];
+  if (t == 0) meta_dev[4 * n_streams + j] = rec[4];
+  if (t == 1) meta_dev[5 * n_streams + j] = rec[5];
+  if (t == 2) meta_dev[6 * n_streams + j + 1] = rec[6];
+  if (t == 3 && j == 0) meta_dev[6 * n_streams] = 0;
   // The carry can overlap its destination, and the new samples land where
   // the old ones were: read the carry and the first new samples before any
   // write.
@@ -93,11 +97,13 @@ logmel_stream_prep_i16_kernel(float* __restrict__ ws, int64_t row_stride,
 // A resampling stream's push, step 1: one workgroup per stream builds its
 // segment in dst: the retained input samples (from the previous push's
 // buffer src), then the new ones (fp32, or int16 PCM as s / 32768). meta is
-// the host's staging slot (pinned host memory, read in place), layout as in
-// the host's rs_push: [0n) carry index in src, [1n) carry length, [2n)
-// offset of the new samples, [3n) their number, [4n) segment start in dst,
-// then [5n, 9n + 1) the resampling kernel's segment arrays, which the
-// kernel copies into meta_dev.
+// the host's staging slot (pinned host memory, read in place), one record of
+// kRStreamMetaRec int64 per stream (one line): 0 carry index in src,
+// 1 carry length, 2 offset of the new samples, 3 their number, 4 segment
+// start in dst, 5 buffer index of the clip's sample 0, 6 segment end,
+// 7 number of the first output, 8 output offset after the stream. The
+// kernel copies fields 5 to 8 into the resampling kernel's segment arrays in
+// meta_dev ([5n, 6n), [6n, 7n), [7n, 8n), [8n + 1, 9n + 1), with 0 at 8n).
 template <typename In>
 __device__ __forceinline__ void rstream_prep_body(float* __restrict__ dst,
                                                   const float* __restrict__ src,
@@ -107,20 +113,50 @@ __device__ __forceinline__ void rstream_prep_body(float* __restrict__ dst,
                                                   int64_t n_streams) {
   const int64_t j = blockIdx.x;
   const int t = threadIdx.x;
-  const int64_t csrc = meta[j];
-  const int64_t clen = meta[n_streams + j];
-  const int64_t noff = meta[2 * n_streams + j];
-  const int64_t nlen = meta[3 * n_streams + j];
+  const int64_t* rec = meta + j * kRStreamMetaRec;
+  const int64_t csrc = rec[0];
+  const int64_t clen = rec[1];
+  const int64_t noff = rec[2];
+  const int64_t nlen = rec[3];
   // the resampling kernel's inputs: segment origin, end, first output
   // number and output offsets
-  if (t == 0) meta_dev[5 * n_streams + j] = meta[5 * n_streams + j];
-  if (t == 1) meta_dev[6 * n_streams + j] = meta[6 * n_streams + j];
-  if (t == 2) meta_dev[7 * n_streams + j] = meta[7 * n_streams + j];
-  if (t == 3) meta_dev[8 * n_streams + j + 1] = meta[8 * n_streams + j + 1];
-  if (t == 4 && j == 0) meta_dev[8 * n_streams] = meta[8 * n_streams];
-  float* seg = dst + meta[4 * n_streams + j];
-  for (int64_t i = t; i < clen; i += 256) seg[i] = src[csrc + i];
-  for (int64_t i = t; i < nlen; i += 256) seg[clen + i] = stream_sample(fresh + noff, i);
+  if (t == 0) meta_dev[5 * n_streams + j] = rec[5];
+  if (t == 1) meta_dev[6 * n_streams + j] = rec[6];
+  if (t == 2) meta_dev[7 * n_streams + j] = rec[7];
+  if (t == 3) meta_dev[8 * n_streams + j + 1] = rec[8];
+  if (t == 4 && j == 0) meta_dev[8 * n_streams] = 0;
+  float* seg = dst + rec[4];
+  // src and dst are different buffers: eight loads per thread in flight
+  // before their stores
+  constexpr int kBatch = 8;
+  for (int64_t i0 = 0; i0 < clen; i0 += 256 * kBatch) {
+    float v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int64_t i = i0 + t + 256 * u;
+      v[u] = i < clen ? src[csrc + i] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int64_t i = i0 + t + 256 * u;
+      if (i < clen) seg[i] = v[u];
+    }
+  }
+  const In* in = fresh + noff;
+  float* row = seg + clen;
+  for (int64_t i0 = 0; i0 < nlen; i0 += 256 * kBatch) {
+    float v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int64_t i = i0 + t + 256 * u;
+      v[u] = i < nlen ? stream_sample(in, i) : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int64_t i = i0 + t + 256 * u;
+      if (i < nlen) row[i] = v[u];
+    }
+  }
 }
 
 extern "C" __global__ void __launch_bounds__(256)

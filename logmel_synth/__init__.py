@@ -287,6 +287,17 @@ def config3_streams(device="cpu", n_streams: int = 512, n_samples: int = 480000)
     return x
 
 
+def config3_streams_at(rate: int, device="cpu", n_streams: int = 512, seconds: int = 30):
+    """Config 3's streams made at another sample rate (input for resampling
+    streams): stream j = G(10000 + j, seconds * rate) at ``rate``; fp32
+    [n_streams, seconds * rate]."""
+    n = int(seconds) * int(rate)
+    x = torch.empty((n_streams, n), dtype=torch.float32, device=device)
+    for j in range(n_streams):
+        speech_like(10000 + j, n, device, out=x[j], fs=int(rate))
+    return x
+
+
 C4_MIN_LEN = 8000
 C4_MAX_LEN = 83_520_000
 
