@@ -13,6 +13,7 @@
 
 #include "logmel_launch.h"
 #include "logmel_resample_launch.h"
+#include "logmel_slots.h"
 
 namespace {
 

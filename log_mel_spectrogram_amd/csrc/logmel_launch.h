@@ -29,10 +29,6 @@ hipError_t logmel_launch_chunk_pad(void* out, int out_f16, const int64_t* frame_
                                    const int64_t* chunk_off, int64_t n_clips, int64_t out_rows,
                                    hipStream_t stream);
 
-// Words per stream in a push's staging slot (one record per stream, so a
-// stream's fields share one line of the pinned slot).
-static constexpr int kStreamMetaRec = 8;
-
 // fresh: fp32, or int16 PCM (s / 32768) with in_i16. meta: the host's
 // staging slot (pinned host memory, its device-side address; records as in
 // logmel_stream.hip); the kernel copies what the transform kernel reads into

@@ -34,9 +34,6 @@ hipError_t logmel_launch_resample(const void* x, int in_i16, const int64_t* seg_
                                   float* y, const float* btab, const int* gbase,
                                   const RsmGeometry& geo, hipStream_t stream);
 
-// Words per stream in a resampling push's staging slot (one 128-byte line).
-static constexpr int kRStreamMetaRec = 16;
-
 // A resampling stream's push, step 1: segment j of dst = src[carry index,
 // + carry length) followed by the new samples of stream j (fp32, or int16
 // PCM with in_i16; fresh may be null when there are none); meta: the host's
