@@ -105,11 +105,11 @@ struct ResGeometry {
 
 // The tile shape for NT row blocks (the other fields of k set; base_max:
 // the last column group's window offset).
-void rsm_set_tiles(RsmGeometry& k, int64_t base_max, int64_t NT) {
+void rsm_set_tiles(RsmGeometry& k, int64_t base_max, int64_t NT, bool pair_blocks = true) {
   k.NT = (int)NT;
   // two row blocks per item share one read of the taps, when that still
   // leaves an item for each of the four wavefronts
-  k.RB = NT % 2 == 0 && k.C * NT / 2 >= 4 ? 2 : 1;
+  k.RB = pair_blocks && NT % 2 == 0 && k.C * NT / 2 >= 4 ? 2 : 1;
   k.span = (int)((16 * NT - 1) * k.S_in + base_max + 4 * k.KS);
   k.TB = NT * 16 * k.S;
 }
@@ -579,13 +579,15 @@ int logmel_stream_create_ex(const logmel_plan* plan, int64_t n_streams, int64_t 
   s->in_rate = in_rate;
   s->rs = r;
   // A push forms about max_push outputs per stream, mostly in partial tiles
-  // at its segments' edges: tiles of half the offline height (when that
-  // keeps two row blocks per item) stage and work less for them (48 kHz,
-  // 80 ms pushes: 70.6 -> 61.0 us; at 44.1 kHz, 2 -> 1 row blocks cost more
-  // than they save). An output's sum is the same in either (same taps, same
-  // samples, same order of steps), so pushes still equal offline resampling.
+  // at its segments' edges: tiles of half the offline height (where the
+  // offline tiles have 4 or more row blocks) stage and work less for them
+  // (48 kHz, 80 ms pushes: 70.6 -> 61.0 us; at 44.1 kHz, 2 -> 1 row blocks
+  // cost more than they save), and one row block per item lets the kernel
+  // skip the row blocks a push does not reach. An output's sum is the same
+  // in any tile (same taps, same samples, same order of steps), so pushes
+  // still equal offline resampling.
   s->rs_k = geo.k;
-  if (geo.k.NT >= 4) rsm_set_tiles(s->rs_k, geo.gbase.back(), geo.k.NT / 2);
+  rsm_set_tiles(s->rs_k, geo.gbase.back(), geo.k.NT >= 4 ? geo.k.NT / 2 : geo.k.NT, false);
   s->in_max_push = max_push;
   s->in_stride = 2 * (int64_t)geo.J + 2 + max_push;
   if (s->in_stride > INT64_MAX / n_streams / 4) {

@@ -188,6 +188,10 @@ __device__ __forceinline__ void rsm_body(const In* __restrict__ x, const int64_t
       const int groups = geo.NT / RB;
       for (int it = wave; it < geo.C * groups; it += NTH / 64) {
         const int gm = it / groups, rg = it - gm * groups;
+        // an item with no output in the call's range (partial tiles at a
+        // segment's edges: stream pushes, clip ends) is skipped
+        const int64_t sp_lo = sp0 + (int64_t)rg * RB * 16;
+        if ((sp_lo + RB * 16) * geo.S <= nf || sp_lo * geo.S >= nf + cnt) continue;
         const int a0 = (rg * RB * 16 + row) * geo.S_in + gbase[gm] + kk;
         const int row_stride = 16 * geo.S_in;
         const float* bcol = btab + (int64_t)gm * geo.KS * 64 + lane;
