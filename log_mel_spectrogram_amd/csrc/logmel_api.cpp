@@ -101,16 +101,17 @@ struct ResGeometry {
   double fc, H;   // cutoff (Hz) and half-width (input samples)
   RsmGeometry k;  // the matrix-core kernel's geometry; k.NT == 0: unsupported
   std::vector<int> gbase;   // per column group, floor(16 g M / L)
+  std::vector<int> abase;   // its LDS offset from its super-period's first float
 };
 
-// The tile shape for NT row blocks (the other fields of k set; base_max:
-// the last column group's window offset).
-void rsm_set_tiles(RsmGeometry& k, int64_t base_max, int64_t NT, bool pair_blocks = true) {
+// The tile shape for NT row blocks (the other fields of k set; abase_max:
+// the last column group's window offset in LDS floats).
+void rsm_set_tiles(RsmGeometry& k, int64_t abase_max, int64_t NT, bool pair_blocks = true) {
   k.NT = (int)NT;
   // two row blocks per item share one read of the taps, when that still
   // leaves an item for each of the four wavefronts
   k.RB = pair_blocks && NT % 2 == 0 && k.C * NT / 2 >= 4 ? 2 : 1;
-  k.span = (int)((16 * NT - 1) * k.S_in + base_max + 4 * k.KS);
+  k.span = (int)((16 * NT - 1) * k.P + abase_max + 4 * k.KS);
   k.TB = NT * 16 * k.S;
 }
 
@@ -124,23 +125,37 @@ ResGeometry res_geometry(int32_t rate) {
   g.J = rate == 16000 ? 0 : (int)std::ceil(g.H);
   g.Tp = (2 * g.J + 1 + 15) / 16 * 16;
   RsmGeometry& k = g.k;
-  k = RsmGeometry{0, 0, 0, 0, 0, 1, g.J, 0, 0};
+  k = RsmGeometry{0, 0, 0, 0, 0, 1, g.J, 0, 0, 0};
   // super-periods of S = lcm(L, 16) outputs, S M / L input samples apart
   const int64_t S = g.L / gcd64(g.L, 16) * 16;
   const int64_t S_in = S / g.L * g.M;
   const int64_t C = S / 16;
   if (S > (1 << 20) || S_in > kRsmLdsMax) return g;   // too many phases, or too sparse
+  // staged super-periods P floats apart: with 32 | S_in the 16 rows of an
+  // MFMA operand would all start in one of the 32 banks (32, 64, 96 and
+  // 192 kHz); two zero floats after each make P = 2 mod 4, 16 distinct even
+  // banks (32 kHz 285 -> 195 us, 96 kHz 749 -> 478 us on the 64 x 30 s
+  // batch). Where 32 does not divide S_in the conflicts are milder and the
+  // pad floats' staging costs more than they save (8 kHz 83 -> 118 us).
+  const int64_t P = S_in % 32 == 0 ? S_in + 2 : S_in;
+  auto lds_of = [&](int64_t u) { return u / S_in * P + u % S_in; };
+  const int64_t T = 2 * g.J + 1;
   g.gbase.resize((size_t)C);
-  int64_t dmax = 0;
+  g.abase.resize((size_t)C);
+  int64_t t_max = 0;
   for (int64_t gm = 0; gm < C; ++gm) {
-    g.gbase[(size_t)gm] = (int)((16 * gm * g.M) / g.L);
-    const int64_t dd = ((16 * gm + 15) * g.M) / g.L - g.gbase[(size_t)gm];
-    if (dd > dmax) dmax = dd;
+    const int64_t gb = (16 * gm * g.M) / g.L;
+    const int64_t dd = ((16 * gm + 15) * g.M) / g.L - gb;
+    g.gbase[(size_t)gm] = (int)gb;
+    g.abase[(size_t)gm] = (int)lds_of(gb);
+    const int64_t t_end = lds_of(gb + dd + T - 1) + 1 - lds_of(gb);   // the group's window in LDS
+    if (t_end > t_max) t_max = t_end;
   }
-  // K / 4 MFMA steps cover 2J + 1 + dmax samples, padded to whole chunks of 8 steps
-  const int64_t KS = ((2 * g.J + 1 + dmax + 3) / 4 + 7) / 8 * 8;
-  const int64_t base_max = g.gbase.back();
-  auto span_of = [&](int64_t nt) { return (16 * nt - 1) * S_in + base_max + 4 * KS; };
+  // K / 4 MFMA steps cover every group's window (2J + 1 + its spread, plus
+  // pad floats), padded to whole chunks of 8 steps
+  const int64_t KS = ((t_max + 3) / 4 + 7) / 8 * 8;
+  const int64_t abase_max = g.abase.back();
+  auto span_of = [&](int64_t nt) { return (16 * nt - 1) * P + abase_max + 4 * KS; };
   int64_t NT = 1;
   if (span_of(1) > kRsmLdsMax) return g;
   while (NT < 8 && span_of(2 * NT) <= kRsmLdsSmall) NT *= 2;   // 1, 2, 4 or 8 row blocks
@@ -148,7 +163,8 @@ ResGeometry res_geometry(int32_t rate) {
   k.S_in = (int)S_in;
   k.C = (int)C;
   k.KS = (int)KS;
-  rsm_set_tiles(k, base_max, NT);
+  k.P = (int)P;
+  rsm_set_tiles(k, abase_max, NT);
   return g;
 }
 
@@ -180,10 +196,11 @@ std::vector<float> res_taps(int32_t rate, const ResGeometry& g) {
 }
 
 // The matrix cores' B operand, [C][KS][64]: for column group g and step s,
-// lane l holds W_g[4 s + l / 16][l % 16], where W_g[k][c] is the tap of
-// output r = 16 g + c (phase r M mod L) for sample k of the group's window,
-// i.e. its row shifted right by floor(r M / L) - floor(16 g M / L), zeros
-// elsewhere.
+// lane l holds W_g[4 s + l / 16][l % 16]. W_g[t][c] multiplies LDS float
+// abase_g + t of a row: the tap of output r = 16 g + c (phase r M mod L) for
+// the sample that float holds, i.e. the output's tap row shifted right by
+// floor(r M / L) - floor(16 g M / L) samples; zero for pad floats and for
+// samples outside the output's window.
 std::vector<float> res_btab(const ResGeometry& g, const std::vector<float>& t) {
   const RsmGeometry& k = g.k;
   const int T = 2 * g.J + 1;
@@ -193,9 +210,13 @@ std::vector<float> res_btab(const ResGeometry& g, const std::vector<float>& t) {
       const int64_t r = 16 * gm + c;
       const int64_t phi = (r * g.M) % g.L;
       const int64_t d = (r * g.M) / g.L - g.gbase[(size_t)gm];
-      for (int j = 0; j < T; ++j) {
-        const int64_t kk = d + j;   // sample of the window
-        b[(size_t)((gm * k.KS + kk / 4) * 64 + (kk % 4) * 16 + c)] = t[(size_t)(phi * g.Tp + j)];
+      for (int64_t tt = 0; tt < 4 * (int64_t)k.KS; ++tt) {
+        const int64_t a = g.abase[(size_t)gm] + tt;   // LDS float of the row
+        if (a % k.P >= k.S_in) continue;               // a pad float
+        const int64_t u = a / k.P * k.S_in + a % k.P;   // its sample, from the row's first
+        const int64_t j = u - g.gbase[(size_t)gm] - d;
+        if (j < 0 || j >= T) continue;
+        b[(size_t)((gm * k.KS + tt / 4) * 64 + (tt % 4) * 16 + c)] = t[(size_t)(phi * g.Tp + j)];
       }
     }
   return b;
@@ -212,8 +233,8 @@ struct logmel_resampler {
   const logmel_plan* plan;
   int32_t rate;
   ResGeometry geo;
-  float* btab = nullptr;   // device: the B operand [C][KS][64], then gbase [C] int32
-  int* gbase = nullptr;    // inside the btab allocation
+  float* btab = nullptr;   // device: the B operand [C][KS][64], then abase [C] int32
+  int* abase = nullptr;    // inside the btab allocation
 };
 
 struct logmel_stream {
@@ -587,7 +608,7 @@ int logmel_stream_create_ex(const logmel_plan* plan, int64_t n_streams, int64_t 
   // in any tile (same taps, same samples, same order of steps), so pushes
   // still equal offline resampling.
   s->rs_k = geo.k;
-  rsm_set_tiles(s->rs_k, geo.gbase.back(), geo.k.NT >= 4 ? geo.k.NT / 2 : geo.k.NT, false);
+  rsm_set_tiles(s->rs_k, geo.abase.back(), geo.k.NT >= 4 ? geo.k.NT / 2 : geo.k.NT, false);
   s->in_max_push = max_push;
   s->in_stride = 2 * (int64_t)geo.J + 2 + max_push;
   if (s->in_stride > INT64_MAX / n_streams / 4) {
@@ -780,7 +801,7 @@ int rs_push(logmel_stream* s, const void* d_new, int sample_type, const int64_t*
   if (total_k > 0 &&
       logmel_launch_resample(dst, 0, s->rmeta_dev + 5 * n, s->rmeta_dev + 6 * n,
                              s->rmeta_dev + 7 * n, s->rmeta_dev + 8 * n, n, total_k, s->res_buf,
-                             s->rs->btab, s->rs->gbase, s->rs_k, st) != hipSuccess)
+                             s->rs->btab, s->rs->abase, s->rs_k, st) != hipSuccess)
     return LOGMEL_ERR_DEVICE;
   const int r = lm_push(s, s->res_buf, LOGMEL_F32, k.data(), d_out, out_type, fo_out, st);
   if (r != LOGMEL_OK) return r;
@@ -959,14 +980,14 @@ int logmel_resampler_create(const logmel_plan* plan, int32_t in_rate, logmel_res
     return LOGMEL_ERR_DEVICE;
   }
   const size_t bbytes = btab.size() * sizeof(float);
-  const size_t gbytes = geo.gbase.size() * sizeof(int);
+  const size_t gbytes = geo.abase.size() * sizeof(int);
   if (hipMalloc(&r->btab, bbytes + gbytes) != hipSuccess) {
     delete r;
     return LOGMEL_ERR_OUT_OF_MEMORY;
   }
-  r->gbase = reinterpret_cast<int*>(reinterpret_cast<char*>(r->btab) + bbytes);
+  r->abase = reinterpret_cast<int*>(reinterpret_cast<char*>(r->btab) + bbytes);
   if (hipMemcpy(r->btab, btab.data(), bbytes, hipMemcpyHostToDevice) != hipSuccess ||
-      hipMemcpy(r->gbase, geo.gbase.data(), gbytes, hipMemcpyHostToDevice) != hipSuccess) {
+      hipMemcpy(r->abase, geo.abase.data(), gbytes, hipMemcpyHostToDevice) != hipSuccess) {
     (void)hipFree(r->btab);
     delete r;
     return LOGMEL_ERR_DEVICE;
@@ -1016,7 +1037,7 @@ int logmel_resample(const logmel_resampler* r, const void* d_samples, int sample
   }
   if (logmel_launch_resample(d_samples, sample_type == LOGMEL_I16, d_sample_offsets,
                              d_sample_offsets + 1, nullptr, d_out_offsets, n_clips, total_out,
-                             d_out, r->btab, r->gbase, r->geo.k, st) !=
+                             d_out, r->btab, r->abase, r->geo.k, st) !=
       hipSuccess)
     return LOGMEL_ERR_DEVICE;
   return LOGMEL_OK;

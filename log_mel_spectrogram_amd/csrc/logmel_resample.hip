@@ -117,7 +117,7 @@ __device__ __forceinline__ void rsm_body(const In* __restrict__ x, const int64_t
                                          const int64_t* __restrict__ out_off, int64_t n_segs,
                                          int64_t total_out, float* __restrict__ y,
                                          const float* __restrict__ btab,
-                                         const int* __restrict__ gbase, const RsmGeometry geo,
+                                         const int* __restrict__ abase, const RsmGeometry geo,
                                          int64_t win, float* xs) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -127,6 +127,10 @@ __device__ __forceinline__ void rsm_body(const In* __restrict__ x, const int64_t
   if (w0 >= total_out) return;
   const int chunks = geo.KS / kRsmChunk;
   const int row = lane & 15, kk = lane >> 4;
+  // staging with pad floats: this thread's first LDS float as (super-period,
+  // offset), and the step between its floats
+  const int q_tid = tid / geo.P, o_tid = tid % geo.P;
+  const int dq = NTH / geo.P, dq_o = NTH % geo.P;
 
   // every wavefront finds the segment holding output w0 (the same answer)
   for (int64_t c = wave_last_le(out_off, n_segs, w0, lane); c < n_segs; ++c) {
@@ -147,7 +151,37 @@ __device__ __forceinline__ void rsm_body(const In* __restrict__ x, const int64_t
       const int64_t sp0 = jt * geo.NT * 16;
       const int64_t k0 = lo + sp0 * geo.S_in - geo.J;   // buffer index of staged value 0
       __syncthreads();                                   // the previous tile's items are done
-      if constexpr (STG == 8) {
+      if (geo.P != geo.S_in) {
+        // LDS float i = q P + o holds the tile's sample q S_in + o (o < S_in),
+        // zero for o >= S_in and outside the available samples, which are
+        // the floats [ia, ib); thread tid takes i = tid + NTH u, its (q, o)
+        // stepping by (NTH / P, NTH % P)
+        const int pad = geo.P - geo.S_in;
+        const int64_t r_lo = max(avail_lo - k0, (int64_t)0);
+        const int64_t r_hi = max(avail_hi - k0, r_lo);
+        const int ia = (int)min(r_lo / geo.S_in * geo.P + r_lo % geo.S_in, (int64_t)geo.span);
+        const int ib = (int)min(r_hi / geo.S_in * geo.P + r_hi % geo.S_in, (int64_t)geo.span);
+        int q = q_tid, o = o_tid;
+        for (int i0 = 0; i0 < geo.span; i0 += 8 * NTH) {
+          float v[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int i = i0 + u * NTH + tid;
+            v[u] = (o < geo.S_in && i >= ia && i < ib) ? res_sample(x, k0 + (i - q * pad)) : 0.0f;
+            q += dq;
+            o += dq_o;
+            if (o >= geo.P) {
+              o -= geo.P;
+              ++q;
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int i = i0 + u * NTH + tid;
+            if (i < geo.span) xs[i] = v[u];
+          }
+        }
+      } else if constexpr (STG == 8) {
         for (int i0 = 0; i0 < geo.span; i0 += 8 * NTH) {
           float v[8];
 #pragma unroll
@@ -192,8 +226,8 @@ __device__ __forceinline__ void rsm_body(const In* __restrict__ x, const int64_t
         // segment's edges: stream pushes, clip ends) is skipped
         const int64_t sp_lo = sp0 + (int64_t)rg * RB * 16;
         if ((sp_lo + RB * 16) * geo.S <= nf || sp_lo * geo.S >= nf + cnt) continue;
-        const int a0 = (rg * RB * 16 + row) * geo.S_in + gbase[gm] + kk;
-        const int row_stride = 16 * geo.S_in;
+        const int a0 = (rg * RB * 16 + row) * geo.P + abase[gm] + kk;
+        const int row_stride = 16 * geo.P;
         const float* bcol = btab + (int64_t)gm * geo.KS * 64 + lane;
         rsm_f4 acc[RB];
 #pragma unroll
@@ -232,10 +266,10 @@ __device__ __forceinline__ void rsm_body(const In* __restrict__ x, const int64_t
   NAME(const IN* __restrict__ x, const int64_t* __restrict__ seg_lo,                            \
        const int64_t* __restrict__ seg_hi, const int64_t* __restrict__ nfirst,                  \
        const int64_t* __restrict__ out_off, int64_t n_segs, int64_t total_out,                  \
-       float* __restrict__ y, const float* __restrict__ btab, const int* __restrict__ gbase,     \
+       float* __restrict__ y, const float* __restrict__ btab, const int* __restrict__ abase,     \
        RsmGeometry geo, int64_t win) {                                                           \
     extern __shared__ float xs[];                                                                \
-    rsm_body<RB, STG, NTH, IN>(x, seg_lo, seg_hi, nfirst, out_off, n_segs, total_out, y, btab, gbase, geo, \
+    rsm_body<RB, STG, NTH, IN>(x, seg_lo, seg_hi, nfirst, out_off, n_segs, total_out, y, btab, abase, geo, \
                      win, xs);                                                                        \
   }
 
@@ -261,7 +295,7 @@ LOGMEL_RESAMPLE_KERNEL(logmel_resample2_wide_i16_8w_kernel, int16_t, 2, 32, 512)
 hipError_t logmel_launch_resample(const void* x, int in_i16, const int64_t* seg_lo,
                                   const int64_t* seg_hi, const int64_t* nfirst,
                                   const int64_t* out_off, int64_t n_segs, int64_t total_out,
-                                  float* y, const float* btab, const int* gbase,
+                                  float* y, const float* btab, const int* abase,
                                   const RsmGeometry& geo, hipStream_t stream) {
   if (total_out <= 0 || n_segs <= 0) return hipSuccess;
   // windows of one tile's size; a call of few windows (a stream's push,
@@ -275,11 +309,11 @@ hipError_t logmel_launch_resample(const void* x, int in_i16, const int64_t* seg_
 #define LOGMEL_RSM(K, IN)                                                                        \
   hipLaunchKernelGGL(logmel::K, dim3((unsigned)blocks), dim3(threads), lds, stream,         \
                      static_cast<const IN*>(x), seg_lo, seg_hi, nfirst, out_off, n_segs,         \
-                     total_out, y, btab, gbase, geo, win)
+                     total_out, y, btab, abase, geo, win)
   // large spans: 32 staged samples per thread in flight, else 8 (fewer
   // registers, more workgroups per compute unit); 8 wavefronts per
   // workgroup when a tile has 8 items or more, else 4
-  const bool wide = geo.span >= 32 * 256;
+  const bool wide = geo.P == geo.S_in && geo.span >= 32 * 256;
   const bool w8 = (int64_t)geo.C * (geo.NT / geo.RB) >= 8;
   const int threads = w8 ? 512 : 256;
 #define LOGMEL_RSM_PICK(K, K8, IN) \

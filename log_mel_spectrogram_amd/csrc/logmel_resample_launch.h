@@ -7,10 +7,13 @@
 // geometry of one input rate. Super-periods of S outputs start S_in input
 // samples apart; C column groups of 16 outputs; KS MFMA steps of 4 samples
 // per output (a multiple of 8); tiles of NT x 16 super-periods, TB outputs,
-// worked in items of RB row blocks (RB divides NT);
-// span: LDS floats one tile stages; J: the half-width in input samples.
+// worked in items of RB row blocks (RB divides NT); J: the half-width in
+// input samples. In LDS a tile's super-periods start P floats apart: P =
+// S_in, or S_in + 2 when 32 divides S_in (two zero floats after each
+// super-period's samples, so that the 16 rows of an MFMA operand start in
+// distinct banks); span: LDS floats one tile stages.
 struct RsmGeometry {
-  int S, S_in, C, KS, NT, RB, J, span;
+  int S, S_in, C, KS, NT, RB, J, span, P;
   int64_t TB;
 };
 
@@ -26,12 +29,13 @@ static constexpr int kRsmLdsSmall = 14336;
 // nfirst[i], nfirst[i] + 1, ... (nfirst null: from 0). The last segment
 // ends x. An offline batch passes its sample offsets as seg_lo and, one
 // further, as seg_hi. btab: [C][KS][64] fp32 (the B operand per column
-// group and step, in the MFMA's lane layout); gbase: [C] int32, the window
-// offset floor(16 g M / L) of column group g.
+// group and step over LDS floats, in the MFMA's lane layout); abase: [C]
+// int32, the LDS offset, from its super-period's first float, of column
+// group g's window start floor(16 g M / L).
 hipError_t logmel_launch_resample(const void* x, int in_i16, const int64_t* seg_lo,
                                   const int64_t* seg_hi, const int64_t* nfirst,
                                   const int64_t* out_off, int64_t n_segs, int64_t total_out,
-                                  float* y, const float* btab, const int* gbase,
+                                  float* y, const float* btab, const int* abase,
                                   const RsmGeometry& geo, hipStream_t stream);
 
 // A resampling stream's push, step 1: segment j of dst = src[carry index,
