@@ -25,7 +25,10 @@
 // forms the tiles whose first output in the call's range falls in window b
 // (a clip's first tile at its first output, the others at their start), so
 // every tile is formed once and clips of any length need no lookup table. A tile's input (zero outside the clip's
-// available samples) is staged in LDS, 8 samples per thread in flight, or 32
+// available samples) is staged in LDS, super-period after super-period P
+// floats apart (P = S_in, or S_in + 2 zero floats when 32 divides S_in, so
+// that the 16 rows of an operand do not all start in one bank; the taps are
+// zero at the pad floats), 8 samples per thread in flight, or 32
 // for spans of 8192 floats or more (the *_wide_* instances: fewer round trips
 // where the span is long, fewer registers where it is short); the 4
 // wavefronts (8 in the *_8w_* instances, for tiles of 8 items or more) take
