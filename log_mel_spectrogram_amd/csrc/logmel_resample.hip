@@ -24,7 +24,8 @@
 // tile's size TB (down to TB / 8 for calls of few windows); workgroup b
 // forms the tiles whose first output in the call's range falls in window b
 // (a clip's first tile at its first output, the others at their start), so
-// every tile is formed once and clips of any length need no lookup table. A tile's input (zero outside the clip's
+// every tile is formed once and clips of any length need no lookup table.
+// A tile's input (zero outside the clip's
 // available samples) is staged in LDS, super-period after super-period P
 // floats apart (P = S_in, or S_in + 2 zero floats when 32 divides S_in, so
 // that the 16 rows of an operand do not all start in one bank; the taps are
