@@ -131,10 +131,6 @@ __device__ __forceinline__ void rsm_body(const In* __restrict__ x, const int64_t
   if (w0 >= total_out) return;
   const int chunks = geo.KS / kRsmChunk;
   const int row = lane & 15, kk = lane >> 4;
-  // staging with pad floats: this thread's first LDS float as (super-period,
-  // offset), and the step between its floats
-  const int q_tid = tid / geo.P, o_tid = tid % geo.P;
-  const int dq = NTH / geo.P, dq_o = NTH % geo.P;
 
   // every wavefront finds the segment holding output w0 (the same answer)
   for (int64_t c = wave_last_le(out_off, n_segs, w0, lane); c < n_segs; ++c) {
@@ -155,7 +151,8 @@ __device__ __forceinline__ void rsm_body(const In* __restrict__ x, const int64_t
       const int64_t sp0 = jt * geo.NT * 16;
       const int64_t k0 = lo + sp0 * geo.S_in - geo.J;   // buffer index of staged value 0
       __syncthreads();                                   // the previous tile's items are done
-      if (geo.P != geo.S_in) {
+      if (STG == 8 && geo.P != geo.S_in) {
+        // (narrow instances only: padded geometries stage narrow)
         // LDS float i = q P + o holds the tile's sample q S_in + o (o < S_in),
         // zero for o >= S_in and outside the available samples, which are
         // the floats [ia, ib); thread tid takes i = tid + NTH u, its (q, o)
@@ -165,7 +162,8 @@ __device__ __forceinline__ void rsm_body(const In* __restrict__ x, const int64_t
         const int64_t r_hi = max(avail_hi - k0, r_lo);
         const int ia = (int)min(r_lo / geo.S_in * geo.P + r_lo % geo.S_in, (int64_t)geo.span);
         const int ib = (int)min(r_hi / geo.S_in * geo.P + r_hi % geo.S_in, (int64_t)geo.span);
-        int q = q_tid, o = o_tid;
+        const int dq = NTH / geo.P, dq_o = NTH % geo.P;
+        int q = tid / geo.P, o = tid % geo.P;   // this thread's first LDS float
         for (int i0 = 0; i0 < geo.span; i0 += 8 * NTH) {
           float v[8];
 #pragma unroll
