@@ -95,7 +95,7 @@ def test_resample_parity(env, rate):
 def test_resample_16k_is_identity_and_int16_bitwise(env):
     lm, plan, torch = env
     dev = torch.device("cuda", 0)
-    say("16 kHz identity; int16 == fp32 at 44.1, 48, 11.025, 9.6 and 176.4 kHz")
+    say("16 kHz identity; int16 == fp32 at 44.1, 48, 11.025, 9.6, 176.4 and 32 kHz")
     x, so = batch_at(16000, 7)
     r = lm.logmel_resampler_create(plan, 16000)
     y, oo = lm.resample(r, torch.from_numpy(x).to(dev), so)
@@ -104,8 +104,8 @@ def test_resample_16k_is_identity_and_int16_bitwise(env):
     assert np.array_equal(y.cpu().numpy(), x)
     # every staging form and workgroup shape the kernel picks: 44.1 and 11.025 kHz
     # wide staging, 8 wavefronts; 48 kHz narrow, 4; 9.6 kHz narrow, 8; 176.4 kHz
-    # wide, one row block per item
-    for rate in (44100, 48000, 11025, 9600, 176400):
+    # wide, one row block per item; 32 kHz super-periods padded with zeros
+    for rate in (44100, 48000, 11025, 9600, 176400, 32000):
         x, so = batch_at(rate, rate + 1)
         s16 = np.clip(np.round(x.astype(np.float64) * 32768), -32768, 32767).astype(np.int16)
         x32 = s16.astype(np.float32) / np.float32(32768.0)
