@@ -314,7 +314,8 @@ def resampled_streams_case(env, rate, n, seconds, seed, in_dtype="f32", out_dtyp
     return k
 
 
-@pytest.mark.parametrize("rate", [48000, 44100, 8000, 22050])
+# 96 kHz: super-periods staged with pad floats
+@pytest.mark.parametrize("rate", [48000, 44100, 8000, 22050, 96000])
 def test_resampling_streams_equal_offline(env, rate):
     say(f"resampling streams at {rate} Hz")
     pushes = resampled_streams_case(env, rate, 10, 3.0, rate)
