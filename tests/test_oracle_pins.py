@@ -589,3 +589,111 @@ def test_resample_half_gain_at_cutoff(rate):
     s = np.sin(2 * np.pi * f * n / 16000)
     A = np.hypot(np.dot(y[m], c), np.dot(y[m], s)) / (0.5 * n.size)
     assert A == pytest.approx(0.5, abs=0.01), (rate, A)
+
+
+# ------------------------------------------ packed and selected resampling
+
+RAGGED_RS = [0, 1, 37, 5000, 2, 12345, 0, 800]
+
+
+@pytest.mark.parametrize("rate", [8000, 44100, 48000, 16000])
+def test_resample_packed_equals_per_clip(rate):
+    """Clip i of a packed batch is resample_clip of that clip alone, at the
+    output rows the exclusive prefix sum of ceil(16000 N / R) gives; clips of
+    0, 1 and 37 samples among them. Catches a misplaced output offset or a
+    clip's window reading its neighbour's samples."""
+    rng = np.random.default_rng(rate + 1)
+    so = np.concatenate([[0], np.cumsum(RAGGED_RS)]).astype(np.int64)
+    s = rng.uniform(-1, 1, so[-1])
+    y, oo, a = O.resample_packed(s, so, rate)
+    assert oo[0] == 0 and y.size == a.size == oo[-1]
+    for i, n in enumerate(RAGGED_RS):
+        assert oo[i + 1] - oo[i] == -(-n * 16000 // rate)
+        yi, ai = O.resample_clip(s[so[i]:so[i + 1]], rate)
+        assert np.array_equal(y[oo[i]:oo[i + 1]], yi)
+        assert np.array_equal(a[oo[i]:oo[i + 1]], ai)
+
+
+@pytest.mark.parametrize("rate", [8000, 44100, 48000, 16000])
+def test_resample_selected_equals_packed(rate):
+    """resample_selected, which forms each output from its own window, agrees
+    with resample_packed at random rows, the first and last rows, and the
+    rows on either side of every clip boundary. Catches an off-by-one in the
+    row-to-clip lookup or in the window's clipping at a clip's ends."""
+    rng = np.random.default_rng(rate + 2)
+    so = np.concatenate([[0], np.cumsum(RAGGED_RS)]).astype(np.int64)
+    s = rng.uniform(-1, 1, so[-1])
+    y, oo, a = O.resample_packed(s, so, rate)
+    total = int(oo[-1])
+    rows = set(rng.integers(0, total, 60).tolist()) | {0, total - 1}
+    for b in oo[1:-1]:
+        rows |= {int(b) - 1, int(b)}
+    rows = np.array(sorted(r for r in rows if 0 <= r < total), dtype=np.int64)
+    ys, as_ = O.resample_selected(s, so, rate, rows)
+    # the same terms summed in another order: equal to rounding
+    assert np.allclose(ys, y[rows], rtol=0, atol=1e-13)
+    assert np.allclose(as_, a[rows], rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("rate", [11025, 44100, 48000])
+def test_resample_error_scale_brute(rate):
+    """The error scale a[n] = sum_k |x[k] h(p_n - k)| by a brute loop over
+    every sample k of the clip (not only the window the oracle visits), with
+    p_n = n R / 16000 from integer arithmetic. Catches a missing absolute
+    value, a window narrower than the kernel's support, or a wrong position.
+    Also a[n] >= |y[n]| (triangle inequality), with equality where every term
+    has one sign."""
+    rng = np.random.default_rng(rate + 3)
+    N = 300
+    x = rng.uniform(-1, 1, N)
+    y, a = O.resample_clip(x, rate)
+    for n in range(0, y.size, 7):
+        p = n * rate / 16000.0
+        acc = 0.0
+        for k in range(N):
+            acc += abs(x[k] * float(O.resample_kernel(p - k, rate)))
+        assert a[n] == pytest.approx(acc, rel=1e-12, abs=1e-15)
+    assert np.all(a >= np.abs(y) - 1e-15)
+    # a single non-zero sample: one term per output, so a = |y| exactly
+    x1 = np.zeros(N)
+    x1[150] = -0.7
+    y1, a1 = O.resample_clip(x1, rate)
+    assert np.array_equal(a1, np.abs(y1))
+
+
+def test_logmel_clip_multi_chunk():
+    """logmel_clip works through a long clip in chunks of frames, each chunk's
+    sample segment carrying the 240-sample halo its last frame needs. A clip
+    of 65,600 frames (more than one default chunk of 65,536) gives the same
+    frames with chunk 7 (thousands of boundaries), with the default chunk, and
+    frame by frame from each frame's own 400 samples (logmel_selected).
+    Catches a dropped halo (a short last frame) or a misplaced chunk start."""
+    rng = np.random.default_rng(11)
+    F = 65600
+    x = rng.uniform(-1, 1, 160 * (F - 1) + 400 + 123)
+    L1, E1 = O.logmel_clip(x)
+    assert L1.shape == (F, 128)
+    L7, E7 = O.logmel_clip(x, chunk=7)
+    # the same per-frame arithmetic; only the batch size of the library calls differs
+    assert np.allclose(E7, E1, rtol=1e-13, atol=0)
+    assert np.allclose(L7, L1, rtol=0, atol=1e-12)
+    rows = np.array([0, 6, 7, 65535, 65536, 65537, F - 1], dtype=np.int64)
+    Ls, Es = O.logmel_selected(x, [0, x.size], rows)
+    assert np.allclose(Es, E1[rows], rtol=1e-13, atol=0)
+    assert np.allclose(Ls, L1[rows], rtol=0, atol=1e-12)
+
+
+def test_nan_frame_is_nan_in_every_band():
+    """A NaN sample reaches every bin of its frame's transform, and the
+    filterbank sum of an empty filter (0 * NaN terms) is NaN too: the frames
+    whose 400 samples hold the NaN are NaN in all 128 bands, the others are
+    finite."""
+    rng = np.random.default_rng(12)
+    x = rng.uniform(-1, 1, 2000)
+    x[700] = np.nan            # frames 2, 3 and 4 hold sample 700 (160 f <= 700 < 160 f + 400)
+    L, _ = O.logmel_clip(x)
+    bad = [f for f in range(L.shape[0]) if 160 * f <= 700 < 160 * f + 400]
+    assert bad == [2, 3, 4]
+    assert np.all(np.isnan(L[bad]))
+    good = [f for f in range(L.shape[0]) if f not in bad]
+    assert np.all(np.isfinite(L[good]))
