@@ -15,16 +15,17 @@ successive steps do not hit in the 256 MB Infinity Cache.
 ``dtype`` names the arithmetic of the path: the window and the transform in fp64 (the filterbank
 and the log in fp32). ``value`` is audio-seconds per second (sum of samples / 16000 per step,
 divided by the wall time per step, measured between device synchronisations
-around exactly K steps). The kernel is bound by vector-ALU issue, so
-``roofline`` is the ALU roofline: ``achieved`` is the algorithmic flops per
-launch (FLOPS_PER_FRAME x frames) divided by the kernel's average duration
-from HIP events recorded around each launch on the stream it runs on, against
-the 78.6 TFLOP/s vector peak; ``hbm_achieved_gbs`` is the algorithmic HBM
-bytes (4 B per input sample + 512 B per output frame + the offsets) over the
-same duration, against 8 TB/s, and ``traffic`` the measured HBM bytes per
-launch from the committed counter summary. ``cpu_baseline`` times the fp64 oracle
-on the host cores over the same clips (a bounded sample: repeated passes for
-about --cpu-seconds seconds).
+around exactly K steps). ``roofline`` is the HBM roofline the target is set
+against: ``achieved`` is the algorithmic HBM bytes per launch (4 B per input
+sample + 512 B per output frame + the offsets) divided by the kernel's average
+duration from HIP events recorded around each launch on the stream it runs on,
+against 8 TB/s, and ``traffic`` the measured HBM bytes per launch from the
+committed counter summary; the vector-ALU figures (this implementation's
+algorithmic flops per launch against the 78.6 TFLOP/s vector peak) ride along
+as ``alu_*`` keys. The default run also times the ragged long batch (200
+clips, 0.5 s to 87 min) and reports it as the nested ``c4`` record.
+``cpu_baseline`` times the fp64 oracle on the host cores over the same clips
+(a bounded sample: repeated passes for about --cpu-seconds seconds).
 """
 
 import argparse
@@ -101,13 +102,24 @@ def _oracle_worker(args):
     return 0
 
 
+def host_cores():
+    """(cores to use, cores in the affinity mask). The GPU machine gives each GPU
+    a share of the host's cores and states it in OMP_NUM_THREADS (16 for one
+    GPU); the affinity mask may list more, which belong to other shares.
+    Every core of the share is used."""
+    aff = len(os.sched_getaffinity(0))
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    n = min(aff, int(share)) if share.isdigit() and int(share) > 0 else aff
+    return n, aff
+
+
 def cpu_baseline(clips, seconds):
     """fp64 oracle over the given clips (list of numpy fp32 arrays) on a
-    process pool of the host's cores (at most 16), one BLAS thread each."""
+    process pool of the host cores of this GPU's share, one BLAS thread each."""
     import multiprocessing as mp
+    cores, aff = host_cores()
     for v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
         os.environ[v] = "1"
-    cores = min(len(os.sched_getaffinity(0)), 16)
     ctx = mp.get_context("spawn")
     audio_per_pass = sum(c.size for c in clips) / FS
     with ctx.Pool(cores) as pool:
@@ -136,6 +148,7 @@ def cpu_baseline(clips, seconds):
         "value": audio_per_pass * reps / dt,
         "unit": "audio-seconds/s",
         "cores": cores,
+        "affinity_cores": aff,
         "kind": "oracle",
         "sample": f"{len(clips)} clips of the workload ({audio_per_pass:.0f} audio-s), "
                   f"{reps} passes, {dt:.1f} s wall",
@@ -296,10 +309,9 @@ def bench_offline(args, lm, plan, torch):
         "config": {"workload": desc, "clips": len(so) - 1, "samples": n_samples,
                    "frames": total, "output_rows": out_rows, "buffer_sets": n_sets},
         "frames_per_s": total / (ms_per_step / 1e3),
-        # The kernel is bound by vector-ALU issue (an fp64 transform), not by
-        # HBM: its roofline is the ALU one; the HBM figures ride along.
-        "roofline": {"bound": "alu", "achieved": achieved_tflops, "peak": ALU_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved_tflops / ALU_PEAK_TFLOPS,
+        # The HBM roofline of the target; the vector-ALU figures ride along.
+        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS,
                      "traffic": traffic,
                      "kernel": (("logmel_chunk_pad_kernel + " if chunked else "")
                                 + {(0, 0): "logmel_tiles_kernel", (1, 0): "logmel_tiles_i16_kernel",
@@ -308,10 +320,13 @@ def bench_offline(args, lm, plan, torch):
                      "kernel_avg_us": kern_avg_s * 1e6,
                      "kernel_median_us": kern_med_s * 1e6,
                      "kernel_min_us": kern_min_s * 1e6,
-                     "algorithmic_flops_per_launch": FLOPS_PER_FRAME * total,
                      "algorithmic_bytes_per_launch": algo_bytes,
                      "hbm_achieved_gbs": achieved_gbs,
                      "hbm_frac": achieved_gbs / HBM_PEAK_GBS,
+                     "alu_achieved_tflops": achieved_tflops,
+                     "alu_peak_tflops": ALU_PEAK_TFLOPS,
+                     "alu_frac": achieved_tflops / ALU_PEAK_TFLOPS,
+                     "algorithmic_flops_per_launch": FLOPS_PER_FRAME * total,
                      # a 1 GiB device-to-device copy in the same run: what a
                      # plain streaming kernel reaches here
                      "copy_gbs": copy_gbs,
@@ -423,9 +438,9 @@ def bench_resampled(args, lm, plan, torch):
     if not args.no_cpu_baseline:
         xh = x.cpu().numpy()
         clips = [xh[so[i]:so[i + 1]] for i in range(16)]
+        cores, _ = host_cores()
         for v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
             os.environ[v] = "1"
-        cores = min(len(os.sched_getaffinity(0)), 16)
         with mp.get_context("spawn").Pool(cores) as pool:
             t0 = time.perf_counter()
             pool.map(_resample_worker, [(c, rate, 1) for c in clips])
@@ -506,6 +521,25 @@ def bench_stream(args, lm, plan, torch):
     return rec, None
 
 
+def nested_c4(args, lm, plan, torch):
+    """The ragged long batch (200 clips, 0.5 s to 87 min) timed in the same
+    run as the headline: a few launches, kernel time from HIP events."""
+    import argparse as _ap
+    sub = _ap.Namespace(**vars(args))
+    sub.workload, sub.steps, sub.warmup = "c4", 5, 2
+    sub.no_cpu_baseline = True
+    r, _ = bench_offline(sub, lm, plan, torch)
+    torch.cuda.empty_cache()
+    rf = r["roofline"]
+    return {"config": r["config"], "value": r["value"], "unit": r["unit"],
+            "steps": sub.steps, "warmup": sub.warmup, "ms_per_step": r["ms_per_step"],
+            "frames_per_s": r["frames_per_s"], "kernel": rf["kernel"],
+            "kernel_avg_us": rf["kernel_avg_us"], "kernel_min_us": rf["kernel_min_us"],
+            "algorithmic_bytes_per_launch": rf["algorithmic_bytes_per_launch"],
+            "hbm_achieved_gbs": rf["hbm_achieved_gbs"], "hbm_frac": rf["hbm_frac"],
+            "traffic": rf["traffic"], "alu_frac": rf["alu_frac"]}
+
+
 def counter_pass(args, lm, plan, torch):
     """The run that hardware-counter summaries are taken over: three launches
     on the workload's buffers, then a 1 GiB fill and three 1 GiB
@@ -544,6 +578,8 @@ def main():
     ap.add_argument("--in-rate", type=int, default=16000,
                     help="make the c2 batch at this rate and resample it to 16 kHz in the step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-c4", action="store_true",
+                    help="skip the nested ragged-long-batch record of the default run")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--counter-pass", action="store_true",
                     help="run three launches and a 1 GiB copy for hardware counters; no timing")
@@ -580,6 +616,9 @@ def main():
         rec, clips = bench_stream(args, lm, plan, torch)
     else:
         rec, clips = bench_offline(args, lm, plan, torch)
+    if args.workload == "c2" and not args.no_c4 and args.layout == "frames" \
+            and args.in_dtype == "f32" and args.out_dtype == "f32":
+        rec["c4"] = nested_c4(args, lm, plan, torch)
     if clips is not None:
         rec["cpu_baseline"] = cpu_baseline(clips, args.cpu_seconds)
     else:
