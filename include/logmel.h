@@ -270,8 +270,13 @@ int logmel_stream_set_state(logmel_stream* s, const void* state_host, void* hip_
  * outputs at once over the union of their windows, with zero taps outside
  * each output's own window; an output gets the same value whichever call
  * forms it, but a non-finite sample also reaches the outputs of its group of
- * 16 whose union holds it, up to 4 ceil((2J + 1 + spread) / 4) - 2J - 1
- * samples beyond their own windows (53 at 44.1 kHz), within its clip).
+ * 16 whose staged window holds it: 4 KS positions of the staged input, KS the
+ * smallest multiple of 8 with 4 KS >= 2J + 1 plus the spread of the group's
+ * windows, so at most 4 KS - 2J - 1 positions beyond an output's own window
+ * (53 at 44.1 kHz, 73 at 48 kHz; at rates whose staged input carries two pad
+ * positions per super-period, 32, 64, 96 and 192 kHz, fewer samples), within
+ * its clip). Output offsets that overstate total_out write nothing past
+ * d_out[total_out - 1].
  * --------------------------------------------------------------------------- */
 #define LOGMEL_RESAMPLE_ZEROS 24
 

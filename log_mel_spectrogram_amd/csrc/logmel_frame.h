@@ -302,7 +302,9 @@ template <int m>
 __device__ __forceinline__ float mel_band(const float (&own)[101]) {
   constexpr int n = kMelCount[m], k0 = kMelStart[m], side = mel_side(m);
   if constexpr (n == 0) {
-    return 0.0f;
+    // An empty filter's sum of zero-weight terms: 0, or NaN where the
+    // frame's powers are NaN (a NaN sample reaches every bin).
+    return 0.0f * own[1];
   } else {
     float lo = 0.0f, hi = 0.0f;
 #pragma unroll

@@ -256,7 +256,10 @@ __device__ __forceinline__ void rsm_body(const In* __restrict__ x, const int64_t
           for (int r = 0; r < 4; ++r) {
             const int64_t sp = sp0 + (rg * RB + rb) * 16 + 4 * kk + r;
             const int64_t nn = sp * geo.S + 16 * gm + row;
-            if (nn >= nf && nn < nf + cnt) y[o_lo + (nn - nf)] = acc[rb][r];
+            // offsets that overstate the output (a precondition the device
+            // does not check) write nothing outside it
+            const int64_t o = o_lo + (nn - nf);
+            if (nn >= nf && nn < nf + cnt && o >= 0 && o < total_out) y[o] = acc[rb][r];
           }
       }
     }
