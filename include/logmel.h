@@ -250,6 +250,34 @@ int64_t logmel_stream_state_bytes(const logmel_stream* s);
 int logmel_stream_get_state(logmel_stream* s, void* state_host, void* hip_stream);
 int logmel_stream_set_state(logmel_stream* s, const void* state_host, void* hip_stream);
 
+/* Streams without a stream object, for callers that cannot allocate (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same push as logmel_stream_push (fp32 in and out, the
+ * frames bit for bit those of logmel_stream_push and of offline log-mel on
+ * the concatenated streams), with the streams' workspace in a fixed device
+ * array of the library (one per GPU, 6.2 MB, held until the process ends)
+ * and their carry counters in static host memory. The call allocates
+ * nothing, device or host.
+ *   n_streams        1..LOGMEL_STATIC_MAX_STREAMS; stream j is the same
+ *                    stream from call to call, whatever n_streams
+ *   push_len_host    n_streams new-sample counts, 0..LOGMEL_STATIC_MAX_PUSH
+ *   reset            non-zero: every stream forgets its history first
+ *   d_out, out_rows  fp32 [out_rows][128]; the push writes rows
+ *                    [0, fo[n_streams]) with fo as for logmel_stream_push
+ *                    (a push emits at most ceil(push_len / 160) frames per
+ *                    stream); INVALID_ARGUMENT if out_rows is too small
+ *   out_frame_offsets_host  optional: receives fo[0..n_streams]
+ * INPUT_TOO_LONG for more streams or samples than the limits. Calls on one
+ * GPU share its array and counters: they must not overlap (two threads, or
+ * two HIP streams in flight at once, race). The per-stream records of a push
+ * go to the device with an asynchronous host-to-device copy on hip_stream. */
+#define LOGMEL_STATIC_MAX_STREAMS 512
+#define LOGMEL_STATIC_MAX_PUSH 2560
+int logmel_stream_push_static(const logmel_plan* plan, int64_t n_streams, const float* d_new,
+                              const int64_t* push_len_host, int reset, float* d_out,
+                              int64_t out_rows, int64_t* out_frame_offsets_host,
+                              void* hip_stream);
+
 /* ---------------------------------------------------------------------------
  * Resampling to 16 kHz, the step before the front end for audio at another
  * rate. The pages require 16 kHz input (page 1, §6, the offline example in

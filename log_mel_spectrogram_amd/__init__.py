@@ -86,6 +86,8 @@ _stream_push = _sig("logmel_stream_push", ctypes.c_int, _p, _p, _i64p, _p, _i64p
 _stream_push_ex = _sig("logmel_stream_push_ex", ctypes.c_int, _p, _p, ctypes.c_int, _i64p, _p,
                        ctypes.c_int, _i64p, _p)
 _stream_counters = _sig("logmel_stream_counters", ctypes.c_int, _p, _i64, _i64p, _i64p)
+_stream_push_static = _sig("logmel_stream_push_static", ctypes.c_int, _p, _i64, _p, _i64p,
+                           ctypes.c_int, _p, _i64, _i64p, _p)
 _stream_state_bytes = _sig("logmel_stream_state_bytes", _i64, _p)
 _stream_get_state = _sig("logmel_stream_get_state", ctypes.c_int, _p, _p, _p)
 _stream_set_state = _sig("logmel_stream_set_state", ctypes.c_int, _p, _p, _p)
@@ -109,8 +111,11 @@ EXPORTED = [
     "logmel_stream_create_ex", "logmel_stream_frames_for_flush", "logmel_stream_flush", "logmel_stream_state_bytes",
     "logmel_stream_get_state", "logmel_stream_set_state", "logmel_resample_length",
     "logmel_resample_offsets", "logmel_resampler_create", "logmel_resampler_destroy",
-    "logmel_resampler_info", "logmel_resample",
+    "logmel_resampler_info", "logmel_resample", "logmel_stream_push_static",
 ]
+
+STATIC_MAX_STREAMS = 512   # LOGMEL_STATIC_MAX_STREAMS
+STATIC_MAX_PUSH = 2560     # LOGMEL_STATIC_MAX_PUSH
 
 
 class LogmelError(RuntimeError):
@@ -423,6 +428,28 @@ def logmel_stream_frames_for_push(s: Stream, push_len) -> np.ndarray:
     fo = np.zeros(s.n_streams + 1, dtype=np.int64)
     _check(_stream_frames_for_push(s.handle, _ptr64(pl), _ptr64(fo)),
            "logmel_stream_frames_for_push")
+    return fo
+
+
+def logmel_stream_push_static(plan, new_samples, push_len, out, reset=False, stream=None):
+    """Pushes fp32 samples to the first len(push_len) streams kept in the
+    library's fixed device array (no stream object, nothing allocated by the
+    call). ``out`` is a caller-provided fp32 [rows, 128] buffer with room for
+    every frame of the push (at most ceil(push_len / 160) per stream); the
+    push writes its first fo[-1] rows. Returns the frame offsets fo."""
+    torch = _torch()
+    pl = _i64_array(push_len)
+    if int(pl.sum()) != int(new_samples.numel()):
+        raise ValueError("new_samples must hold sum(push_len) samples")
+    if out.dim() != 2 or out.shape[1] != N_MELS:
+        raise ValueError(f"out must be [rows, {N_MELS}]")
+    st = _stream_handle(stream, new_samples.device)
+    fo = np.zeros(pl.size + 1, dtype=np.int64)
+    _check(_stream_push_static(plan.handle, pl.size,
+                               _dev_ptr(new_samples, torch.float32, "new_samples"), _ptr64(pl),
+                               1 if reset else 0, _dev_ptr(out, torch.float32, "out"),
+                               int(out.shape[0]), _ptr64(fo), st),
+           "logmel_stream_push_static")
     return fo
 
 

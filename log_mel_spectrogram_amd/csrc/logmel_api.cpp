@@ -866,6 +866,101 @@ int logmel_stream_flush(logmel_stream* s, void* d_out, int out_type, int64_t* fo
   return logmel_stream_reset(s);
 }
 
+// ------------------------------------------- streams in the fixed device array
+
+namespace {
+
+static_assert(kStreamMetaRec == 8, "kStaticRecBytes assumes 8 words per stream");
+static_assert(kStaticMaxStreams == LOGMEL_STATIC_MAX_STREAMS &&
+                  kStaticMaxPush == LOGMEL_STATIC_MAX_PUSH,
+              "the header states the limits of the fixed array");
+
+// Host shadow of the streams of logmel_stream_push_static, one set per
+// device, in static storage (the entry point allocates nothing): each
+// stream's carry (where it sits in its workspace row and how long it is),
+// and the records and frame offsets of the push being issued.
+struct StaticStreams {
+  int64_t carry_len[kStaticMaxStreams];
+  int64_t carry_src[kStaticMaxStreams];
+  int64_t rec[kStaticMaxStreams * kStreamMetaRec];
+  int64_t fo[kStaticMaxStreams + 1];
+};
+static StaticStreams g_static_streams[kStaticMaxDevices];
+
+}  // namespace
+
+int logmel_stream_push_static(const logmel_plan* plan, int64_t n_streams, const float* d_new,
+                              const int64_t* push_len, int reset, float* d_out, int64_t out_rows,
+                              int64_t* fo_out, void* hip_stream) {
+  if (!plan || !push_len || n_streams < 1 || out_rows < 0) return LOGMEL_ERR_INVALID_ARGUMENT;
+  if (n_streams > kStaticMaxStreams) return LOGMEL_ERR_INPUT_TOO_LONG;
+  const int dev = plan->cfg.device;
+  if (dev < 0 || dev >= kStaticMaxDevices) return LOGMEL_ERR_UNSUPPORTED;
+  int64_t fresh = 0;
+  for (int64_t j = 0; j < n_streams; ++j) {
+    if (push_len[j] < 0) return LOGMEL_ERR_INVALID_ARGUMENT;
+    if (push_len[j] > kStaticMaxPush) return LOGMEL_ERR_INPUT_TOO_LONG;
+    fresh += push_len[j];
+  }
+  if (fresh > 0 && !d_new) return LOGMEL_ERR_INVALID_ARGUMENT;
+  StaticStreams& S = g_static_streams[dev];
+  // Frame offsets of this push (a reset push starts every stream empty).
+  S.fo[0] = 0;
+  for (int64_t j = 0; j < n_streams; ++j)
+    S.fo[j + 1] = S.fo[j] + frames_of((reset ? 0 : S.carry_len[j]) + push_len[j]);
+  const int64_t total_frames = S.fo[n_streams];
+  if (total_frames > out_rows) return LOGMEL_ERR_INVALID_ARGUMENT;
+  if (total_frames > 0 && !d_out) return LOGMEL_ERR_INVALID_ARGUMENT;
+  DeviceGuard g(dev);
+  if (!g.ok) return LOGMEL_ERR_DEVICE;
+  void* scratch = nullptr;
+  if (logmel_static_scratch(dev, &scratch) != hipSuccess) return LOGMEL_ERR_DEVICE;
+  if (reset)
+    for (int64_t j = 0; j < kStaticMaxStreams; ++j) S.carry_len[j] = 0;
+  float* ws = static_cast<float*>(scratch);
+  int64_t* rec_dev = reinterpret_cast<int64_t*>(static_cast<unsigned char*>(scratch) +
+                                                kStaticWsBytes);
+  int64_t* meta_dev = reinterpret_cast<int64_t*>(static_cast<unsigned char*>(scratch) +
+                                                 kStaticWsBytes + kStaticRecBytes);
+  // One record per stream, as for a stream object's push (layout in
+  // logmel_stream.hip), copied into the array on the caller's stream.
+  int64_t off = 0;
+  for (int64_t j = 0; j < n_streams; ++j) {
+    const int64_t c = S.carry_len[j], p = push_len[j];
+    const int64_t base = j * kStaticStride;
+    int64_t* r = S.rec + j * kStreamMetaRec;
+    r[0] = c > 0 ? S.carry_src[j] : base + kRing;
+    r[1] = c;
+    r[2] = off;
+    r[3] = p;
+    r[4] = base + kRing - c;
+    r[5] = base + kRing + p;
+    r[6] = S.fo[j + 1];
+    r[7] = 0;
+    off += p;
+  }
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  if (hipMemcpyAsync(rec_dev, S.rec, (size_t)n_streams * kStreamMetaRec * 8,
+                     hipMemcpyHostToDevice, st) != hipSuccess ||
+      logmel_launch_stream_prep(ws, kStaticStride, d_new, 0, rec_dev, meta_dev, n_streams, st) !=
+          hipSuccess ||
+      logmel_launch_tiles(plan->tables, ws, 0, meta_dev + 4 * n_streams, meta_dev + 5 * n_streams,
+                          meta_dev + 6 * n_streams, n_streams, total_frames, d_out, 0,
+                          meta_dev + 6 * n_streams, 1, total_frames, plan->resident_waves, st) !=
+          hipSuccess)
+    return LOGMEL_ERR_DEVICE;
+  // Advance the host shadow.
+  for (int64_t j = 0; j < n_streams; ++j) {
+    const int64_t c = S.carry_len[j], p = push_len[j];
+    const int64_t F = frames_of(c + p);
+    const int64_t seg0 = j * kStaticStride + kRing - c;
+    S.carry_src[j] = seg0 + kHop * F;
+    S.carry_len[j] = c + p - kHop * F;
+  }
+  if (fo_out) std::memcpy(fo_out, S.fo, (n_streams + 1) * sizeof(int64_t));
+  return LOGMEL_OK;
+}
+
 int logmel_stream_counters(const logmel_stream* s, int64_t j, int64_t* seen, int64_t* emitted) {
   if (!s || j < 0 || j >= s->n) return LOGMEL_ERR_INVALID_ARGUMENT;
   if (seen) *seen = s->rs ? s->rs_in[j] : s->seen[j];

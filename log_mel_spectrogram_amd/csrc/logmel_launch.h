@@ -37,3 +37,21 @@ hipError_t logmel_launch_stream_prep(float* ws, int64_t row_stride, const void* 
                                      const int64_t* meta, int64_t* meta_dev, int64_t n_streams,
                                      hipStream_t stream);
 
+
+// The fixed device array of logmel_stream_push_static (logmel_static.hip):
+// its streams' workspace rows (kStaticStride fp32 each: 400 carry slots, then
+// up to kStaticMaxPush new samples, 256-byte aligned), then the per-stream
+// records of a push (kStaticRecBytes), then the offsets the prep kernel
+// hands the transform kernel (7 n + 1 int64).
+static constexpr int kStaticMaxDevices = 16;
+static constexpr int64_t kStaticMaxStreams = 512;
+static constexpr int64_t kStaticMaxPush = 2560;
+static constexpr int64_t kStaticStride = (400 + kStaticMaxPush + 63) / 64 * 64;
+static constexpr size_t kStaticWsBytes = (size_t)kStaticMaxStreams * kStaticStride * 4;
+static constexpr size_t kStaticRecBytes = (size_t)kStaticMaxStreams * 8 * 8;
+static constexpr size_t kStaticMetaBytes = ((7 * (size_t)kStaticMaxStreams + 1) * 8 + 255) / 256 * 256;
+static constexpr size_t kStaticScratchBytes = kStaticWsBytes + kStaticRecBytes + kStaticMetaBytes;
+
+// Device address of `device`'s copy of that array (looked up once per
+// device; the calling thread's current device must be `device`).
+hipError_t logmel_static_scratch(int device, void** ptr);
