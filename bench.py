@@ -51,7 +51,8 @@ FLOPS_PER_FRAME = 8228 + 788
 FS = 16000
 
 
-TILES_SOURCES = ("logmel_kernels.hip", "logmel_frame.h", "logmel_launch.h", "gen_tables.py")
+TILES_SOURCES = ("logmel_kernels.hip", "logmel_tile.h", "logmel_frame.h", "logmel_launch.h",
+                 "gen_tables.py")
 # the resampler's counters also depend on its geometry and taps, built in
 # the C-ABI layer
 RESAMPLE_SOURCES = ("logmel_resample.hip", "logmel_resample_launch.h", "logmel_api.cpp")
