@@ -34,7 +34,7 @@ def build(verbose: bool = False) -> str:
                            os.path.join(CSRC, "logmel_tables.h")])
     tmp = LIB + ".tmp"
     cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           os.path.join(CSRC, "logmel_kernels.hip"), os.path.join(CSRC, "logmel_quad.hip"), os.path.join(CSRC, "logmel_resample.hip"),
+           os.path.join(CSRC, "logmel_kernels.hip"), os.path.join(CSRC, "logmel_resample.hip"),
            os.path.join(CSRC, "logmel_stream.hip"),
            os.path.join(CSRC, "logmel_static.hip"),
            os.path.join(CSRC, "logmel_api.cpp"),

@@ -52,12 +52,6 @@ static const double kHostWindow[200] = {
 static const double kHostRot800[208] = {
 #include "logmel_rot800.inc"
 };
-static const double kHostQWin[200] = {
-#include "logmel_qwin.inc"
-};
-static const double kHostQRot[204] = {
-#include "logmel_qrot.inc"
-};
 
 struct logmel_plan {
   logmel_config cfg;
@@ -356,8 +350,6 @@ int logmel_plan_create(const logmel_config* cfg, logmel_plan** out) {
   double host[kTabDoubles];
   std::memcpy(host + kTabWindow, kHostWindow, sizeof(kHostWindow));
   std::memcpy(host + kTabRot800, kHostRot800, sizeof(kHostRot800));
-  std::memcpy(host + kTabQWin, kHostQWin, sizeof(kHostQWin));
-  std::memcpy(host + kTabQRot, kHostQRot, sizeof(kHostQRot));
   if (hipMalloc(&p->tables, kTabBytes) != hipSuccess) {
     delete p;
     return LOGMEL_ERR_OUT_OF_MEMORY;

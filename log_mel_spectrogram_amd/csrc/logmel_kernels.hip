@@ -455,7 +455,7 @@ logmel_chunk_pad_f16_kernel(_Float16* __restrict__ out, const int64_t* __restric
 // ---------------------------------------------------------------------------
 // Host-side launchers, called by the C-ABI layer.
 // ---------------------------------------------------------------------------
-hipError_t logmel_launch_tiles_v1(const double* tables, const void* samples, int in_i16,
+hipError_t logmel_launch_tiles(const double* tables, const void* samples, int in_i16,
                                const int64_t* seg_start, const int64_t* seg_end,
                                const int64_t* frame_off, int64_t n_clips, int64_t total_frames,
                                void* out, int out_f16, const int64_t* row_base, int64_t row_unit,

@@ -12,12 +12,7 @@
 // tile's 5360-sample span.
 static constexpr int kTabWindow = 0;
 static constexpr int kTabRot800 = 200;
-// The four-class transform's tables: the window of class c (0, 1) in
-// [c][n1][n2] order, 2 x 100, and its rotations cos, sin of
-// 2 pi (2c + 1) kappa / 800 for kappa = 0..50, [c][kappa][2].
-static constexpr int kTabQWin = 408;
-static constexpr int kTabQRot = 608;
-static constexpr int kTabDoubles = 812;
+static constexpr int kTabDoubles = 408;
 static constexpr int kTabPadFloats = 5360;
 static constexpr size_t kTabBytes = 8 * kTabDoubles + 4 * kTabPadFloats;
 
@@ -29,21 +24,6 @@ hipError_t logmel_launch_tiles(const double* tables, const void* samples, int in
                                const int64_t* frame_off, int64_t n_clips, int64_t total_frames,
                                void* out, int out_f16, const int64_t* row_base, int64_t row_unit,
                                int64_t out_rows, int resident_waves, hipStream_t stream);
-
-hipError_t logmel_launch_tiles_v1(const double* tables, const void* samples, int in_i16,
-                                  const int64_t* seg_start, const int64_t* seg_end,
-                                  const int64_t* frame_off, int64_t n_clips,
-                                  int64_t total_frames, void* out, int out_f16,
-                                  const int64_t* row_base, int64_t row_unit, int64_t out_rows,
-                                  int resident_waves, hipStream_t stream);
-
-// The same call on the four-lanes-per-frame kernel (logmel_quad.hip);
-// resident_groups: workgroups of two wavefronts resident at once.
-hipError_t logmel_launch_quad(const double* tables, const void* samples, int in_i16,
-                              const int64_t* seg_start, const int64_t* seg_end,
-                              const int64_t* frame_off, int64_t n_clips, int64_t total_frames,
-                              void* out, int out_f16, const int64_t* row_base, int64_t row_unit,
-                              int64_t out_rows, int resident_groups, hipStream_t stream);
 
 hipError_t logmel_launch_chunk_pad(void* out, int out_f16, const int64_t* frame_off,
                                    const int64_t* chunk_off, int64_t n_clips, int64_t out_rows,
