@@ -77,10 +77,12 @@ void logmel_plan_destroy(logmel_plan* plan);
  * else floor((n_samples - 400) / 160) + 1. Negative n gives 0. */
 int64_t logmel_num_frames(int64_t n_samples);
 
-/* Host helper. Clip i holds samples [sample_offsets_host[i],
- * sample_offsets_host[i+1]) of a packed buffer (n_clips + 1 non-decreasing
- * int64, first 0). Writes frame_offsets_host[0..n_clips] = exclusive prefix
- * sum of the clips' frame counts: clip i's frames are output rows
+/* Host helper (page 1, §2.3 step 1: each clip's frame count, as
+ * logmel_num_frames, summed clip by clip). Clip i holds samples
+ * [sample_offsets_host[i], sample_offsets_host[i+1]) of a packed buffer
+ * (n_clips + 1 non-decreasing int64, first 0). Writes
+ * frame_offsets_host[0..n_clips] = exclusive prefix sum of the clips' frame
+ * counts, in exact int64 arithmetic: clip i's frames are output rows
  * [frame_offsets[i], frame_offsets[i+1]). Errors: INVALID_ARGUMENT for null
  * pointers, n_clips < 0, a non-zero first offset or decreasing offsets. */
 int logmel_frame_offsets(const int64_t* sample_offsets_host, int64_t n_clips,
@@ -190,7 +192,11 @@ int logmel_stream_reset(logmel_stream* s);
 
 /* Frames each stream will emit if push_len_host[j] new samples are pushed
  * to stream j: writes out_frame_offsets_host[0..n_streams] (exclusive
- * prefix sum). Does not change the state. */
+ * prefix sum). Stream j emits logmel_num_frames(total after the push) minus
+ * the frames it has already emitted: the offline count of page 1, §2.3
+ * step 1, applied to the stream's audio so far (the pushes are the audio
+ * clock of the Audio8-ASR-Infinite page). Computed from the stream object's
+ * host-side counters; does not change the state and reads nothing back. */
 int logmel_stream_frames_for_push(const logmel_stream* s, const int64_t* push_len_host,
                                   int64_t* out_frame_offsets_host);
 
@@ -225,8 +231,8 @@ int logmel_stream_push_ex(logmel_stream* s, const void* d_new, int sample_type,
  * concatenated input followed by logmel_compute: each 16 kHz sample is
  * formed once its whole window has arrived, and the last ones (whose windows
  * reach past the input) at logmel_stream_flush. UNSUPPORTED for rates the
- * resampler does not take; snapshot and restore are UNSUPPORTED for such
- * streams. logmel_stream_counters reports input samples for them. */
+ * resampler does not take. logmel_stream_counters reports input samples for
+ * them. */
 int logmel_stream_create_ex(const logmel_plan* plan, int64_t n_streams, int64_t max_push,
                             int32_t in_rate, logmel_stream** out);
 
@@ -242,10 +248,21 @@ int logmel_stream_flush(logmel_stream* s, void* d_out, int out_type,
 int logmel_stream_counters(const logmel_stream* s, int64_t j, int64_t* samples_seen,
                            int64_t* frames_emitted);
 
-/* Snapshot / restore of all streams. State blob layout (int64 and fp32 words,
- * size from logmel_stream_state_bytes): per stream, int64 samples_seen,
- * int64 frames_emitted, int64 carry_len, then 400 fp32 carry samples (the
- * first carry_len used). get_state synchronises hip_stream. */
+/* Snapshot / restore of all streams (a stream's state is its carry and
+ * counters, so a restored stream continues bit for bit as the uninterrupted
+ * one). State blob layout (int64 and fp32 words, size from
+ * logmel_stream_state_bytes), per stream:
+ *   16 kHz streams: int64 samples_seen, int64 frames_emitted, int64
+ *     carry_len, then 400 fp32 carry samples (the first carry_len used);
+ *   streams at another input rate: int64 samples_seen (16 kHz samples),
+ *     frames_emitted, carry_len, input samples seen, 16 kHz samples formed,
+ *     input carry length, then the 400 fp32 carry words as above, then 2J
+ *     fp32 input carry samples (the first input-carry-length used; J the
+ *     resampler's half width in input samples, logmel_resampler_info).
+ * get_state and set_state synchronise hip_stream (get_state reads the
+ * carries after the pushes queued on it). set_state accepts only a state a
+ * stream of this object's kind (rate) can reach: counters and carry lengths
+ * that agree, else INVALID_ARGUMENT with nothing changed. */
 int64_t logmel_stream_state_bytes(const logmel_stream* s);
 int logmel_stream_get_state(logmel_stream* s, void* state_host, void* hip_stream);
 int logmel_stream_set_state(logmel_stream* s, const void* state_host, void* hip_stream);
@@ -345,6 +362,10 @@ int logmel_resample(const logmel_resampler* r, const void* d_samples, int sample
                     const int64_t* d_sample_offsets, const int64_t* d_out_offsets,
                     int64_t n_clips, int64_t total_out, float* d_out, void* hip_stream);
 
+/* Names a status code (a static string; "unknown status" for codes this
+ * library does not return). Every failure is an explicit negative code and
+ * over-long input is an error, never a silent truncation: the convention
+ * the transcribe.cpp Qwen3-ASR page (§四) states for its input-length limit. */
 const char* logmel_status_string(int status);
 
 /* Version of this ABI, for binding checks. */

@@ -970,25 +970,61 @@ int logmel_stream_counters(const logmel_stream* s, int64_t j, int64_t* seen, int
 
 static constexpr int64_t kStateWords = 3 * 2 + kRing;  // 3 int64 + 400 fp32, in 4-byte words
 
+namespace {
+
+// A resampling stream's record: 6 int64 (16 kHz samples seen, frames
+// emitted, 16 kHz carry length, input samples seen, 16 kHz samples formed,
+// input carry length), the 400-word 16 kHz carry, then the input carry of
+// at most 2J samples (every input sample before the next output's window has
+// been used), in 4-byte words.
+int64_t rs_state_words(const logmel_stream* s) { return 6 * 2 + kRing + 2 * (int64_t)s->rs->geo.J; }
+
+// The input carry a stream holds after rs_in input samples and rs_out
+// outputs: from the first sample of output rs_out's window on.
+int64_t rs_expected_carry(const ResGeometry& geo, int64_t rs_in, int64_t rs_out) {
+  int64_t a = (rs_out * geo.M) / geo.L - geo.J;
+  if (a < 0) a = 0;
+  if (a > rs_in) a = rs_in;
+  return rs_in - a;
+}
+
+// The 16 kHz carry after `seen` samples: from the start of the next frame on.
+int64_t expected_carry(int64_t seen) { return seen < kNFFT ? seen : seen - kHop * frames_of(seen); }
+
+}  // namespace
+
 int64_t logmel_stream_state_bytes(const logmel_stream* s) {
-  return (s && !s->rs) ? s->n * kStateWords * 4 : 0;
+  if (!s) return 0;
+  return s->n * (s->rs ? rs_state_words(s) : kStateWords) * 4;
 }
 
 int logmel_stream_get_state(logmel_stream* s, void* state_host, void* hip_stream) {
   if (!s || !state_host) return LOGMEL_ERR_INVALID_ARGUMENT;
-  if (s->rs) return LOGMEL_ERR_UNSUPPORTED;
   DeviceGuard g(s->plan->cfg.device);
   if (!g.ok) return LOGMEL_ERR_DEVICE;
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   char* b = static_cast<char*>(state_host);
+  const int64_t words = s->rs ? rs_state_words(s) : kStateWords;
+  const int64_t hdr_bytes = s->rs ? 48 : 24;
   for (int64_t j = 0; j < s->n; ++j) {
-    char* r = b + j * kStateWords * 4;
-    int64_t hdr[3] = {s->seen[j], s->emitted[j], s->carry_len[j]};
-    std::memcpy(r, hdr, sizeof(hdr));
-    std::memset(r + 24, 0, kRing * 4);
+    char* r = b + j * words * 4;
+    std::memset(r, 0, words * 4);
+    if (s->rs) {
+      const int64_t hdr[6] = {s->seen[j],  s->emitted[j], s->carry_len[j],
+                              s->rs_in[j], s->rs_out[j],  s->rcarry_len[j]};
+      std::memcpy(r, hdr, sizeof(hdr));
+    } else {
+      const int64_t hdr[3] = {s->seen[j], s->emitted[j], s->carry_len[j]};
+      std::memcpy(r, hdr, sizeof(hdr));
+    }
+    // both carries are read on hip_stream, after the pushes that wrote them
     if (s->carry_len[j] > 0 &&
-        hipMemcpyAsync(r + 24, s->ws + s->carry_src[j], s->carry_len[j] * 4,
+        hipMemcpyAsync(r + hdr_bytes, s->ws + s->carry_src[j], s->carry_len[j] * 4,
                        hipMemcpyDeviceToHost, st) != hipSuccess)
+      return LOGMEL_ERR_DEVICE;
+    if (s->rs && s->rcarry_len[j] > 0 &&
+        hipMemcpyAsync(r + hdr_bytes + kRing * 4, s->in_buf[s->in_cur] + s->rcarry_src[j],
+                       s->rcarry_len[j] * 4, hipMemcpyDeviceToHost, st) != hipSuccess)
       return LOGMEL_ERR_DEVICE;
   }
   return hipStreamSynchronize(st) == hipSuccess ? LOGMEL_OK : LOGMEL_ERR_DEVICE;
@@ -996,33 +1032,53 @@ int logmel_stream_get_state(logmel_stream* s, void* state_host, void* hip_stream
 
 int logmel_stream_set_state(logmel_stream* s, const void* state_host, void* hip_stream) {
   if (!s || !state_host) return LOGMEL_ERR_INVALID_ARGUMENT;
-  if (s->rs) return LOGMEL_ERR_UNSUPPORTED;
   const char* b = static_cast<const char*>(state_host);
+  const int64_t words = s->rs ? rs_state_words(s) : kStateWords;
+  const int64_t hdr_bytes = s->rs ? 48 : 24;
+  // The state must be one a stream can reach: carries and counters agree.
   for (int64_t j = 0; j < s->n; ++j) {
-    int64_t hdr[3];
-    std::memcpy(hdr, b + j * kStateWords * 4, sizeof(hdr));
+    int64_t hdr[6] = {0, 0, 0, 0, 0, 0};
+    std::memcpy(hdr, b + j * words * 4, hdr_bytes);
     const int64_t seen = hdr[0], emitted = hdr[1], c = hdr[2];
-    // The state must be one a stream can reach: carry and counters agree.
-    const int64_t expect_c = seen < kNFFT ? seen : seen - kHop * frames_of(seen);
-    if (seen < 0 || emitted != frames_of(seen) || c != expect_c || c < 0 || c >= kRing)
+    if (seen < 0 || emitted != frames_of(seen) || c != expected_carry(seen) || c < 0 ||
+        c >= kRing)
       return LOGMEL_ERR_INVALID_ARGUMENT;
+    if (s->rs) {
+      const int64_t rs_in = hdr[3], rs_out = hdr[4], rc = hdr[5];
+      if (rs_in < 0 || rs_in > INT64_MAX / 16000 || rs_out != res_final(s->rs->geo, rs_in) ||
+          seen != rs_out || rc != rs_expected_carry(s->rs->geo, rs_in, rs_out) ||
+          rc > 2 * (int64_t)s->rs->geo.J)
+        return LOGMEL_ERR_INVALID_ARGUMENT;
+    }
   }
   DeviceGuard g(s->plan->cfg.device);
   if (!g.ok) return LOGMEL_ERR_DEVICE;
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  int64_t rpos = 0;   // input carries, packed stream by stream in the carry buffer
   for (int64_t j = 0; j < s->n; ++j) {
-    const char* r = b + j * kStateWords * 4;
-    int64_t hdr[3];
-    std::memcpy(hdr, r, sizeof(hdr));
+    const char* r = b + j * words * 4;
+    int64_t hdr[6] = {0, 0, 0, 0, 0, 0};
+    std::memcpy(hdr, r, hdr_bytes);
     const int64_t c = hdr[2];
     const int64_t dst = j * s->stride + kRing - c;
-    if (c > 0 && hipMemcpyAsync(s->ws + dst, r + 24, c * 4, hipMemcpyHostToDevice, st) !=
+    if (c > 0 && hipMemcpyAsync(s->ws + dst, r + hdr_bytes, c * 4, hipMemcpyHostToDevice, st) !=
                      hipSuccess)
       return LOGMEL_ERR_DEVICE;
     s->seen[j] = hdr[0];
     s->emitted[j] = hdr[1];
     s->carry_len[j] = c;
     s->carry_src[j] = dst;
+    if (s->rs) {
+      const int64_t rc = hdr[5];
+      if (rc > 0 && hipMemcpyAsync(s->in_buf[s->in_cur] + rpos, r + hdr_bytes + kRing * 4,
+                                   rc * 4, hipMemcpyHostToDevice, st) != hipSuccess)
+        return LOGMEL_ERR_DEVICE;
+      s->rs_in[j] = hdr[3];
+      s->rs_out[j] = hdr[4];
+      s->rcarry_len[j] = rc;
+      s->rcarry_src[j] = rpos;
+      rpos += rc;
+    }
   }
   // The host buffer is the caller's: finish the copies before returning.
   return hipStreamSynchronize(st) == hipSuccess ? LOGMEL_OK : LOGMEL_ERR_DEVICE;

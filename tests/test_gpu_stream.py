@@ -330,11 +330,14 @@ def test_resampling_streams_int16_fp16(env):
 def test_resampling_stream_limits(env):
     lm, plan, torch = env
     s = lm.logmel_stream_create(plan, 2, 1000, in_rate=48000)
-    assert lm.logmel_stream_state_bytes(s) == 0
+    r = lm.logmel_resampler_create(plan, 48000)
+    taps = lm.logmel_resampler_info(r)[1]
+    r.close()
+    # per stream: 6 int64, 400 carry words, 2J input carry words
+    assert lm.logmel_stream_state_bytes(s) == 2 * (12 + 400 + (taps - 1)) * 4
     with pytest.raises(lm.LogmelError) as e:
         lm.logmel_stream_push(s, torch.zeros(2002, device="cuda"), [1001, 1001])
     assert e.value.status == lm.LOGMEL_ERR_INPUT_TOO_LONG
-    assert lm._stream_get_state(s.handle, lm._p(1), None) == lm.LOGMEL_ERR_UNSUPPORTED
     s.close()
     with pytest.raises(lm.LogmelError):
         lm.logmel_stream_create(plan, 2, 1000, in_rate=44101)
@@ -345,3 +348,108 @@ def test_resampling_stream_limits(env):
     assert out.shape[0] == 0 and list(f) == [0, 0, 0, 0]
     assert lm.logmel_stream_counters(s, 0) == (0, 0)
     s.close()
+
+
+def _resampling_pushes(rate, lens, seed):
+    """A fixed schedule of ragged pushes around 80 ms covering every stream."""
+    rng = np.random.default_rng(seed)
+    push = rate * 80 // 1000
+    pos = np.zeros(len(lens), dtype=np.int64)
+    sched = []
+    k = 0
+    while (pos < np.array(lens)).any():
+        pl = np.full(len(lens), push) if k % 3 else rng.integers(0, push + push // 2 + 1, len(lens))
+        pl = np.minimum(pl, np.array(lens) - pos)
+        sched.append(pl)
+        pos += pl
+        k += 1
+    return sched, push + push // 2
+
+
+def _run_resampling(lm, s, clips, sched, got, start):
+    pos = start.copy()
+    for pl in sched:
+        new = torch_cat([clips[j][pos[j]:pos[j] + pl[j]] for j in range(len(clips))])
+        out, f = lm.logmel_stream_push(s, new, pl)
+        for j in range(len(clips)):
+            if f[j + 1] > f[j]:
+                got[j].append(out[f[j]:f[j + 1]])
+        pos += pl
+    return pos
+
+
+def torch_cat(parts):
+    import torch
+    return torch.cat(parts).contiguous()
+
+
+@pytest.mark.parametrize("rate", [48000, 44100])
+def test_resampling_snapshot_restore(env, rate):
+    """A stream at another input rate: snapshot after half its pushes,
+    destroy, restore into a new object, continue and flush: bit for bit the
+    uninterrupted run, and the offline resample-then-log-mel frames. A state
+    whose counters disagree, or one of another rate, is refused."""
+    lm, plan, torch = env
+    dev = torch.device("cuda", 0)
+    say(f"resampling stream snapshot/restore at {rate} Hz")
+    rng = np.random.default_rng(rate + 7)
+    n = 6
+    lens = [int(rng.integers(rate, 3 * rate)) for _ in range(n)]
+    clips = [S.speech_like(950 + j, L, "cuda", fs=rate) for j, L in enumerate(lens)]
+    sched, max_push = _resampling_pushes(rate, lens, rate)
+    half = len(sched) // 2 + 1
+
+    def flush_into(s, got):
+        out, f = lm.logmel_stream_flush(s)
+        for j in range(n):
+            if f[j + 1] > f[j]:
+                got[j].append(out[f[j]:f[j + 1]])
+
+    a = lm.logmel_stream_create(plan, n, max_push, in_rate=rate)
+    ga = [[] for _ in range(n)]
+    _run_resampling(lm, a, clips, sched, ga, np.zeros(n, dtype=np.int64))
+    flush_into(a, ga)
+    a.close()
+
+    b = lm.logmel_stream_create(plan, n, max_push, in_rate=rate)
+    gb = [[] for _ in range(n)]
+    pos = _run_resampling(lm, b, clips, sched[:half], gb, np.zeros(n, dtype=np.int64))
+    state = lm.logmel_stream_get_state(b)
+    counters = [lm.logmel_stream_counters(b, j) for j in range(n)]
+    b.close()
+    c = lm.logmel_stream_create(plan, n, max_push, in_rate=rate)
+    # a state whose input carry length disagrees with its counters is refused
+    # and changes nothing (word 5 of stream 0's record)
+    bad = bytearray(state)
+    v = int.from_bytes(bad[40:48], "little", signed=True)
+    bad[40:48] = (v + 1).to_bytes(8, "little", signed=True)
+    with pytest.raises(lm.LogmelError) as e:
+        lm.logmel_stream_set_state(c, bytes(bad))
+    assert e.value.status == lm.LOGMEL_ERR_INVALID_ARGUMENT
+    assert lm.logmel_stream_counters(c, 0) == (0, 0)
+    lm.logmel_stream_set_state(c, state)
+    assert [lm.logmel_stream_counters(c, j) for j in range(n)] == counters
+    assert all(counters[j][0] == pos[j] for j in range(n))
+    _run_resampling(lm, c, clips, sched[half:], gb, pos)
+    flush_into(c, gb)
+    c.close()
+    torch.cuda.synchronize()
+
+    packed = torch.cat(clips).contiguous()
+    so = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    r = lm.logmel_resampler_create(plan, rate)
+    y, oo = lm.resample(r, packed, so)
+    r.close()
+    fo = lm.logmel_frame_offsets(oo)
+    ref = lm.logmel_compute(plan, y, torch.from_numpy(oo).to(dev), torch.from_numpy(fo).to(dev),
+                            int(fo[-1]))
+    for j in range(n):
+        ra, rb = torch.cat(ga[j]), torch.cat(gb[j])
+        assert torch.equal(ra, rb), (rate, j)
+        assert torch.equal(rb, ref[fo[j]:fo[j + 1]]), (rate, j)
+
+    # another rate's state does not fit this stream
+    other = lm.logmel_stream_create(plan, n, max_push, in_rate=22050 if rate != 22050 else 8000)
+    with pytest.raises((ValueError, lm.LogmelError)):
+        lm.logmel_stream_set_state(other, state)
+    other.close()
