@@ -298,6 +298,28 @@ __device__ __forceinline__ void tiles_body(const In* __restrict__ samples,
   if (role == 0) row_lds[0][fl] = cur.row;
   typename SpanOf<In>::type span;
   if (cur.fast) load_span(samples, cur.s0, lane, span);
+  {
+    // A kernel starts with its scalar cache invalidated, and the transform
+    // reads the window and the rotations through it: touch every 64-byte
+    // line of the plan's tables now, while the first span's loads are in
+    // flight, instead of missing on them one by one inside the first
+    // transform.
+    // One 4-byte load per line, in batches that are all in flight before
+    // their first use (one round trip to L2 per batch).
+    constexpr int kLines = (kTabDoubles * 8 + 63) / 64;   // 51
+    constexpr int kBatch = 13;
+    const uint32_t* tl = reinterpret_cast<const uint32_t*>(tables);
+#pragma unroll
+    for (int b = 0; b < kLines; b += kBatch) {
+      uint32_t v[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) v[i] = b + i < kLines ? tl[16 * (b + i)] : 0u;
+      uint32_t x = 0;
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) x ^= v[i];
+      asm volatile("" ::"s"(x));
+    }
+  }
 
   for (int it = 0;; ++it) {
     // Lane-derived LDS addresses are formed inside the loop: hoisted out of
