@@ -14,11 +14,12 @@
 // in fp64 and rounded once.
 //
 // Work split. fp64 doubles the registers a frame needs, so a frame takes two
-// adjacent lanes (a "pair"): role 0 transforms the even samples in order,
-// e[m] = x[2m], role 1 the odd samples in reverse order, o[m] = x[399 - 2m]
-// (decimation in time). The window is symmetric, w[399 - 2m] = w[2m], so
-// both roles apply the same window values, and every constant of the
-// routine is the same for all lanes. Each role runs the same code:
+// lanes of a wavefront, f and f + 32 (a "pair"): role 0 (lanes 0..31)
+// transforms the even samples in order, e[m] = x[2m], role 1 (lanes 32..63)
+// the odd samples in reverse order, o[m] = x[399 - 2m] (decimation in time).
+// The window is symmetric, w[399 - 2m] = w[2m], so both roles apply the same
+// window values, and every constant of the routine is the same for all
+// lanes. Each role runs the same code:
 //   * a 200-point real DFT as a prime-factor (Good-Thomas) 8 x 25 transform,
 //       m = (25 n1 + 8 n2) mod 200,  k = (25 k1 + 176 k2) mod 200,
 //     with 8 real-input 25-point DFTs (5 x 5, conjugate halves skipped)
@@ -28,10 +29,15 @@
 //     W800^k (a unit phase) gives, with u = W800^k E[k], v = W800^k R[k],
 //       |X[k]|       = |u + conj(v)|,
 //       |X[200 - k]| = |u - conj(v)|.
-//     Each role forms its own rotation (the same W800^k for both), swaps it
-//     with its partner (DPP) and forms one of the two powers, so each lane
-//     holds one half of the spectrum; the filterbank runs on the halves (see
-//     pair_logmel) and each lane logs and stores one half of the 128 bands.
+//     Every column k2 of the 8-point DFTs holds bins k <= 50 and k + 50 in
+//     pairs (bins taken as k or 200 - k, whichever is <= 100). Both roles
+//     rotate both bins of a pair (the same W800^k for both), and one
+//     v_permlane32_swap per 32-bit word exchanges the upper lanes' first bin
+//     with the lower lanes' second: afterwards lane f holds u and v of bin k
+//     and lane f + 32 those of bin k + 50, and each forms both powers of its
+//     bin. So role 0 holds bins 1..50 and 150..199, role 1 bins 51..149, and
+//     one swap word serves two bins. The filterbank runs on these halves (see
+//     pair_logmel); role 0 logs and stores bands 0..63, role 1 bands 64..127.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -167,21 +173,39 @@ __device__ __forceinline__ void dft25_real(const double (&w)[25], const double (
 __host__ __device__ constexpr int pfa_m(int n1, int n2) { return (25 * n1 + 8 * n2) % 200; }
 __host__ __device__ constexpr int pfa_k(int k1, int k2) { return (25 * k1 + 176 * k2) % 200; }
 
-// Swap a double with the pair partner (lanes 2f <-> 2f+1): DPP quad_perm [1,0,3,2].
-__device__ __forceinline__ double pair_swap(double v) {
-  const long long b = __builtin_bit_cast(long long, v);
-  // quad_perm reads a lane of the same quad for every lane, so no lane keeps
-  // an old value (bound_ctrl is irrelevant and set).
-  const int lo = __builtin_amdgcn_mov_dpp((int)b, 0xB1, 0xf, 0xf, true);
-  const int hi = __builtin_amdgcn_mov_dpp((int)(b >> 32), 0xB1, 0xf, 0xf, true);
-  return __builtin_bit_cast(double, ((long long)hi << 32) | (unsigned int)lo);
+// Exchange of the wavefront's halves: lanes 32..63 of a trade places with
+// lanes 0..31 of b (v_permlane32_swap on each 32-bit word). Afterwards a
+// holds the lower lanes' a in lanes 0..31 and their b in lanes 32..63, and b
+// holds the upper lanes' a in lanes 0..31 and their b in lanes 32..63.
+__device__ __forceinline__ void half_swap(double& a, double& b) {
+  const uint64_t ua = __builtin_bit_cast(uint64_t, a), ub = __builtin_bit_cast(uint64_t, b);
+  const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)ua, (uint32_t)ub, false, false);
+  const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(ua >> 32), (uint32_t)(ub >> 32), false, false);
+  a = __builtin_bit_cast(double, ((uint64_t)hi[0] << 32) | lo[0]);
+  b = __builtin_bit_cast(double, ((uint64_t)hi[1] << 32) | lo[1]);
 }
 
-// The value of the pair's lane `src` (0 = even, 1 = odd) in both lanes.
+// The value of the pair's lane of role `src` (0: lane f, 1: lane f + 32) in
+// both lanes of the pair.
 __device__ __forceinline__ float pair_from(float v, int src) {
-  const int b = __builtin_bit_cast(int, v);
-  return __builtin_bit_cast(float, src == 0 ? __builtin_amdgcn_mov_dpp(b, 0xA0, 0xf, 0xf, true)
-                                            : __builtin_amdgcn_mov_dpp(b, 0xF5, 0xf, 0xf, true));
+  const uint32_t b = __builtin_bit_cast(uint32_t, v);
+  const auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+  return __builtin_bit_cast(float, src == 0 ? r[0] : r[1]);
+}
+
+// Bins of column k2: kap(k1, k2) is bin k = pfa_k(k1, k2) taken as k or
+// 200 - k (whichever is <= 100), 0 where the column has no such bin
+// (k1 > 4 of column 0 repeats k1 = 3..1 conjugated; bin 0 carries no weight).
+__host__ __device__ constexpr int pfa_kap(int k1, int k2) {
+  return (k2 == 0 && k1 > 4) ? 0
+       : (pfa_k(k1, k2) <= 100 ? pfa_k(k1, k2) : 200 - pfa_k(k1, k2));
+}
+// The k1 of column k2 whose bin is kap(k1a, k2) + 50 (-1: none).
+__host__ __device__ constexpr int pfa_partner(int k1a, int k2) {
+  int r = -1;
+  for (int k1 = 0; k1 < 8; ++k1)
+    if (pfa_kap(k1a, k2) != 0 && pfa_kap(k1, k2) == pfa_kap(k1a, k2) + 50) r = k1;
+  return r;
 }
 
 // Power spectrum of one frame on a lane pair.
@@ -189,12 +213,12 @@ __device__ __forceinline__ float pair_from(float v, int src) {
 //            x[399 - 2m] for role 1
 //   win      w[2m], m = (25 n1 + 8 n2) mod 200, in [n1][n2] order (uniform)
 //   rot      cos, sin of 2 pi kap / 800 for the bins in [k2][k1] order (uniform)
-//   sgn      +1.0 for role 0, -1.0 for role 1
-//   own[101] this lane's half of the power spectrum: own[kap] = |X[kap]|^2
-//            for role 0 and |X[200 - kap]|^2 for role 1, kap = 1..100
+//   Pp, Pm   this lane's half of the power spectrum, a = 1..50:
+//            role 0: Pp[a] = |X[a]|^2,      Pm[a] = |X[200 - a]|^2
+//            role 1: Pp[a] = |X[a + 50]|^2, Pm[a] = |X[150 - a]|^2
 __device__ __forceinline__ void pair_power(const float (&v)[200], const double* __restrict__ win,
-                                           const double* __restrict__ rot, double sgn,
-                                           float (&P)[101]) {
+                                           const double* __restrict__ rot, float (&Pp)[51],
+                                           float (&Pm)[51]) {
   // Stage 1: 8 real 25-point DFTs over n2, two rows n1 per scheduling region
   // (two independent transforms give the scheduler work to overlap).
   // A[n1][k2], k2 = 0..12 (k2 = 0 is real: its .im is an exact 0).
@@ -234,10 +258,9 @@ __device__ __forceinline__ void pair_power(const float (&v)[200], const double* 
   }
 
   // Stage 2 and the combine: for each k2, an 8-point DFT over n1 gives this
-  // role's spectrum R at k = pfa_k(k1, k2) (k > 100 through conjugation);
-  // rotate, swap with the partner, and form this role's power of bin k or
-  // bin 200 - k.
-  P[0] = 0.0f;   // no filter reaches bins 0 and 200
+  // role's spectrum at k = pfa_k(k1, k2) (k > 100 through conjugation); for
+  // each pair of bins a, a + 50 of the column, rotate both, exchange halves
+  // and form the two powers of this half's bin.
 #pragma unroll
   for (int k2 = 0; k2 <= 12; ++k2) {
     cd q[8];
@@ -257,85 +280,117 @@ __device__ __forceinline__ void pair_power(const float (&v)[200], const double* 
     }
     dft8(q);
 #pragma unroll
-    for (int k1 = 0; k1 < 8; ++k1) {
-      if (k2 == 0 && k1 > 4) continue;          // conjugates of k1 = 1..3
-      const int k = pfa_k(k1, k2);
-      const int kap = k <= 100 ? k : 200 - k;
-      if (kap == 0) continue;                   // bins 0 and 200 carry no weight
-      const cd r = k <= 100 ? q[k1] : cd{q[k1].re, -q[k1].im};
-      // r * W800^kap, the same rotation in both roles
-      const cd u = c_twiddle(r, rc[k1], rs[k1]);
-      const cd w = {pair_swap(u.re), pair_swap(u.im)};
-      // role 0: |u + conj(w)|^2 = bin kap; role 1: |u - conj(w)|^2 = bin 200 - kap
-      const double are = w.re * sgn + u.re, aim = u.im - w.im * sgn;
-      P[kap] = (float)(are * are + aim * aim);
+    for (int ka = 0; ka < 8; ++ka) {
+      const int a = pfa_kap(ka, k2), kb = pfa_partner(ka, k2);
+      if (a == 0 || a > 50 || kb < 0) continue;
+      // this role's spectrum at bins a and a + 50, times W800^kap
+      const cd ra = pfa_k(ka, k2) <= 100 ? q[ka] : cd{q[ka].re, -q[ka].im};
+      const cd rb = pfa_k(kb, k2) <= 100 ? q[kb] : cd{q[kb].re, -q[kb].im};
+      cd u = c_twiddle(ra, rc[ka], rs[ka]);
+      cd w = c_twiddle(rb, rc[kb], rs[kb]);
+      // u := role 0's value, w := role 1's value, of bin a in the lower
+      // lanes and of bin a + 50 in the upper ones
+      half_swap(u.re, w.re);
+      half_swap(u.im, w.im);
+      const double pre = u.re + w.re, pim = u.im - w.im;   // u + conj(w)
+      const double mre = u.re - w.re, mim = u.im + w.im;   // u - conj(w)
+      Pp[a] = (float)(pre * pre + pim * pim);
+      Pm[a] = (float)(mre * mre + mim * mim);
     }
     // one scheduling region per column
 #pragma unroll
-    for (int k1 = 0; k1 < 8; ++k1) {
-      if (k2 == 0 && k1 > 4) continue;
-      const int k = pfa_k(k1, k2);
-      const int kap = k <= 100 ? k : 200 - k;
-      if (kap == 0) continue;
-      fence(P[kap]);
+    for (int ka = 0; ka < 8; ++ka) {
+      const int a = pfa_kap(ka, k2);
+      if (a == 0 || a > 50 || pfa_partner(ka, k2) < 0) continue;
+      fence(Pp[a]);
+      fence(Pm[a]);
     }
   }
 
 }
 
-// Band-sparse mel projection and log. Each lane holds only its own half of
-// the spectrum (own[kap]: bin kap in role 0, bin 200 - kap in role 1), and
-// both run the same code: a band whose bins all lie below 100 is summed over
-// own[bin] (right in role 0), a band whose bins all lie above 100 over
-// own[200 - bin] (right in role 1), and the bands around bin 100 as the two
-// partial sums. Role 0 logs bands 0..63, all below bin 100; role 1 logs bands
-// 64..127 and takes the energies that only role 0 holds from its partner
-// (DPP). The log has the 1e-10 floor; the floor test keeps a NaN energy NaN.
-__host__ __device__ constexpr int mel_side(int m) {   // 0: bins < 100, 1: bins > 100, 2: both
-  return kMelCount[m] == 0 ? 0
-       : (kMelStart[m] + kMelCount[m] - 1 < 100 ? 0 : (kMelStart[m] > 100 ? 1 : 2));
+// Band-sparse mel projection and log. Role 0 holds the powers of bins 1..50
+// and 150..199, role 1 those of bins 51..149 (see pair_power), and both run
+// the same code: every band is summed over this lane's registers, which
+// gives the right sum in the half that holds the band's bins (a band whose
+// bins lie in both halves is the sum of two partial sums). Bands 0..63 lie in
+// role 0's half, and role 0 logs them; role 1 logs bands 64..127 and takes
+// the sums that only role 0 holds from its partner (v_permlane32_swap). The
+// log has the 1e-10 floor; the floor test keeps a NaN energy NaN.
+
+// Half of the pair that holds bin b (1..199): 0 for bins 1..50 and
+// 150..199, 1 for bins 51..149.
+__host__ __device__ constexpr int bin_half(int b) { return (b >= 51 && b <= 149) ? 1 : 0; }
+
+// Where band m's bins lie: 0 all in role 0's half, 1 all in role 1's, 2 in
+// both, -1 no bins.
+__host__ __device__ constexpr int mel_side(int m) {
+  int in0 = 0, in1 = 0;
+  for (int j = 0; j < kMelCount[m]; ++j) {
+    if (bin_half(kMelStart[m] + j)) in1 = 1; else in0 = 1;
+  }
+  return (in0 && in1) ? 2 : (in1 ? 1 : (in0 ? 0 : -1));
+}
+// First tap of band m whose bin lies in half h (-1: none).
+__host__ __device__ constexpr int mel_first_tap(int m, int h) {
+  int r = -1;
+  for (int j = kMelCount[m] - 1; j >= 0; --j)
+    if (bin_half(kMelStart[m] + j) == h) r = j;
+  return r;
+}
+__host__ __device__ constexpr bool mel_layout_ok() {
+  for (int m = 0; m < 128; ++m) {
+    if (kMelCount[m] > 0 && (kMelStart[m] < 1 || kMelStart[m] + kMelCount[m] - 1 > 199))
+      return false;                     // bins 0 and 200 have no register
+    if (m < 64 && mel_side(m) > 0) return false;   // role 0 logs bands 0..63 alone
+  }
+  return true;
+}
+static_assert(mel_layout_ok(), "mel bands do not fit the lane-pair layout");
+
+// Power of bin b (1..199) in this lane's registers (right in half bin_half(b)).
+__device__ __forceinline__ float bin_power(const float (&Pp)[51], const float (&Pm)[51], int b) {
+  return b <= 50 ? Pp[b] : (b <= 100 ? Pp[b - 50] : (b <= 149 ? Pm[150 - b] : Pm[200 - b]));
 }
 
-// Energy of band m from this lane's half spectrum (bins in order, one
-// instance per band so that every index and weight is a constant).
+// Energy of band m as the role that logs it needs it (one instance per band,
+// so that every index and weight is a constant).
 template <int m>
-__device__ __forceinline__ float mel_band(const float (&own)[101]) {
+__device__ __forceinline__ float mel_band(const float (&Pp)[51], const float (&Pm)[51]) {
   constexpr int n = kMelCount[m], k0 = kMelStart[m], side = mel_side(m);
   if constexpr (n == 0) {
     // An empty filter's sum of zero-weight terms: 0, or NaN where the
     // frame's powers are NaN (a NaN sample reaches every bin).
-    return 0.0f * own[1];
+    return 0.0f * Pp[1];
   } else {
-    float lo = 0.0f, hi = 0.0f;
+    constexpr int f0 = mel_first_tap(m, 0), f1 = mel_first_tap(m, 1);
+    float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
     for (int j = 0; j < n; ++j) {
-      const int bin = k0 + j;
-      if (bin <= 100) {
-        lo = (bin == k0) ? kMelW[m][j] * own[bin] : lo + kMelW[m][j] * own[bin];
-      } else {
-        hi = (bin == k0 || bin == 101) ? kMelW[m][j] * own[200 - bin]
-                                       : hi + kMelW[m][j] * own[200 - bin];
-      }
+      const float t = kMelW[m][j] * bin_power(Pp, Pm, k0 + j);
+      if (bin_half(k0 + j) == 0) s0 = (j == f0) ? t : s0 + t;
+      else s1 = (j == f1) ? t : s1 + t;
     }
     if constexpr (side == 0) {
-      return m < 64 ? lo : pair_from(lo, 0);
+      return m < 64 ? s0 : pair_from(s0, 0);
     } else if constexpr (side == 1) {
-      return hi;
+      return s1;
     } else {
-      return pair_from(lo, 0) + hi;
+      return pair_from(s0, 0) + s1;
     }
   }
 }
 
 template <int... M>
-__device__ __forceinline__ void mel_bands(const float (&own)[101], float (&E)[128],
-                                          std::integer_sequence<int, M...>) {
-  ((E[M] = mel_band<M>(own)), ...);
+__device__ __forceinline__ void mel_bands(const float (&Pp)[51], const float (&Pm)[51],
+                                          float (&E)[128], std::integer_sequence<int, M...>) {
+  ((E[M] = mel_band<M>(Pp, Pm)), ...);
 }
 
-__device__ __forceinline__ void pair_logmel(const float (&own)[101], int role, float (&out)[64]) {
+__device__ __forceinline__ void pair_logmel(const float (&Pp)[51], const float (&Pm)[51], int role,
+                                            float (&out)[64]) {
   float E[128];
-  mel_bands(own, E, std::make_integer_sequence<int, 128>{});
+  mel_bands(Pp, Pm, E, std::make_integer_sequence<int, 128>{});
 #pragma unroll
   for (int i = 0; i < 64; ++i) {
     float e = role ? E[64 + i] : E[i];

@@ -5,8 +5,8 @@
 //   and logmel_tiles_i16_f16out_kernel are the same code for int16 PCM
 //   input and fp16 output).
 //   The flattened frame space [0, total_frames) is cut into tiles of 32
-//   consecutive frames, one frame per lane pair (role 0: even samples, role
-//   1: odd samples; see logmel_frame.h). A persistent grid of one wavefront
+//   consecutive frames, one frame per lane pair f, f + 32 (role 0: even
+//   samples, role 1: odd samples; see logmel_frame.h). A persistent grid of one wavefront
 //   per SIMD walks the tiles, each wavefront a contiguous run of them; a
 //   wavefront locates and loads its next tile while it finishes the current
 //   one. A tile may straddle clips: each pair
@@ -41,8 +41,8 @@ namespace logmel {
 // 84 and the 16-byte reads of the 32 frames fall on distinct bank groups.
 // The even sequence holds sample 2i of the span in order; the odd one holds
 // sample 2i + 1 in reverse order (value i is sample 5359 - 2i), which is the
-// order the odd lane of a pair consumes: frame f's even values start at
-// 84 f, its reversed odd values at 84 (31 - f).
+// order role 1 of a pair consumes: frame f's even values start at 84 f, its
+// reversed odd values at 84 (31 - f).
 static constexpr int kSpan = (kTile - 1) * 160 + 400;
 static constexpr int kSpanGroups = kSpan / 4;
 static constexpr int kParityLen = 2812;   // last element 2679 sits at 2811
@@ -185,7 +185,7 @@ __device__ __forceinline__ void pieces_to_lds(const In* __restrict__ samples, co
   // piece they give the following frames' own slots).
   if (ln <= kPieceT) slots[ln].lim = 0;
   lds_barrier();
-  const bool w = !(ln & 1) && t.valid;
+  const bool w = ln < 32 && t.valid;
   if (w) slots[sigma + 2] = PieceSlot{t.s + 320, 80, 0};
   lds_barrier();
   if (w) slots[sigma + 1] = PieceSlot{t.s + 160, 160, 0};
@@ -278,8 +278,8 @@ __device__ __forceinline__ void tiles_body(const In* __restrict__ samples,
   const RowMap rows{row_base, row_unit};
   const int lane = threadIdx.x;
   __builtin_assume(lane < kWaveLanes);
-  const int role = lane & 1;
-  const int fl = lane >> 1;
+  const int role = lane >> 5;
+  const int fl = lane & 31;
   const int64_t n_tiles = (total_frames + kTile - 1) / kTile;
 
   // Wavefront w takes a contiguous run of tiles (the first n_tiles % grid
@@ -335,7 +335,7 @@ __device__ __forceinline__ void tiles_body(const In* __restrict__ samples,
       span_to_lds(span, ln, lds);
       lds_barrier();
       const float4* a = reinterpret_cast<const float4*>(
-          lds + ((ln & 1) ? kOddBase + 84 * (kTile - 1 - (ln >> 1)) : 84 * (ln >> 1)));
+          lds + ((ln >> 5) ? kOddBase + 84 * (kTile - 1 - (ln & 31)) : 84 * (ln & 31)));
 #pragma unroll
       for (int q = 0; q < 50; ++q) {
         const float4 t = a[q + q / 20];
@@ -350,7 +350,7 @@ __device__ __forceinline__ void tiles_body(const In* __restrict__ samples,
       pieces_to_lds(samples, cur, span_pad, sigma, ln, lds, slots);
       lds_barrier();
       const float4* a = reinterpret_cast<const float4*>(
-          lds + ((ln & 1) ? kPieceOddBase + 84 * (kPieceT - 2 - sigma) : 84 * sigma));
+          lds + ((ln >> 5) ? kPieceOddBase + 84 * (kPieceT - 2 - sigma) : 84 * sigma));
 #pragma unroll
       for (int q = 0; q < 50; ++q) {
         const float4 t = a[q + q / 20];
@@ -378,8 +378,8 @@ __device__ __forceinline__ void tiles_body(const In* __restrict__ samples,
     // Only a wave-wide mask crosses the transform (no per-lane registers).
     const uint64_t valid_mask = __ballot(cur.valid);
 
-    float P[101];
-    pair_power(v, tables + kTabWindow, tables + kTabRot800, role ? -1.0 : 1.0, P);
+    float Pp[51], Pm[51];
+    pair_power(v, tables + kTabWindow, tables + kTabRot800, Pp, Pm);
 
     const int64_t next = tile + 1;
     const bool more = next < tile_end;
@@ -394,9 +394,9 @@ __device__ __forceinline__ void tiles_body(const In* __restrict__ samples,
     load_span(more && nxt.fast ? samples : span_pad, more && nxt.fast ? nxt.s0 : 0, lane, span);
 
     float o[64];
-    pair_logmel(P, role, o);
+    pair_logmel(Pp, Pm, role, o);
     const int64_t g = tile * kTile + fl;
-    const int64_t row = row_lds[it & 1][ln >> 1];
+    const int64_t row = row_lds[it & 1][ln & 31];
     if (g < total_frames && row >= 0 && row < out_rows)
       store_bands(out + row * 128 + 64 * role, o, (valid_mask >> lane) & 1);
     if (!more) break;

@@ -1,6 +1,6 @@
 // Tile bookkeeping shared by the log-mel transform kernels (gfx950): the
 // flattened frame space is cut into tiles of 32 consecutive frames; a
-// wavefront's lane pair 2f, 2f + 1 (lane >> 1 = f) belongs to frame f of its
+// wavefront's lanes f and f + 32 (lane & 31 = f) belong to frame f of its
 // tile. Locating a tile's clips from the int64 frame offsets, the cached
 // clip of a contiguous run of tiles, the output row map, input sample types
 // and the slot records of tiles across clips.
@@ -82,7 +82,7 @@ __device__ __forceinline__ TileSrc locate_tile(int64_t tile, int lane,
                                                int64_t total_frames, ClipCache& cc) {
   TileSrc t;
   const int64_t g0 = tile * kTile;
-  t.g = g0 + (lane >> 1);
+  t.g = g0 + (lane & 31);
   t.in_range = t.g < total_frames;
   if (cc.lo <= g0 && g0 + kTile <= cc.hi && g0 + kTile <= total_frames) {
     // all 32 frames in the cached clip (so all inside the batch)
@@ -184,14 +184,17 @@ __device__ __forceinline__ float4 load_group(const int16_t* p) {
 }
 
 // Slot of each lane's frame in the pieces layout, and the number of pieces
-// after the first (wave-uniform).
+// after the first (wave-uniform). Frame f's lanes are f and f + 32, so lane
+// ln - 1 holds the previous frame (for ln & 31 >= 1) and the lower 32 bits of
+// a ballot hold one bit per frame.
 __device__ __forceinline__ void piece_slot(const TileSrc& t, int ln, int& sigma, int& breaks) {
-  const int64_t s_prev = __shfl(t.s, ln - 2);
-  const bool v_prev = __shfl((int)t.valid, ln - 2) != 0;
-  const bool brk = t.valid && ln >= 2 && !(v_prev && t.s == s_prev + 160);
-  const uint64_t bm = __ballot(brk) & 0x5555555555555555ull;
+  const int f = ln & 31;
+  const int64_t s_prev = __shfl(t.s, ln - 1);
+  const bool v_prev = __shfl((int)t.valid, ln - 1) != 0;
+  const bool brk = t.valid && f >= 1 && !(v_prev && t.s == s_prev + 160);
+  const uint64_t bm = __ballot(brk) & 0xffffffffull;
   breaks = __popcll(bm);
-  sigma = (ln >> 1) + 2 * __popcll(bm & ((2ull << (ln & ~1)) - 1));
+  sigma = f + 2 * __popcll(bm & ((2ull << f) - 1));
 }
 
 // The fp32 value is fenced first, so that the conversion rounds the fp32
