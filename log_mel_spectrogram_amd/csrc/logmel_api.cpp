@@ -49,8 +49,8 @@ int64_t frames_of(int64_t n) { return n < kNFFT ? 0 : (n - kNFFT) / kHop + 1; }
 static const double kHostWindow[200] = {
 #include "logmel_window.inc"
 };
-static const double kHostRot800[208] = {
-#include "logmel_rot800.inc"
+static const double kHostRot400[200] = {
+#include "logmel_rot400.inc"
 };
 
 struct logmel_plan {
@@ -349,7 +349,7 @@ int logmel_plan_create(const logmel_config* cfg, logmel_plan** out) {
   p->resident_waves = 4 * cus;   // 4 SIMDs per compute unit
   double host[kTabDoubles];
   std::memcpy(host + kTabWindow, kHostWindow, sizeof(kHostWindow));
-  std::memcpy(host + kTabRot800, kHostRot800, sizeof(kHostRot800));
+  std::memcpy(host + kTabRot400, kHostRot400, sizeof(kHostRot400));
   if (hipMalloc(&p->tables, kTabBytes) != hipSuccess) {
     delete p;
     return LOGMEL_ERR_OUT_OF_MEMORY;

@@ -30,14 +30,16 @@
 //       |X[k]|       = |u + conj(v)|,
 //       |X[200 - k]| = |u - conj(v)|.
 //     Every column k2 of the 8-point DFTs holds bins k <= 50 and k + 50 in
-//     pairs (bins taken as k or 200 - k, whichever is <= 100). Both roles
-//     rotate both bins of a pair (the same W800^k for both), and one
+//     pairs (bins taken as k or 200 - k, whichever is <= 100). One
 //     v_permlane32_swap per 32-bit word exchanges the upper lanes' first bin
-//     with the lower lanes' second: afterwards lane f holds u and v of bin k
-//     and lane f + 32 those of bin k + 50, and each forms both powers of its
-//     bin. So role 0 holds bins 1..50 and 150..199, role 1 bins 51..149, and
-//     one swap word serves two bins. The filterbank runs on these halves (see
-//     pair_logmel); role 0 logs and stores bands 0..63, role 1 bands 64..127.
+//     with the lower lanes' second: afterwards lane f holds E and R of bin k
+//     and lane f + 32 those of bin k + 50, so one swap word serves two bins.
+//     Dividing u + conj(v) by W800^k, each lane forms with its own bin's
+//     rotation (from LDS: the two halves combine different bins)
+//       t = W400^-k conj(R[k]),  |X[k]| = |E[k] + t|,  |X[200 - k]| = |E[k] - t|.
+//     So role 0 holds bins 1..50 and 150..199, role 1 bins 51..149. The
+//     filterbank runs on these halves (see pair_logmel); role 0 logs and
+//     stores bands 0..63, role 1 bands 64..127.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -207,17 +209,44 @@ __host__ __device__ constexpr int pfa_partner(int k1a, int k2) {
     if (pfa_kap(k1a, k2) != 0 && pfa_kap(k1, k2) == pfa_kap(k1a, k2) + 50) r = k1;
   return r;
 }
+// Whether (k1a, k2) is the first bin of a pair, and the pair's slot: pairs
+// numbered in order of k2, then k1 (the order of the plan's rotation table).
+__host__ __device__ constexpr bool pfa_pair_first(int k1a, int k2) {
+  return pfa_kap(k1a, k2) >= 1 && pfa_kap(k1a, k2) <= 50 && pfa_partner(k1a, k2) >= 0;
+}
+__host__ __device__ constexpr int pfa_slot(int k1a, int k2) {
+  int n = 0;
+  for (int c = 0; c < 13; ++c)
+    for (int k1 = 0; k1 < 8; ++k1) {
+      if (c == k2 && k1 == k1a) return n;
+      if (pfa_pair_first(k1, c)) ++n;
+    }
+  return n;
+}
+static_assert(pfa_slot(0, 13) == 50, "50 bin pairs");
+// This half's rotations of column k2's pairs (LDS), by the k1 of the
+// pair's first bin.
+__device__ __forceinline__ void column_rotations(const double* rot, int k2, double (&c)[8],
+                                                 double (&s)[8]) {
+#pragma unroll
+  for (int k1 = 0; k1 < 8; ++k1) {
+    if (!pfa_pair_first(k1, k2)) continue;
+    c[k1] = rot[2 * pfa_slot(k1, k2)];
+    s[k1] = rot[2 * pfa_slot(k1, k2) + 1];
+  }
+}
 
 // Power spectrum of one frame on a lane pair.
 //   v[200]   this lane's samples, m = 0..199 (fp32): x[2m] for role 0,
 //            x[399 - 2m] for role 1
 //   win      w[2m], m = (25 n1 + 8 n2) mod 200, in [n1][n2] order (uniform)
-//   rot      cos, sin of 2 pi kap / 800 for the bins in [k2][k1] order (uniform)
+//   rot      this half's cos, sin of 2 pi kap / 400 in pair order (LDS: role 0
+//            bins a, role 1 bins a + 50; see pfa_slot)
 //   Pp, Pm   this lane's half of the power spectrum, a = 1..50:
 //            role 0: Pp[a] = |X[a]|^2,      Pm[a] = |X[200 - a]|^2
 //            role 1: Pp[a] = |X[a + 50]|^2, Pm[a] = |X[150 - a]|^2
 __device__ __forceinline__ void pair_power(const float (&v)[200], const double* __restrict__ win,
-                                           const double* __restrict__ rot, float (&Pp)[51],
+                                           const double* rot, float (&Pp)[51],
                                            float (&Pm)[51]) {
   // Stage 1: 8 real 25-point DFTs over n2, two rows n1 per scheduling region
   // (two independent transforms give the scheduler work to overlap).
@@ -259,10 +288,13 @@ __device__ __forceinline__ void pair_power(const float (&v)[200], const double* 
 
   // Stage 2 and the combine: for each k2, an 8-point DFT over n1 gives this
   // role's spectrum at k = pfa_k(k1, k2) (k > 100 through conjugation); for
-  // each pair of bins a, a + 50 of the column, rotate both, exchange halves
-  // and form the two powers of this half's bin.
+  // each pair of bins a, a + 50 of the column, exchange halves, rotate this
+  // half's R and form the two powers of this half's bin.
 #pragma unroll
   for (int k2 = 0; k2 <= 12; ++k2) {
+    // The column's rotations (LDS); the compiler places the reads.
+    double rc[8], rs[8];
+    column_rotations(rot, k2, rc, rs);
     cd q[8];
 #pragma unroll
     for (int n1 = 0; n1 < 8; ++n1) {
@@ -270,40 +302,32 @@ __device__ __forceinline__ void pair_power(const float (&v)[200], const double* 
       fence(q[n1].re);
       if (k2 > 0) fence(q[n1].im);
     }
-    // This column's rotations, loaded ahead of the 8-point DFT so that the
-    // scalar loads overlap it.
-    double rc[8], rs[8];
-#pragma unroll
-    for (int k1 = 0; k1 < 8; ++k1) {
-      rc[k1] = rot[16 * k2 + 2 * k1];
-      rs[k1] = rot[16 * k2 + 2 * k1 + 1];
-    }
     dft8(q);
 #pragma unroll
     for (int ka = 0; ka < 8; ++ka) {
+      if (!pfa_pair_first(ka, k2)) continue;
       const int a = pfa_kap(ka, k2), kb = pfa_partner(ka, k2);
-      if (a == 0 || a > 50 || kb < 0) continue;
-      // this role's spectrum at bins a and a + 50, times W800^kap
-      const cd ra = pfa_k(ka, k2) <= 100 ? q[ka] : cd{q[ka].re, -q[ka].im};
-      const cd rb = pfa_k(kb, k2) <= 100 ? q[kb] : cd{q[kb].re, -q[kb].im};
-      cd u = c_twiddle(ra, rc[ka], rs[ka]);
-      cd w = c_twiddle(rb, rc[kb], rs[kb]);
-      // u := role 0's value, w := role 1's value, of bin a in the lower
-      // lanes and of bin a + 50 in the upper ones
-      half_swap(u.re, w.re);
-      half_swap(u.im, w.im);
-      const double pre = u.re + w.re, pim = u.im - w.im;   // u + conj(w)
-      const double mre = u.re - w.re, mim = u.im + w.im;   // u - conj(w)
+      // this role's spectrum at bins a and a + 50
+      cd e = pfa_k(ka, k2) <= 100 ? q[ka] : cd{q[ka].re, -q[ka].im};
+      cd r = pfa_k(kb, k2) <= 100 ? q[kb] : cd{q[kb].re, -q[kb].im};
+      // e := role 0's spectrum E, r := role 1's R, at bin a in the lower
+      // lanes and at bin a + 50 in the upper ones
+      half_swap(e.re, r.re);
+      half_swap(e.im, r.im);
+      // t = W400^-kap conj(R) = (c + i s)(R.re - i R.im), this half's kap
+      const double c = rc[ka], s = rs[ka];
+      const double tre = c * r.re + s * r.im, tim = s * r.re - c * r.im;
+      const double pre = e.re + tre, pim = e.im + tim;   // X[kap]
+      const double mre = e.re - tre, mim = e.im - tim;   // conj X[200 - kap]
       Pp[a] = (float)(pre * pre + pim * pim);
       Pm[a] = (float)(mre * mre + mim * mim);
     }
     // one scheduling region per column
 #pragma unroll
     for (int ka = 0; ka < 8; ++ka) {
-      const int a = pfa_kap(ka, k2);
-      if (a == 0 || a > 50 || pfa_partner(ka, k2) < 0) continue;
-      fence(Pp[a]);
-      fence(Pm[a]);
+      if (!pfa_pair_first(ka, k2)) continue;
+      fence(Pp[pfa_kap(ka, k2)]);
+      fence(Pm[pfa_kap(ka, k2)]);
     }
   }
 

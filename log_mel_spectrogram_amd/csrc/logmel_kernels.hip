@@ -272,7 +272,7 @@ __device__ __forceinline__ void tiles_body(const In* __restrict__ samples,
                                            int64_t row_unit, int64_t out_rows,
                                            const double* __restrict__ tables,
                                            float* lds, int64_t (&row_lds)[2][kTile],
-                                           PieceSlot* slots) {
+                                           PieceSlot* slots, double* rot_lds) {
   // a readable stand-in for a span when there is none to fetch (zeros)
   const In* span_pad = reinterpret_cast<const In*>(tables + kTabDoubles);
   const RowMap rows{row_base, row_unit};
@@ -292,23 +292,29 @@ __device__ __forceinline__ void tiles_body(const In* __restrict__ samples,
   int64_t tile = blockIdx.x * per + min((int64_t)blockIdx.x, extra);
   const int64_t tile_end = tile + per + ((int64_t)blockIdx.x < extra ? 1 : 0);
   if (tile >= tile_end) return;
+  // The combine's rotations go to LDS (the two halves of a pair read
+  // different ones): 100 16-byte entries, loaded now and written after the
+  // first tile is located, so that the loads' latency overlaps the lookup.
+  const float4* rot_src = reinterpret_cast<const float4*>(tables + kTabRot400);
+  const float4 rot0 = rot_src[lane], rot1 = rot_src[min(lane + kWaveLanes, 99)];
   ClipCache cc{0, 0, 0, 0, 0};
   TileSrc cur = locate_tile(tile, lane, seg_start, seg_end, frame_off, rows, n_clips,
                             total_frames, cc);
   if (role == 0) row_lds[0][fl] = cur.row;
   typename SpanOf<In>::type span;
   if (cur.fast) load_span(samples, cur.s0, lane, span);
+  reinterpret_cast<float4*>(rot_lds)[lane] = rot0;
+  if (lane + kWaveLanes < 100) reinterpret_cast<float4*>(rot_lds)[lane + kWaveLanes] = rot1;
   {
     // A kernel starts with its scalar cache invalidated, and the transform
-    // reads the window and the rotations through it: touch every 64-byte
-    // line of the plan's tables now, while the first span's loads are in
-    // flight, instead of missing on them one by one inside the first
-    // transform.
+    // reads the window through it: touch every 64-byte line of the window
+    // now, while the first span's loads are in flight, instead of missing on
+    // them one by one inside the first transform.
     // One 4-byte load per line, in batches that are all in flight before
     // their first use (one round trip to L2 per batch).
-    constexpr int kLines = (kTabDoubles * 8 + 63) / 64;   // 51
+    constexpr int kLines = (200 * 8 + 63) / 64;   // 25
     constexpr int kBatch = 13;
-    const uint32_t* tl = reinterpret_cast<const uint32_t*>(tables);
+    const uint32_t* tl = reinterpret_cast<const uint32_t*>(tables + kTabWindow);
 #pragma unroll
     for (int b = 0; b < kLines; b += kBatch) {
       uint32_t v[kBatch];
@@ -379,7 +385,7 @@ __device__ __forceinline__ void tiles_body(const In* __restrict__ samples,
     const uint64_t valid_mask = __ballot(cur.valid);
 
     float Pp[51], Pm[51];
-    pair_power(v, tables + kTabWindow, tables + kTabRot800, Pp, Pm);
+    pair_power(v, tables + kTabWindow, rot_lds + 100 * role, Pp, Pm);
 
     const int64_t next = tile + 1;
     const bool more = next < tile_end;
@@ -416,9 +422,11 @@ __device__ __forceinline__ void tiles_body(const In* __restrict__ samples,
     __shared__ float4 span_lds[(kLdsFloats + 3) / 4];                                           \
     __shared__ int64_t row_lds[2][kTile];                                                       \
     __shared__ PieceSlot slots[kPieceT + 1];                                                    \
+    __shared__ float4 rot_lds[100];                                                             \
     tiles_body<IN, OUT>(samples, seg_start, seg_end, frame_off, n_clips, total_frames, out,     \
                         row_base, row_unit, out_rows, tables,                                   \
-                        reinterpret_cast<float*>(span_lds), row_lds, slots);                    \
+                        reinterpret_cast<float*>(span_lds), row_lds, slots,                     \
+                        reinterpret_cast<double*>(rot_lds));                                    \
   }
 
 // samples [seg_start[i], seg_end[i]) are clip i; frame f of clip i goes to

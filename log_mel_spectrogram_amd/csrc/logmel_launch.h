@@ -6,13 +6,14 @@
 
 // Device constant tables owned by a plan (fp64): the window at the even
 // points in the order the transform consumes them (both lanes of a pair use
-// it), then cos/sin of 2 pi k / 800 interleaved, in the order the
-// transform's 8-point DFTs produce bins ([k2][k1], 13 x 8 pairs).
+// it), then cos/sin of 2 pi k / 400 interleaved for the bins each half of a
+// lane pair combines ([half][slot], 2 x 50 pairs; the kernel copies them to
+// LDS).
 // After the doubles, kTabPadFloats zero floats: a readable stand-in for a
 // tile's 5360-sample span.
 static constexpr int kTabWindow = 0;
-static constexpr int kTabRot800 = 200;
-static constexpr int kTabDoubles = 408;
+static constexpr int kTabRot400 = 200;
+static constexpr int kTabDoubles = 400;
 static constexpr int kTabPadFloats = 5360;
 static constexpr size_t kTabBytes = 8 * kTabDoubles + 4 * kTabPadFloats;
 
