@@ -70,17 +70,52 @@ __device__ __forceinline__ void load_span(const float* __restrict__ base, int64_
   }
 }
 
-__device__ __forceinline__ void span_to_lds(const SpanF32& sp, int ln, float* lds) {
+// Group j = ln + 64 i of the span (i = 0 .. kSpanRegs - 2: inside the span
+// for every lane) puts its even values at par_pos(2j) and its reversed odd
+// values at kOddBase + par_pos(2678 - 2j). From i to i + 1 these move by
+// +132 or +136 and by -132 or -136 (the padding after every 80 values is
+// crossed once or twice); bit i of the lane's masks, fixed for the kernel,
+// says which, so a group's two positions cost a few instructions instead
+// of two divisions by 40.
+struct SpanSteps {
+  uint32_t even, odd;
+};
+__device__ __forceinline__ SpanSteps span_steps(int ln) {
+  uint32_t me = 0, mo = 0;
 #pragma unroll
-  for (int i = 0; i < kSpanRegs; ++i) {
-    const int j = min(ln + kWaveLanes * i, kSpanGroups - 1);
-    // even values 2j, 2j + 1; reversed odd values 2678 - 2j (sample 4j + 3)
-    // and 2679 - 2j (sample 4j + 1)
-    const int e = par_pos(2 * j);
-    const int o = kOddBase + par_pos(kSpan / 2 - 2 - 2 * j);
+  for (int i = 0; i < kSpanRegs - 2; ++i) {
+    me |= (uint32_t)((ln + kWaveLanes * (i + 1)) / 40 - (ln + kWaveLanes * i) / 40 - 1) << i;
+    const int x0 = kSpanGroups - 1 - ln - kWaveLanes * i, x1 = x0 - kWaveLanes;
+    mo |= (uint32_t)(x0 / 40 - x1 / 40 - 1) << i;
+  }
+  return {me, mo};
+}
+
+// Writes the even and reversed odd values of the span's groups to LDS: put(i,
+// e, o) stores group i's values at positions e (even) and o (odd).
+template <typename Put>
+__device__ __forceinline__ void span_positions(int ln, SpanSteps st, const Put& put) {
+  int e = par_pos(2 * ln), o = kOddBase + par_pos(kSpan / 2 - 2 - 2 * ln);
+#pragma unroll
+  for (int i = 0; i < kSpanRegs - 1; ++i) {
+    put(i, e, o);
+    if (i < kSpanRegs - 2) {
+      e += 132 + 4 * (int)((st.even >> i) & 1u);
+      o -= 132 + 4 * (int)((st.odd >> i) & 1u);
+    }
+  }
+  // the last group: lanes past the span's end repeat its last group
+  const int j = min(ln + kWaveLanes * (kSpanRegs - 1), kSpanGroups - 1);
+  put(kSpanRegs - 1, par_pos(2 * j), kOddBase + par_pos(kSpan / 2 - 2 - 2 * j));
+}
+
+__device__ __forceinline__ void span_to_lds(const SpanF32& sp, int ln, SpanSteps st, float* lds) {
+  // even values 2j, 2j + 1; reversed odd values 2678 - 2j (sample 4j + 3)
+  // and 2679 - 2j (sample 4j + 1)
+  span_positions(ln, st, [&](int i, int e, int o) {
     *reinterpret_cast<float2*>(lds + e) = make_float2(sp.g[i].x, sp.g[i].z);
     *reinterpret_cast<float2*>(lds + o) = make_float2(sp.g[i].w, sp.g[i].y);
-  }
+  });
 }
 
 // The span of a tile inside one clip, int16: 8-byte groups (4 samples) from
@@ -115,18 +150,15 @@ __device__ __forceinline__ void load_span(const int16_t* __restrict__ base, int6
 __device__ __forceinline__ float lo16(uint32_t v) { return (float)(int16_t)(v & 0xffff) * kI16Scale; }
 __device__ __forceinline__ float hi16(uint32_t v) { return (float)(int16_t)(v >> 16) * kI16Scale; }
 
-__device__ __forceinline__ void span_to_lds(const SpanI16& sp, int ln, float* lds) {
+__device__ __forceinline__ void span_to_lds(const SpanI16& sp, int ln, SpanSteps st, float* lds) {
   if (!sp.odd) {
     // samples 4j .. 4j + 3 of the span, as in the fp32 layout
-#pragma unroll
-    for (int i = 0; i < kSpanRegs; ++i) {
-      const int j = min(ln + kWaveLanes * i, kSpanGroups - 1);
+    span_positions(ln, st, [&](int i, int e, int o) {
       const float f0 = lo16(sp.g[i].x), f1 = hi16(sp.g[i].x);
       const float f2 = lo16(sp.g[i].y), f3 = hi16(sp.g[i].y);
-      *reinterpret_cast<float2*>(lds + par_pos(2 * j)) = make_float2(f0, f2);
-      *reinterpret_cast<float2*>(lds + kOddBase + par_pos(kSpan / 2 - 2 - 2 * j)) =
-          make_float2(f3, f1);
-    }
+      *reinterpret_cast<float2*>(lds + e) = make_float2(f0, f2);
+      *reinterpret_cast<float2*>(lds + o) = make_float2(f3, f1);
+    });
   } else {
     // group j holds span samples 4j - 1 .. 4j + 2: even values 2j, 2j + 1
     // (samples 4j, 4j + 2), odd values 2j - 1 and 2j (samples 4j - 1, 4j + 1)
@@ -298,6 +330,7 @@ __device__ __forceinline__ void tiles_body(const In* __restrict__ samples,
   const float4* rot_src = reinterpret_cast<const float4*>(tables + kTabRot400);
   const float4 rot0 = rot_src[lane], rot1 = rot_src[min(lane + kWaveLanes, 99)];
   ClipCache cc{0, 0, 0, 0, 0};
+  const SpanSteps steps = span_steps(lane);
   TileSrc cur = locate_tile(tile, lane, seg_start, seg_end, frame_off, rows, n_clips,
                             total_frames, cc);
   if (role == 0) row_lds[0][fl] = cur.row;
@@ -338,7 +371,7 @@ __device__ __forceinline__ void tiles_body(const In* __restrict__ samples,
     if (cur.fast) {
       // Split the span by parity into LDS (layout above), then read back this
       // lane's 200 values.
-      span_to_lds(span, ln, lds);
+      span_to_lds(span, ln, steps, lds);
       lds_barrier();
       const float4* a = reinterpret_cast<const float4*>(
           lds + ((ln >> 5) ? kOddBase + 84 * (kTile - 1 - (ln & 31)) : 84 * (ln & 31)));
