@@ -340,7 +340,7 @@ __device__ __forceinline__ void pair_power(const float (&v)[200], const double* 
 // bins lie in both halves is the sum of two partial sums). Bands 0..63 lie in
 // role 0's half, and role 0 logs them; role 1 logs bands 64..127 and takes
 // the sums that only role 0 holds from its partner (v_permlane32_swap). The
-// log has the 1e-10 floor; the floor test keeps a NaN energy NaN.
+// log has the 1e-10 floor, taken so that a NaN energy stays NaN.
 
 // Half of the pair that holds bin b (1..199): 0 for bins 1..50 and
 // 150..199, 1 for bins 51..149.
@@ -377,49 +377,93 @@ __device__ __forceinline__ float bin_power(const float (&Pp)[51], const float (&
   return b <= 50 ? Pp[b] : (b <= 100 ? Pp[b - 50] : (b <= 149 ? Pm[150 - b] : Pm[200 - b]));
 }
 
-// Energy of band m as the role that logs it needs it (one instance per band,
-// so that every index and weight is a constant).
+// Sum of band m's terms whose bins lie in half h, over this lane's registers
+// (right in half h; one instance per band and half, so that every index
+// and weight is a constant).
+template <int m, int h>
+__device__ __forceinline__ float mel_part(const float (&Pp)[51], const float (&Pm)[51]) {
+  constexpr int n = kMelCount[m], k0 = kMelStart[m], f = mel_first_tap(m, h);
+  static_assert(f >= 0, "band has no bins in this half");
+  float acc = 0.0f;
+#pragma unroll
+  for (int j = 0; j < n; ++j) {
+    if (bin_half(k0 + j) != h) continue;
+    const float t = kMelW[m][j] * bin_power(Pp, Pm, k0 + j);
+    acc = (j == f) ? t : acc + t;
+  }
+  return acc;
+}
+
+// Bands 64..127 whose bins lie (also) in role 0's half: role 0's partial
+// sums, moved to role 1 with the whole wavefront active.
 template <int m>
-__device__ __forceinline__ float mel_band(const float (&Pp)[51], const float (&Pm)[51]) {
-  constexpr int n = kMelCount[m], k0 = kMelStart[m], side = mel_side(m);
-  if constexpr (n == 0) {
+__device__ __forceinline__ void mel_transfer(const float (&Pp)[51], const float (&Pm)[51], float& t) {
+  if constexpr (mel_side(m) == 0 || mel_side(m) == 2) t = pair_from(mel_part<m, 0>(Pp, Pm), 0);
+}
+template <int... I>
+__device__ __forceinline__ void mel_transfers(const float (&Pp)[51], const float (&Pm)[51],
+                                             float (&T)[64], std::integer_sequence<int, I...>) {
+  (mel_transfer<64 + I>(Pp, Pm, T[I]), ...);
+}
+
+// Role 0's bands 0..63 (all in its half).
+template <int m>
+__device__ __forceinline__ float mel_low_band(const float (&Pp)[51], const float (&Pm)[51]) {
+  if constexpr (mel_side(m) < 0) {
+    return 0.0f * Pp[1];   // an empty filter (see mel_high_band)
+  } else {
+    return mel_part<m, 0>(Pp, Pm);
+  }
+}
+template <int... I>
+__device__ __forceinline__ void mel_low(const float (&Pp)[51], const float (&Pm)[51], float (&E)[64],
+                                        std::integer_sequence<int, I...>) {
+  ((E[I] = mel_low_band<I>(Pp, Pm)), ...);
+}
+
+template <int m>
+__device__ __forceinline__ float mel_high_band(const float (&Pp)[51], const float (&Pm)[51], float t) {
+  constexpr int side = mel_side(m);
+  if constexpr (side < 0) {
     // An empty filter's sum of zero-weight terms: 0, or NaN where the
     // frame's powers are NaN (a NaN sample reaches every bin).
     return 0.0f * Pp[1];
+  } else if constexpr (side == 0) {
+    return t;
+  } else if constexpr (side == 1) {
+    return mel_part<m, 1>(Pp, Pm);
   } else {
-    constexpr int f0 = mel_first_tap(m, 0), f1 = mel_first_tap(m, 1);
-    float s0 = 0.0f, s1 = 0.0f;
-#pragma unroll
-    for (int j = 0; j < n; ++j) {
-      const float t = kMelW[m][j] * bin_power(Pp, Pm, k0 + j);
-      if (bin_half(k0 + j) == 0) s0 = (j == f0) ? t : s0 + t;
-      else s1 = (j == f1) ? t : s1 + t;
-    }
-    if constexpr (side == 0) {
-      return m < 64 ? s0 : pair_from(s0, 0);
-    } else if constexpr (side == 1) {
-      return s1;
-    } else {
-      return pair_from(s0, 0) + s1;
-    }
+    return t + mel_part<m, 1>(Pp, Pm);
   }
 }
-
-template <int... M>
-__device__ __forceinline__ void mel_bands(const float (&Pp)[51], const float (&Pm)[51],
-                                          float (&E)[128], std::integer_sequence<int, M...>) {
-  ((E[M] = mel_band<M>(Pp, Pm)), ...);
+// Role 1's bands 64..127.
+template <int... I>
+__device__ __forceinline__ void mel_high(const float (&Pp)[51], const float (&Pm)[51],
+                                         const float (&T)[64], float (&E)[64],
+                                         std::integer_sequence<int, I...>) {
+  ((E[I] = mel_high_band<64 + I>(Pp, Pm, T[I])), ...);
 }
 
 __device__ __forceinline__ void pair_logmel(const float (&Pp)[51], const float (&Pm)[51], int role,
                                             float (&out)[64]) {
-  float E[128];
-  mel_bands(Pp, Pm, E, std::make_integer_sequence<int, 128>{});
+  float T[64];
+  mel_transfers(Pp, Pm, T, std::make_integer_sequence<int, 64>{});
+  // Each role sums only the bands it logs (the other half of the wavefront
+  // is masked off meanwhile), so no select between the two sets is needed.
+  float E[64];
+  if (role == 0) {
+    mel_low(Pp, Pm, E, std::make_integer_sequence<int, 64>{});
+  } else {
+    mel_high(Pp, Pm, T, E, std::make_integer_sequence<int, 64>{});
+  }
 #pragma unroll
   for (int i = 0; i < 64; ++i) {
-    float e = role ? E[64 + i] : E[i];
-    e = (e < kLogFloor) ? kLogFloor : e;
-    out[i] = __builtin_amdgcn_logf(e) * kLn2;
+    // A band's energy is a sum of products of non-negative weights and
+    // powers: +0 or more, or NaN. Such floats order like their bit patterns
+    // read as unsigned integers, and every NaN lies above +Inf, so the
+    // integer maximum with the floor is max(e, 1e-10) that keeps NaN.
+    const uint32_t b = __builtin_bit_cast(uint32_t, E[i]), f = __builtin_bit_cast(uint32_t, kLogFloor);
+    out[i] = __builtin_amdgcn_logf(__builtin_bit_cast(float, __builtin_elementwise_max(b, f))) * kLn2;
   }
 }
 

@@ -261,32 +261,18 @@ __device__ __forceinline__ void pieces_to_lds(const In* __restrict__ samples, co
 // ---------------------------------------------------------------------------
 // Output types: fp32, or fp16 (each value rounded once to nearest).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void store_bands(float* __restrict__ dst, const float (&o)[64], bool ok) {
+__device__ __forceinline__ void store_bands(float* __restrict__ dst, const float (&o)[64]) {
   float4* d = reinterpret_cast<float4*>(dst);
-  if (ok) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) d[i] = make_float4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
-  } else {
-    // Offsets that promise a frame the clip cannot hold: a loud row, not a
-    // silent truncation.
-    const float qnan = __builtin_nanf("");
-#pragma unroll
-    for (int i = 0; i < 16; ++i) d[i] = make_float4(qnan, qnan, qnan, qnan);
-  }
+  for (int i = 0; i < 16; ++i) d[i] = make_float4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
 }
 
-__device__ __forceinline__ void store_bands(_Float16* __restrict__ dst, const float (&o)[64], bool ok) {
+__device__ __forceinline__ void store_bands(_Float16* __restrict__ dst, const float (&o)[64]) {
   uint4* d = reinterpret_cast<uint4*>(dst);
-  if (ok) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      d[i] = make_uint4(pack_half2(o[8 * i], o[8 * i + 1]), pack_half2(o[8 * i + 2], o[8 * i + 3]),
-                        pack_half2(o[8 * i + 4], o[8 * i + 5]), pack_half2(o[8 * i + 6], o[8 * i + 7]));
-  } else {
-    const uint32_t qnan2 = 0x7e007e00u;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) d[i] = make_uint4(qnan2, qnan2, qnan2, qnan2);
-  }
+  for (int i = 0; i < 8; ++i)
+    d[i] = make_uint4(pack_half2(o[8 * i], o[8 * i + 1]), pack_half2(o[8 * i + 2], o[8 * i + 3]),
+                      pack_half2(o[8 * i + 4], o[8 * i + 5]), pack_half2(o[8 * i + 6], o[8 * i + 7]));
 }
 
 template <typename In> struct SpanOf;
@@ -412,10 +398,12 @@ __device__ __forceinline__ void tiles_body(const In* __restrict__ samples,
 #pragma unroll
       for (int i = 0; i < 200; ++i) v[i] = 0.0f;
     }
+    // Offsets that promise a frame the clip cannot hold give a row of NaN (a
+    // loud row, not a silent truncation): a NaN sample reaches every bin of
+    // both halves, so one select here stands for 64 selects of outputs.
+    if (!cur.valid) v[0] = __builtin_nanf("");
 #pragma unroll
     for (int i = 0; i < 200; ++i) fence(v[i]);
-    // Only a wave-wide mask crosses the transform (no per-lane registers).
-    const uint64_t valid_mask = __ballot(cur.valid);
 
     float Pp[51], Pm[51];
     pair_power(v, tables + kTabWindow, rot_lds + 100 * role, Pp, Pm);
@@ -437,7 +425,7 @@ __device__ __forceinline__ void tiles_body(const In* __restrict__ samples,
     const int64_t g = tile * kTile + fl;
     const int64_t row = row_lds[it & 1][ln & 31];
     if (g < total_frames && row >= 0 && row < out_rows)
-      store_bands(out + row * 128 + 64 * role, o, (valid_mask >> lane) & 1);
+      store_bands(out + row * 128 + 64 * role, o);
     if (!more) break;
     tile = next;
     cur = nxt;
