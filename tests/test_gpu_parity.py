@@ -192,6 +192,34 @@ def test_inconsistent_offsets_give_nan_rows(env):
     assert_parity(o[[0, 3, 4]], L, E, "rows that are valid")
 
 
+@pytest.mark.gpu
+@pytest.mark.parametrize("in_i16,out_f16", [(False, True), (True, False), (True, True)])
+def test_inconsistent_offsets_nan_rows_all_types(env, in_i16, out_f16):
+    """The same NaN rows with int16 PCM input and with fp16 output (a NaN
+    sample marks the frame before the transform, so the row is NaN in every
+    output type), and the other rows equal to the fp32 path's, rounded once
+    to fp16 for fp16 output."""
+    lm, plan, torch = env
+    say(f"inconsistent offsets, int16 in {in_i16}, fp16 out {out_f16}")
+    dev = torch.device("cuda", 0)
+    rng = np.random.default_rng(25)
+    s16 = rng.integers(-32768, 32768, 1060).astype(np.int16)
+    x32 = s16.astype(np.float32) / np.float32(32768.0)
+    so = torch.tensor([0, 500, 1060], dtype=torch.int64, device=dev)   # 1 and 2 frames
+    fo = torch.tensor([0, 3, 5], dtype=torch.int64, device=dev)        # claims 3 and 2
+    xin = torch.from_numpy(s16 if in_i16 else x32).to(dev)
+    got = lm.logmel_compute_ex(plan, xin, so, fo, 5,
+                               out_dtype=torch.float16 if out_f16 else torch.float32)
+    ref = lm.logmel_compute_ex(plan, torch.from_numpy(x32).to(dev), so, fo, 5)
+    torch.cuda.synchronize()
+    g = got.float().cpu().numpy()
+    r = ref.cpu().numpy()
+    assert np.all(np.isnan(g[1:3]))
+    assert not np.any(np.isnan(g[[0, 3, 4]]))
+    want = r[[0, 3, 4]].astype(np.float16).astype(np.float32) if out_f16 else r[[0, 3, 4]]
+    assert np.array_equal(g[[0, 3, 4]], want)
+
+
 def test_validate_mode_rejects(env, monkeypatch):
     lm, plan, torch = env
     say("validate mode")
