@@ -500,8 +500,8 @@ def bench_stream(args, lm, plan, torch):
     def one_pass():
         lm.logmel_stream_reset(s)
         for c in range(pushes):
-            fo = lm.logmel_stream_frames_for_push(s, pls[c])
-            lm.logmel_stream_push(s, chunks[c], pls[c], out=out[:int(fo[-1])], stream=stream)
+            # out has room for the largest push; the push writes its first rows
+            lm.logmel_stream_push(s, chunks[c], pls[c], out=out, stream=stream)
         if rate != FS:
             fo = lm.logmel_stream_frames_for_flush(s)
             lm.logmel_stream_flush(s, out=flush_out[:int(fo[-1])], stream=stream)

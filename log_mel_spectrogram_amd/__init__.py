@@ -365,6 +365,12 @@ class Stream:
         self.max_push = int(max_push)
         self.in_rate = int(in_rate)
         self._destroy = _stream_destroy
+        # Host arrays a push reuses (push lengths, frame offsets) and their
+        # addresses, so that a push marshals no new numpy or ctypes objects.
+        self._pl = np.zeros(self.n_streams, dtype=np.int64)
+        self._fo = np.zeros(self.n_streams + 1, dtype=np.int64)
+        self._pl_p = _ptr64(self._pl)
+        self._fo_p = _ptr64(self._fo)
 
     def close(self):
         if getattr(self, "handle", None):
@@ -457,19 +463,27 @@ def logmel_stream_push(s: Stream, new_samples, push_len, out=None, stream=None, 
     """Pushes packed new samples; returns (out [frames, 128], frame offsets).
 
     new_samples fp32 or int16 (s / 32768); output fp32 or fp16 (out_dtype,
-    default fp32, or out's dtype)."""
+    default fp32, or out's dtype). ``out`` may have more rows than the push
+    emits (a buffer sized once for the largest push): the push writes its
+    first fo[-1] rows and returns a view of them."""
     torch = _torch()
-    pl = _i64_array(push_len)
-    if pl.size != s.n_streams:
+    pl = s._pl
+    try:
+        ok = len(push_len) == s.n_streams
+    except TypeError:
+        ok = False
+    if not ok:
         raise ValueError("push_len must have n_streams entries")
-    if int(pl.sum()) != int(new_samples.numel()):
+    pl[...] = push_len
+    if int(pl.sum()) != new_samples.numel():
         raise ValueError("new_samples must hold sum(push_len) samples")
-    if new_samples.dtype == torch.float32:
+    dt = new_samples.dtype
+    if dt == torch.float32:
         st_in = LOGMEL_F32
-    elif new_samples.dtype == torch.int16:
+    elif dt == torch.int16:
         st_in = LOGMEL_I16
     else:
-        raise TypeError(f"new_samples must be float32 or int16, got {new_samples.dtype}")
+        raise TypeError(f"new_samples must be float32 or int16, got {dt}")
     out_dtype = out_dtype or (out.dtype if out is not None else torch.float32)
     if out_dtype == torch.float32:
         st_out = LOGMEL_F32
@@ -477,24 +491,21 @@ def logmel_stream_push(s: Stream, new_samples, push_len, out=None, stream=None, 
         st_out = LOGMEL_F16
     else:
         raise TypeError(f"output must be float32 or float16, got {out_dtype}")
-    fo = logmel_stream_frames_for_push(s, pl)
-    total = int(fo[-1])
+    _check(_stream_frames_for_push(s.handle, s._pl_p, s._fo_p), "logmel_stream_frames_for_push")
+    total = int(s._fo[-1])
     if out is None:
         out = torch.empty((total, N_MELS), dtype=out_dtype, device=new_samples.device)
-    if tuple(out.shape) != (total, N_MELS):
-        raise ValueError(f"out must be [{total}, {N_MELS}]")
+    if out.dim() != 2 or out.shape[1] != N_MELS or out.shape[0] < total:
+        raise ValueError(f"out must be [rows >= {total}, {N_MELS}]")
     st = _stream_handle(stream, new_samples.device)
-    fo2 = np.zeros(s.n_streams + 1, dtype=np.int64)
+    d_new = _dev_ptr(new_samples, dt, "new_samples")
+    d_out = _dev_ptr(out, out_dtype, "out")
     if st_in == LOGMEL_F32 and st_out == LOGMEL_F32:
-        _check(_stream_push(s.handle, _dev_ptr(new_samples, torch.float32, "new_samples"),
-                            _ptr64(pl), _dev_ptr(out, torch.float32, "out"), _ptr64(fo2), st),
-               "logmel_stream_push")
+        _check(_stream_push(s.handle, d_new, s._pl_p, d_out, s._fo_p, st), "logmel_stream_push")
     else:
-        _check(_stream_push_ex(s.handle, _dev_ptr(new_samples, new_samples.dtype, "new_samples"),
-                               st_in, _ptr64(pl), _dev_ptr(out, out_dtype, "out"), st_out,
-                               _ptr64(fo2), st),
+        _check(_stream_push_ex(s.handle, d_new, st_in, s._pl_p, d_out, st_out, s._fo_p, st),
                "logmel_stream_push_ex")
-    return out, fo2
+    return (out if out.shape[0] == total else out[:total]), s._fo.copy()
 
 
 def logmel_stream_counters(s: Stream, j: int):
