@@ -209,7 +209,10 @@ int logmel_stream_frames_for_push(const logmel_stream* s, const int64_t* push_le
  * Two kernel launches on hip_stream; the per-push offsets go up through the
  * stream object's pinned staging area. INPUT_TOO_LONG if a push_len exceeds
  * max_push. The new samples are copied before the call returns its work to
- * the queue, so d_new may be reused once hip_stream has passed this call. */
+ * the queue, so d_new may be reused once hip_stream has passed this call.
+ * A push reads the carry the previous push of the same stream object wrote:
+ * successive pushes must run in order on the device (one hip_stream, or
+ * streams the caller orders). */
 int logmel_stream_push(logmel_stream* s, const float* d_new, const int64_t* push_len_host,
                        float* d_out, int64_t* out_frame_offsets_host, void* hip_stream);
 

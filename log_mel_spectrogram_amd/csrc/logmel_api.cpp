@@ -244,11 +244,17 @@ struct logmel_stream {
   int64_t stride;              // floats per workspace row
   float* ws = nullptr;         // device [n][stride]
   int64_t* meta_dev = nullptr; // device [7n + 1]
-  // pinned staging ring for the per-push metadata
-  static constexpr int kSlots = 4;
-  int64_t* meta_host[kSlots] = {nullptr, nullptr, nullptr, nullptr};
-  int64_t* meta_host_dev[kSlots] = {nullptr, nullptr, nullptr, nullptr};   // their device addresses
-  hipEvent_t slot_done[kSlots] = {nullptr, nullptr, nullptr, nullptr};
+  // Pinned staging ring for the per-push metadata, taken in order and
+  // reused in groups of kSlotGroup: one event, recorded after the prep
+  // kernel of a group's last slot, tells the host that the group's slots
+  // have all been read (an event per push would put a packet of its own
+  // between the kernels of every push).
+  static constexpr int kSlots = 8;
+  static constexpr int kSlotGroup = 4;
+  static constexpr int kGroups = kSlots / kSlotGroup;
+  int64_t* meta_host[kSlots] = {};
+  int64_t* meta_host_dev[kSlots] = {};   // their device addresses
+  hipEvent_t slot_done[kGroups] = {};
   int slot = 0;
   // host shadow, per stream
   std::vector<int64_t> seen, emitted, carry_len, carry_src;
@@ -267,9 +273,9 @@ struct logmel_stream {
   int in_cur = 0;                       // the buffer holding the carries
   float* res_buf = nullptr;             // one push's 16 kHz samples, packed
   int64_t* rmeta_dev = nullptr;         // [9n + 1], layout in rs_push
-  int64_t* rmeta_host[kSlots] = {nullptr, nullptr, nullptr, nullptr};
-  int64_t* rmeta_host_dev[kSlots] = {nullptr, nullptr, nullptr, nullptr};
-  hipEvent_t rslot_done[kSlots] = {nullptr, nullptr, nullptr, nullptr};
+  int64_t* rmeta_host[kSlots] = {};      // the same ring for the resampling prep
+  int64_t* rmeta_host_dev[kSlots] = {};
+  hipEvent_t rslot_done[kGroups] = {};
   int rslot = 0;
   std::vector<int64_t> rs_in, rs_out, rcarry_len, rcarry_src;
 };
@@ -531,8 +537,9 @@ int logmel_stream_create(const logmel_plan* plan, int64_t n_streams, int64_t max
   for (int i = 0; ok && i < logmel_stream::kSlots; ++i)
     ok = hipHostMalloc(&s->meta_host[i], slot_words * 8, hipHostMallocDefault) == hipSuccess &&
          hipHostGetDevicePointer(reinterpret_cast<void**>(&s->meta_host_dev[i]), s->meta_host[i],
-                                 0) == hipSuccess &&
-         hipEventCreateWithFlags(&s->slot_done[i], hipEventDisableTiming) == hipSuccess;
+                                 0) == hipSuccess;
+  for (int i = 0; ok && i < logmel_stream::kGroups; ++i)
+    ok = hipEventCreateWithFlags(&s->slot_done[i], hipEventDisableTiming) == hipSuccess;
   if (!ok) {
     logmel_stream_destroy(s);
     return LOGMEL_ERR_OUT_OF_MEMORY;
@@ -549,22 +556,26 @@ int logmel_stream_create(const logmel_plan* plan, int64_t n_streams, int64_t max
 void logmel_stream_destroy(logmel_stream* s) {
   if (!s) return;
   DeviceGuard g(s->plan->cfg.device);
-  for (int i = 0; i < logmel_stream::kSlots; ++i) {
+  // The pushes of a group not yet closed by its event may still be reading
+  // their slots: wait for the device before freeing them.
+  if (s->slot % logmel_stream::kSlotGroup != 0 || s->rslot % logmel_stream::kSlotGroup != 0)
+    (void)hipDeviceSynchronize();
+  for (int i = 0; i < logmel_stream::kGroups; ++i) {
     if (s->slot_done[i]) {
       (void)hipEventSynchronize(s->slot_done[i]);
       (void)hipEventDestroy(s->slot_done[i]);
     }
-    if (s->meta_host[i]) (void)hipHostFree(s->meta_host[i]);
-  }
-  if (s->ws) (void)hipFree(s->ws);
-  if (s->meta_dev) (void)hipFree(s->meta_dev);
-  for (int i = 0; i < logmel_stream::kSlots; ++i) {
     if (s->rslot_done[i]) {
       (void)hipEventSynchronize(s->rslot_done[i]);
       (void)hipEventDestroy(s->rslot_done[i]);
     }
+  }
+  for (int i = 0; i < logmel_stream::kSlots; ++i) {
+    if (s->meta_host[i]) (void)hipHostFree(s->meta_host[i]);
     if (s->rmeta_host[i]) (void)hipHostFree(s->rmeta_host[i]);
   }
+  if (s->ws) (void)hipFree(s->ws);
+  if (s->meta_dev) (void)hipFree(s->meta_dev);
   for (int i = 0; i < 2; ++i)
     if (s->in_buf[i]) (void)hipFree(s->in_buf[i]);
   if (s->res_buf) (void)hipFree(s->res_buf);
@@ -630,8 +641,9 @@ int logmel_stream_create_ex(const logmel_plan* plan, int64_t n_streams, int64_t 
     ok = hipHostMalloc(&s->rmeta_host[i], kRStreamMetaRec * (size_t)n_streams * 8,
                        hipHostMallocDefault) == hipSuccess &&
          hipHostGetDevicePointer(reinterpret_cast<void**>(&s->rmeta_host_dev[i]),
-                                 s->rmeta_host[i], 0) == hipSuccess &&
-         hipEventCreateWithFlags(&s->rslot_done[i], hipEventDisableTiming) == hipSuccess;
+                                 s->rmeta_host[i], 0) == hipSuccess;
+  for (int i = 0; ok && i < logmel_stream::kGroups; ++i)
+    ok = hipEventCreateWithFlags(&s->rslot_done[i], hipEventDisableTiming) == hipSuccess;
   if (!ok) {
     logmel_stream_destroy(s);
     return LOGMEL_ERR_OUT_OF_MEMORY;
@@ -696,9 +708,12 @@ namespace {
 int lm_push(logmel_stream* s, const void* d_new, int sample_type, const int64_t* push_len,
             void* d_out, int out_type, int64_t* fo_out, hipStream_t st) {
   const int64_t n = s->n;
-  // Fill the next staging slot once the push that last used it has gone up.
-  const int slot = s->slot;
-  if (hipEventSynchronize(s->slot_done[slot]) != hipSuccess) return LOGMEL_ERR_DEVICE;
+  // Fill the next staging slot; at the first slot of a group, once the
+  // group's previous pushes have read it.
+  const int slot = s->slot, grp = slot / logmel_stream::kSlotGroup;
+  const bool first = slot % logmel_stream::kSlotGroup == 0;
+  const bool last = slot % logmel_stream::kSlotGroup == logmel_stream::kSlotGroup - 1;
+  if (first && hipEventSynchronize(s->slot_done[grp]) != hipSuccess) return LOGMEL_ERR_DEVICE;
   // One record of kStreamMetaRec words per stream (a stream's fields in one
   // line of the pinned slot, read by its prep workgroup in one load):
   // carry index, carry length, offset and number of new samples, segment
@@ -729,7 +744,7 @@ int lm_push(logmel_stream* s, const void* d_new, int sample_type, const int64_t*
   // path) and hands the transform kernel its offsets in meta_dev.
   if (logmel_launch_stream_prep(s->ws, s->stride, d_new, sample_type == LOGMEL_I16,
                                 s->meta_host_dev[slot], s->meta_dev, n, st) != hipSuccess ||
-      hipEventRecord(s->slot_done[slot], st) != hipSuccess)
+      (last && hipEventRecord(s->slot_done[grp], st) != hipSuccess))
     return LOGMEL_ERR_DEVICE;
   s->slot = (slot + 1) % logmel_stream::kSlots;
   if (logmel_launch_tiles(s->plan->tables, s->ws, 0, s->meta_dev + 4 * n, s->meta_dev + 5 * n,
@@ -765,8 +780,10 @@ int rs_push(logmel_stream* s, const void* d_new, int sample_type, const int64_t*
             void* d_out, int out_type, int64_t* fo_out, hipStream_t st, bool flush) {
   const int64_t n = s->n;
   const ResGeometry& geo = s->rs->geo;
-  const int slot = s->rslot;
-  if (hipEventSynchronize(s->rslot_done[slot]) != hipSuccess) return LOGMEL_ERR_DEVICE;
+  const int slot = s->rslot, grp = slot / logmel_stream::kSlotGroup;
+  const bool first = slot % logmel_stream::kSlotGroup == 0;
+  const bool last = slot % logmel_stream::kSlotGroup == logmel_stream::kSlotGroup - 1;
+  if (first && hipEventSynchronize(s->rslot_done[grp]) != hipSuccess) return LOGMEL_ERR_DEVICE;
   int64_t* m = s->rmeta_host[slot];
   std::vector<int64_t> k(n);
   int64_t seg = 0, noff = 0, total_k = 0;
@@ -795,7 +812,7 @@ int rs_push(logmel_stream* s, const void* d_new, int sample_type, const int64_t*
   // its segment arrays in rmeta_dev.
   if (logmel_launch_rstream_prep(dst, src, flush ? nullptr : d_new, sample_type == LOGMEL_I16,
                                  s->rmeta_host_dev[slot], s->rmeta_dev, n, st) != hipSuccess ||
-      hipEventRecord(s->rslot_done[slot], st) != hipSuccess)
+      (last && hipEventRecord(s->rslot_done[grp], st) != hipSuccess))
     return LOGMEL_ERR_DEVICE;
   s->rslot = (slot + 1) % logmel_stream::kSlots;
   if (total_k > 0 &&
