@@ -380,7 +380,8 @@ def _resample_worker(args):
 def bench_resampled(args, lm, plan, torch):
     """One step = the 64 x 30 s batch made at --in-rate, resampled to 16 kHz
     (logmel_resample) and then turned into log-mel (logmel_compute): two
-    launches on one stream, each timed with its own HIP events."""
+    launches on one stream, each timed with its own HIP events (on every
+    --event-every-th step)."""
     import logmel_synth as S
     import numpy as np
     import multiprocessing as mp
@@ -411,13 +412,16 @@ def bench_resampled(args, lm, plan, torch):
     for i in range(args.warmup):
         step(i % n_sets)
     torch.cuda.synchronize()
+    # events on every event_every-th step only (their packets lengthen a step)
+    every = args.event_every if args.steps >= 2 * args.event_every else 1
+    timed = [i for i in range(args.steps) if i % every == 0]
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i % n_sets, ev[i])
+        step(i % n_sets, ev[i] if i % every == 0 else None)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    rs_s = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps / 1e3
-    lm_s = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps / 1e3
+    rs_s = sum(ev[i][0].elapsed_time(ev[i][1]) for i in timed) / len(timed) / 1e3
+    lm_s = sum(ev[i][1].elapsed_time(ev[i][2]) for i in timed) / len(timed) / 1e3
     ms_per_step = wall / args.steps * 1e3
     # taps inside the kernel's support per output: 2 H on average
     H = 24 * rate / (0.96 * min(rate, FS))
