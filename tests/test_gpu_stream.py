@@ -453,3 +453,47 @@ def test_resampling_snapshot_restore(env, rate):
     with pytest.raises((ValueError, lm.LogmelError)):
         lm.logmel_stream_set_state(other, state)
     other.close()
+
+
+def test_push_into_larger_buffer_and_slot_groups(env):
+    """A push into a buffer with spare rows writes exactly its own rows (the
+    rest stay untouched) and returns a view of them, equal bit for bit to the
+    same push into a buffer of its size. Stream objects closed after 1 to 13
+    pushes (inside and at the ends of the staging slots' groups of four)
+    leave the next object's pushes intact, and every frame so far equals the
+    offline frame of the stream's audio."""
+    lm, plan, torch = env
+    n, P, K = 6, 1280, 13
+    streams = S.config3_streams(device="cuda", n_streams=n, n_samples=K * P)
+    ref, fo_ref = offline(env, streams)
+    torch.cuda.synchronize()
+    for k in (1, 3, 4, 5, 8, 9, 13):
+        say(f"slot groups: {k} pushes")
+        s = lm.logmel_stream_create(plan, n, P)
+        t = lm.logmel_stream_create(plan, n, P)
+        big = torch.empty((n * 10, 128), dtype=torch.float32, device="cuda")
+        got = [[] for _ in range(n)]
+        for c in range(k):
+            new = streams[:, c * P:(c + 1) * P].contiguous().reshape(-1)
+            o1, f1 = lm.logmel_stream_push(s, new, [P] * n)
+            big.fill_(float("nan"))
+            o2, f2 = lm.logmel_stream_push(t, new, np.full(n, P), out=big)
+            torch.cuda.synchronize()
+            total = int(f1[-1])
+            assert np.array_equal(f1, f2)
+            assert tuple(o2.shape) == (total, 128) and o2.data_ptr() == big.data_ptr()
+            assert torch.equal(o1, o2), (k, c)
+            assert bool(torch.isnan(big[total:]).all()), (k, c)
+            for j in range(n):
+                got[j].append(o1[f1[j]:f1[j + 1]].clone())
+        with pytest.raises(ValueError):
+            lm.logmel_stream_push(t, streams[:, :P].contiguous().reshape(-1), [P] * n,
+                                  out=big[:4])
+        with pytest.raises(ValueError):
+            lm.logmel_stream_push(t, streams[:, :P].contiguous().reshape(-1), [P] * (n - 1) + [P, 0])
+        s.close()
+        t.close()
+        for j in range(n):
+            m = sum(int(x.shape[0]) for x in got[j])
+            assert m == lm.logmel_num_frames(k * P)
+            assert torch.equal(torch.cat(got[j]), ref[fo_ref[j]:fo_ref[j] + m]), (k, j)
