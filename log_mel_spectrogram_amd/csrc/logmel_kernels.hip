@@ -310,6 +310,17 @@ __device__ __forceinline__ void tiles_body(const In* __restrict__ samples,
   int64_t tile = blockIdx.x * per + min((int64_t)blockIdx.x, extra);
   const int64_t tile_end = tile + per + ((int64_t)blockIdx.x < extra ? 1 : 0);
   if (tile >= tile_end) return;
+  // Wavefronts that start together run their tiles in step, and the four of
+  // a compute unit then issue their span loads and stores at the same time;
+  // tiles run faster once the wavefronts drift apart. Where each wavefront
+  // has several tiles, SIMD s of a compute unit starts s x 1920 cycles late
+  // (the SIMD from the hardware-ID register), so that the four begin out of
+  // step; a launch of one or a few tiles per wavefront, whose time is one
+  // tile's latency, starts at once.
+  if (n_tiles >= 4 * (int64_t)gridDim.x) {
+    const uint32_t simd = __builtin_amdgcn_s_getreg((1 << 11) | (4 << 6) | 4) & 3u;   // HW_ID[5:4]
+    for (uint32_t i = 0; i < simd; ++i) __builtin_amdgcn_s_sleep(30);
+  }
   // The combine's rotations go to LDS (the two halves of a pair read
   // different ones): 100 16-byte entries, loaded now and written after the
   // first tile is located, so that the loads' latency overlaps the lookup.
