@@ -278,3 +278,68 @@ def test_config4_ragged_long_sampled(env):
     say(f"config4: {rep}")
     del x, out
     torch.cuda.empty_cache()
+
+
+
+def _sampled_rows_parity(torch, x, so, fo, out, rows, what):
+    """Rows ``rows`` of ``out`` against the oracle on each row's own 400
+    samples of ``x`` (fp32 on the GPU)."""
+    clip = np.searchsorted(fo, rows, side="right") - 1
+    start = so[clip] + 160 * (rows - fo[clip])
+    idx = torch.from_numpy(start).cuda()[:, None] + torch.arange(400, device="cuda")[None, :]
+    frames = x[idx].cpu().numpy()
+    L, E = O.logmel_frames(frames)
+    Lg = out[torch.from_numpy(rows).cuda()].float().cpu().numpy()
+    return assert_parity(Lg, L, E, what)
+
+
+def test_config4_recipe_past_2_31_samples(env):
+    """The ragged long batch's recipe with seed 20009, whose 200 clips hold
+    2,167,173,778 samples: sample indices pass 2**31, so every sample
+    position must be carried in 64 bits. fp32 input, then the same samples
+    as int16 PCM (read two bytes per sample, another address computation).
+    The oracle checks every clip's first and last three frames, the frames
+    whose 400 samples lie around sample 2**31, 5000 random rows and 2000
+    random rows past sample 2**31, each from its own samples; the frame
+    offsets exactly."""
+    lm, plan, torch = env
+    say("config4 recipe, seed 20009: generate on GPU")
+    x, so = S.config4(device="cuda", seed=20009)
+    assert int(so[-1]) == 2_167_173_778 and int(so[-1]) > 2**31
+    fo = O.frame_offsets(so)
+    total = int(fo[-1])
+    rng = np.random.default_rng(26)
+    rows = []
+    for i in range(len(so) - 1):
+        a, b = int(fo[i]), int(fo[i + 1])
+        rows += list(range(a, min(b, a + 3))) + list(range(max(a, b - 3), b))
+    c = int(np.searchsorted(so, 2**31, side="right")) - 1
+    f0 = int(fo[c]) + (2**31 - int(so[c])) // 160
+    rows += [r for r in range(f0 - 4, f0 + 4) if fo[c] <= r < fo[c + 1]]
+    rows = np.unique(np.concatenate([np.array(rows, dtype=np.int64),
+                                     rng.integers(0, total, 5000),
+                                     rng.integers(f0 + 1, total, 2000)]))
+    clip = np.searchsorted(fo, rows, side="right") - 1
+    start = so[clip] + 160 * (rows - fo[clip])
+    assert int((start > 2**31).sum()) > 1000     # rows that read samples past 2**31
+    so_d = torch.from_numpy(so).cuda()
+    fo_d = torch.from_numpy(fo).cuda()
+    say(f"config4 seed 20009 fp32: samples={int(so[-1])} frames={total}")
+    out = lm.logmel_compute(plan, x, so_d, fo_d, total)
+    torch.cuda.synchronize()
+    rep = _sampled_rows_parity(torch, x, so, fo, out, rows, "past 2**31, fp32 in")
+    say(f"config4 seed 20009 fp32: {rep}")
+    say("config4 seed 20009 int16")
+    x16 = torch.round(x * 32767.0).to(torch.int16)
+    del x
+    torch.cuda.empty_cache()
+    out.fill_(0.0)
+    lm.logmel_compute_ex(plan, x16, so_d, fo_d, total, out=out)
+    torch.cuda.synchronize()
+    xs = x16.to(torch.float32) * (1.0 / 32768.0)
+    del x16
+    torch.cuda.empty_cache()
+    rep = _sampled_rows_parity(torch, xs, so, fo, out, rows, "past 2**31, int16 in")
+    say(f"config4 seed 20009 int16: {rep}")
+    del xs, out
+    torch.cuda.empty_cache()
