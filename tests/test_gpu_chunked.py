@@ -122,6 +122,49 @@ def test_chunked_config2(env):
     check_layout(off, ch, fo, co, so, lm, silent_value(env))
 
 
+
+def test_chunked_past_2_31_samples(env):
+    """The ragged long batch's recipe with seed 20009 (2,167,173,778
+    samples, 4,641 chunks) in the chunk layout: every frame row of every
+    chunk equals the offline row bit for bit and every padding row holds
+    the silent frame's value, compared on the GPU (the layouts are 7 GB
+    each)."""
+    lm, plan, torch = env
+    say("chunked: config4 recipe seed 20009, past 2**31 samples")
+    dev = torch.device("cuda", 0)
+    x, so = S.config4(device=dev, seed=20009)
+    assert int(so[-1]) > 2**31
+    fo = lm.logmel_frame_offsets(so)
+    co = lm.logmel_chunk_offsets(so)
+    so_d = torch.from_numpy(so).to(dev)
+    fo_d = torch.from_numpy(fo).to(dev)
+    co_d = torch.from_numpy(co).to(dev)
+    total, chunks = int(fo[-1]), int(co[-1])
+    off = lm.logmel_compute(plan, x, so_d, fo_d, total)
+    ch = torch.full((chunks, 3000, 128), float("nan"), dtype=torch.float32, device=dev)
+    lm.logmel_compute_chunked(plan, x, so_d, fo_d, co_d, total, chunks, out=ch)
+    torch.cuda.synchronize()
+    del x
+    torch.cuda.empty_cache()
+    # flat chunk row of every frame: co[clip] * 3000 + (frame - fo[clip])
+    clip = torch.from_numpy(np.repeat(np.arange(len(so) - 1), np.diff(fo))).to(dev)
+    frame = torch.arange(total, device=dev)
+    flat = co_d[clip] * 3000 + (frame - fo_d[clip])
+    chf = ch.view(-1, 128)
+    same = torch.zeros(total, dtype=torch.bool, device=dev)
+    for a in range(0, total, 1 << 22):
+        b = min(total, a + (1 << 22))
+        same[a:b] = (chf[flat[a:b]] == off[a:b]).all(dim=1)
+    assert bool(same.all()), int((~same).sum())
+    is_frame = torch.zeros(chunks * 3000, dtype=torch.bool, device=dev)
+    is_frame[flat] = True
+    pad = chf[~is_frame]
+    assert pad.shape[0] == chunks * 3000 - total
+    assert bool((pad == silent_value(env)).all())
+    say(f"chunked past 2**31: {total} frame rows equal offline, {pad.shape[0]} padding rows")
+    del off, ch, chf, pad, same, is_frame, flat
+    torch.cuda.empty_cache()
+
 def test_chunked_validate_and_empty(env, monkeypatch):
     lm, plan, torch = env
     say("chunked: validate mode, empty calls")
