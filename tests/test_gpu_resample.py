@@ -157,6 +157,35 @@ def test_resample_full_size_sampled(env):
           "64 x 30 s at 44.1 kHz (sampled)")
 
 
+
+def test_resample_past_2_31_input_samples(env):
+    """30 speech-like clips of 75,000,017 samples at 44.1 kHz (28 minutes
+    each, 2,250,000,510 samples: input positions pass 2**31), resampled in
+    one launch; outputs at the clips' edges, around input sample 2**31 and
+    3000 random ones against the oracle, computed one by one."""
+    lm, plan, torch = env
+    dev = torch.device("cuda", 0)
+    n = 75_000_017
+    say("30 x 75e6 samples at 44.1 kHz (past 2**31), sampled outputs")
+    x, so = S.pack([n] * 30, lambda i, v: S.speech_like(700 + i, n, dev, out=v, fs=44100), dev)
+    assert int(so[-1]) > 2**31
+    r = lm.logmel_resampler_create(plan, 44100)
+    y, oo = lm.resample(r, x, so)
+    torch.cuda.synchronize()
+    c = int(np.searchsorted(so, 2**31, side="right")) - 1
+    m = int(oo[c]) + ((2**31 - int(so[c])) * 16000) // 44100     # output at input 2**31
+    rng = np.random.default_rng(13)
+    rows = np.unique(np.concatenate([rng.integers(0, int(oo[-1]), 3000),
+                                     oo[:-1], oo[1:] - 1, np.arange(m - 40, m + 40)]))
+    xh = x.cpu().numpy()
+    del x
+    torch.cuda.empty_cache()
+    y_ref, a_ref = O.resample_selected(xh, so, 44100, rows)
+    check(y.cpu().numpy()[rows], y_ref, a_ref, lm.logmel_resampler_info(r)[1],
+          "30 x 75e6 samples at 44.1 kHz (sampled)")
+    del y
+    torch.cuda.empty_cache()
+
 def test_resample_validate_empty_and_unsupported(env, monkeypatch):
     lm, plan, torch = env
     dev = torch.device("cuda", 0)
