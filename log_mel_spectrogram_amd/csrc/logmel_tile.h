@@ -96,11 +96,14 @@ __device__ __forceinline__ TileSrc locate_tile(int64_t tile, int lane,
   }
   const int64_t gq = t.in_range ? t.g : total_frames - 1;   // lookup key for idle lanes
 
-  // Clip of the tile's first frame (wave-uniform): the last c with
-  // frame_off[c] <= g0, by a 64-ary search (one load per lane and one ballot
-  // per level; the entries <= g0 form a prefix).
+  // A clip at or before the tile's first frame's (wave-uniform): a 64-ary
+  // search for the last c with frame_off[c] <= g0 (one load per lane and one
+  // ballot per level; the entries <= g0 form a prefix), stopped once at most
+  // 16 candidates remain. The boundaries read next, 64 from c0 on, place
+  // the remaining candidates as well, so the search costs one round of loads
+  // fewer (none for up to 16 clips).
   int64_t c0 = 0;
-  for (int64_t len = n_clips + 1; len > 1;) {
+  for (int64_t len = n_clips + 1; len > 16;) {
     const int64_t stride = (len + kWaveLanes - 1) / kWaveLanes;
     const int64_t idx = c0 + lane * stride;
     const bool le = idx < c0 + len && frame_off[idx] <= g0;
@@ -113,13 +116,14 @@ __device__ __forceinline__ TileSrc locate_tile(int64_t tile, int lane,
   c0 = max(min(c0, n_clips - 1), (int64_t)0);
   // Then the clip of every pair: lane j holds the j-th clip boundary after
   // c0 (and clip c0 + j's sample range), and each lane counts the boundaries
-  // at or below its frame.
+  // at or below its frame (64 or more of them, a tile among runs of empty or
+  // one-frame clips, take a binary search per lane instead).
   const int64_t bidx = c0 + 1 + lane;
   const int64_t B = bidx <= n_clips ? frame_off[bidx] : INT64_MAX;
   const int64_t cl = min(c0 + lane, n_clips - 1);
   const int64_t SS = seg_start[cl], SE = seg_end[cl], RB = rows.base[cl];
   const int64_t B63 = __shfl(B, 63);
-  int64_t c, fo_c, ss_c, se_c, rb_c;
+  int64_t c, fo_c, ss_c, se_c, rb_c, hi_c;
   // The cross-lane search below needs every lane (__shfl reads inactive
   // lanes as garbage), so the choice is made for the whole wavefront.
   if (__any(B63 <= gq)) {
@@ -130,6 +134,7 @@ __device__ __forceinline__ TileSrc locate_tile(int64_t tile, int lane,
     ss_c = seg_start[c];
     se_c = seg_end[c];
     rb_c = rows.base[c];
+    hi_c = fo_c;          // an empty cache: the next tile is looked up
   } else {
     int cnt = 0;
 #pragma unroll
@@ -142,13 +147,14 @@ __device__ __forceinline__ TileSrc locate_tile(int64_t tile, int lane,
     ss_c = __shfl(SS, j);
     se_c = __shfl(SE, j);
     rb_c = __shfl(RB, j);
+    hi_c = __shfl(B, j);  // frame_off[c + 1], the end of the lane's clip
   }
   const int64_t f = gq - fo_c;
   t.s = ss_c + 160 * f;
   t.row = rb_c * rows.unit + f;
-  // lane 0's clip is the first frame's: cache it (hi from the next boundary)
+  // lane 0's clip is the first frame's: cache it
   cc.lo = uniform64(fo_c);
-  cc.hi = uniform64(c == c0 ? B : fo_c);
+  cc.hi = uniform64(hi_c);
   cc.ss = uniform64(ss_c);
   cc.se = uniform64(se_c);
   cc.rb = uniform64(rb_c);
