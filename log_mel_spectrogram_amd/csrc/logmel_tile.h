@@ -99,11 +99,12 @@ __device__ __forceinline__ TileSrc locate_tile(int64_t tile, int lane,
   // A clip at or before the tile's first frame's (wave-uniform): a 64-ary
   // search for the last c with frame_off[c] <= g0 (one load per lane and one
   // ballot per level; the entries <= g0 form a prefix), stopped once at most
-  // 16 candidates remain. The boundaries read next, 64 from c0 on, place
-  // the remaining candidates as well, so the search costs one round of loads
-  // fewer (none for up to 16 clips).
+  // 16 candidates remain, and not run for up to 64 clips. The boundaries
+  // read next, 64 from c0 on, place the remaining candidates as well (all
+  // of them for up to 64 clips), so the search costs one round of loads
+  // fewer, or none.
   int64_t c0 = 0;
-  for (int64_t len = n_clips + 1; len > 16;) {
+  for (int64_t len = n_clips + 1; len > (n_clips <= kWaveLanes ? kWaveLanes + 1 : 16);) {
     const int64_t stride = (len + kWaveLanes - 1) / kWaveLanes;
     const int64_t idx = c0 + lane * stride;
     const bool le = idx < c0 + len && frame_off[idx] <= g0;
