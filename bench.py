@@ -447,8 +447,9 @@ def bench_resampled(args, lm, plan, torch):
                      "unit": "TFLOP/s", "frac": rs_tflops / FP32_PEAK_TFLOPS,
                      "traffic": measured_traffic("logmel_resample_c2_44k", RESAMPLE_SOURCES)
                      if rate == 44100 else None,
-                     "kernel": "logmel_resample (its instance for this rate: "
-                               "logmel_resample2_wide_8w_kernel at 44.1 kHz)",
+                     "kernel": "logmel_resample" + (" (instance logmel_resample2_wide_8w_kernel)"
+                                                    if rate == 44100 else
+                                                    " (the instance the launcher picks for this rate)"),
                      "kernel_avg_us": rs_s * 1e6,
                      "algorithmic_flops_per_launch": rs_flops,
                      "algorithmic_bytes_per_launch": rs_bytes,
