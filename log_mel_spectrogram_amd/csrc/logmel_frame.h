@@ -38,8 +38,8 @@
 //     rotation (from LDS: the two halves combine different bins)
 //       t = W400^-k conj(R[k]),  |X[k]| = |E[k] + t|,  |X[200 - k]| = |E[k] - t|.
 //     So role 0 holds bins 1..50 and 150..199, role 1 bins 51..149. The
-//     filterbank runs on these halves (see pair_logmel); role 0 logs and
-//     stores bands 0..63, role 1 bands 64..127.
+//     filterbank runs on these halves (see pair_logmel); each role logs and
+//     stores 64 bands, in alternate runs of the row (band_role).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -337,10 +337,10 @@ __device__ __forceinline__ void pair_power(const float (&v)[200], const double* 
 // and 150..199, role 1 those of bins 51..149 (see pair_power), and both run
 // the same code: every band is summed over this lane's registers, which
 // gives the right sum in the half that holds the band's bins (a band whose
-// bins lie in both halves is the sum of two partial sums). Bands 0..63 lie in
-// role 0's half, and role 0 logs them; role 1 logs bands 64..127 and takes
-// the sums that only role 0 holds from its partner (v_permlane32_swap). The
-// log has the 1e-10 floor, taken so that a NaN energy stays NaN.
+// bins lie in both halves is the sum of two partial sums). Each role logs 64
+// bands (band_role); the sums a role logs but the other half holds move
+// across the pair with v_permlane32_swap. The log has the 1e-10 floor, taken
+// so that a NaN energy stays NaN.
 
 // Half of the pair that holds bin b (1..199): 0 for bins 1..50 and
 // 150..199, 1 for bins 51..149.
@@ -366,7 +366,6 @@ __host__ __device__ constexpr bool mel_layout_ok() {
   for (int m = 0; m < 128; ++m) {
     if (kMelCount[m] > 0 && (kMelStart[m] < 1 || kMelStart[m] + kMelCount[m] - 1 > 199))
       return false;                     // bins 0 and 200 have no register
-    if (m < 64 && mel_side(m) > 0) return false;   // role 0 logs bands 0..63 alone
   }
   return true;
 }
@@ -394,67 +393,128 @@ __device__ __forceinline__ float mel_part(const float (&Pp)[51], const float (&P
   return acc;
 }
 
-// Bands 64..127 whose bins lie (also) in role 0's half: role 0's partial
-// sums, moved to role 1 with the whole wavefront active.
-template <int m>
-__device__ __forceinline__ void mel_transfer(const float (&Pp)[51], const float (&Pm)[51], float& t) {
-  if constexpr (mel_side(m) == 0 || mel_side(m) == 2) t = pair_from(mel_part<m, 0>(Pp, Pm), 0);
+// Which role of a pair logs band m: the roles take alternate runs of U
+// bands of the row, role 0 the first (U = 4 for fp32 output: the two lanes
+// of a pair then store adjacent 16-byte pieces of their frame's row, 32
+// contiguous bytes per store instruction and frame, which the memory
+// pipeline takes faster than 16-byte pieces 256 bytes apart; U = 64 for fp16
+// output, one 128-byte run per role, measured faster there).
+template <int U>
+__host__ __device__ constexpr int band_role(int m) { return (m / U) & 1; }
+// The j-th band (j = 0..63) that role r logs.
+template <int U>
+__host__ __device__ constexpr int band_of(int r, int j) { return (j / U) * 2 * U + r * U + j % U; }
+// Whether band m's logging role needs the other half's partial sum.
+template <int U>
+__host__ __device__ constexpr bool band_xfer(int m) {
+  return mel_side(m) == 2 || (mel_side(m) >= 0 && mel_side(m) != band_role<U>(m));
 }
-template <int... I>
-__device__ __forceinline__ void mel_transfers(const float (&Pp)[51], const float (&Pm)[51],
-                                             float (&T)[64], std::integer_sequence<int, I...>) {
-  (mel_transfer<64 + I>(Pp, Pm, T[I]), ...);
+// Slot of band m among the partial sums moved towards its logging role (in
+// band order), and the number moved towards role r.
+template <int U>
+__host__ __device__ constexpr int xfer_slot(int m) {
+  int n = 0;
+  for (int k = 0; k < m; ++k)
+    if (band_xfer<U>(k) && band_role<U>(k) == band_role<U>(m)) ++n;
+  return n;
+}
+template <int U>
+__host__ __device__ constexpr int xfer_count(int r) {
+  int n = 0;
+  for (int k = 0; k < 128; ++k)
+    if (band_xfer<U>(k) && band_role<U>(k) == r) ++n;
+  return n;
 }
 
-// Role 0's bands 0..63 (all in its half).
-template <int m>
-__device__ __forceinline__ float mel_low_band(const float (&Pp)[51], const float (&Pm)[51]) {
-  if constexpr (mel_side(m) < 0) {
-    return 0.0f * Pp[1];   // an empty filter (see mel_high_band)
-  } else {
-    return mel_part<m, 0>(Pp, Pm);
+// The k-th band (in band order) whose partial sum moves towards role r.
+template <int U>
+__host__ __device__ constexpr int xfer_band(int r, int k) {
+  int n = 0;
+  for (int m = 0; m < 128; ++m)
+    if (band_xfer<U>(m) && band_role<U>(m) == r && n++ == k) return m;
+  return -1;
+}
+
+// The k-th moved sum of each direction, formed with the whole wavefront
+// active (half 0's partial sum for the k-th band role 1 logs, half 1's for
+// the k-th band role 0 logs) and exchanged with one v_permlane32_swap; a
+// select by half then leaves role 0's received sum in lanes 0..31 and role
+// 1's in lanes 32..63 of one register.
+template <int U, int k, int NM>
+__device__ __forceinline__ void xfer_one(const float (&Pp)[51], const float (&Pm)[51], bool upper,
+                                         float (&M)[NM]) {
+  constexpr int N0 = xfer_count<U>(1), N1 = xfer_count<U>(0);
+  if constexpr (k < N0 && k < N1) {
+    const float x0 = mel_part<xfer_band<U>(1, k), 0>(Pp, Pm);
+    const float x1 = mel_part<xfer_band<U>(0, k), 1>(Pp, Pm);
+    const auto w = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x1),
+                                                     __builtin_bit_cast(uint32_t, x0), false,
+                                                     false);
+    // w[0]: x0 of lanes 0..31 in lanes 32..63; w[1]: x1 of lanes 32..63 in lanes 0..31
+    M[k] = __builtin_bit_cast(float, upper ? w[0] : w[1]);
+  } else if constexpr (k < N0) {
+    M[k] = pair_from(mel_part<xfer_band<U>(1, k), 0>(Pp, Pm), 0);
+  } else if constexpr (k < N1) {
+    M[k] = pair_from(mel_part<xfer_band<U>(0, k), 1>(Pp, Pm), 1);
   }
 }
-template <int... I>
-__device__ __forceinline__ void mel_low(const float (&Pp)[51], const float (&Pm)[51], float (&E)[64],
-                                        std::integer_sequence<int, I...>) {
-  ((E[I] = mel_low_band<I>(Pp, Pm)), ...);
+template <int U, int NM, int... K>
+__device__ __forceinline__ void xfer_all(const float (&Pp)[51], const float (&Pm)[51], bool upper,
+                                         float (&M)[NM], std::integer_sequence<int, K...>) {
+  (xfer_one<U, K, NM>(Pp, Pm, upper, M), ...);
 }
 
-template <int m>
-__device__ __forceinline__ float mel_high_band(const float (&Pp)[51], const float (&Pm)[51], float t) {
+// Energy of the j-th band role r logs; R holds the partial sums received
+// from the other half (right in role r's lanes).
+template <int U, int r, int j, int NR>
+__device__ __forceinline__ float band_energy(const float (&Pp)[51], const float (&Pm)[51],
+                                             const float (&R)[NR > 0 ? NR : 1]) {
+  constexpr int m = band_of<U>(r, j);
   constexpr int side = mel_side(m);
+  constexpr int slot = band_xfer<U>(m) ? xfer_slot<U>(m) : 0;
   if constexpr (side < 0) {
     // An empty filter's sum of zero-weight terms: 0, or NaN where the
     // frame's powers are NaN (a NaN sample reaches every bin).
     return 0.0f * Pp[1];
-  } else if constexpr (side == 0) {
-    return t;
-  } else if constexpr (side == 1) {
-    return mel_part<m, 1>(Pp, Pm);
+  } else if constexpr (side == r) {
+    return mel_part<m, r>(Pp, Pm);
+  } else if constexpr (side == 1 - r) {
+    return R[slot];
   } else {
-    return t + mel_part<m, 1>(Pp, Pm);
+    // Half 0's partial sum plus half 1's, one rounding, whichever role adds
+    // them: with contraction off the add is not folded into the last
+    // multiply-add of either sum, so the fp32 and fp16 kernels (whose roles
+    // log different bands) give a band the same energy.
+    const float own = mel_part<m, r>(Pp, Pm), other = R[slot];
+    {
+#pragma clang fp contract(off)
+      return own + other;
+    }
   }
 }
-// Role 1's bands 64..127.
-template <int... I>
-__device__ __forceinline__ void mel_high(const float (&Pp)[51], const float (&Pm)[51],
-                                         const float (&T)[64], float (&E)[64],
-                                         std::integer_sequence<int, I...>) {
-  ((E[I] = mel_high_band<64 + I>(Pp, Pm, T[I])), ...);
+template <int U, int r, int NR, int... J>
+__device__ __forceinline__ void role_bands(const float (&Pp)[51], const float (&Pm)[51],
+                                           const float (&R)[NR > 0 ? NR : 1], float (&E)[64],
+                                           std::integer_sequence<int, J...>) {
+  ((E[J] = band_energy<U, r, J, NR>(Pp, Pm, R)), ...);
 }
 
+// The log-mel values of the 64 bands this lane logs, out[j] for band
+// band_of<U>(role, j).
+template <int U>
 __device__ __forceinline__ void pair_logmel(const float (&Pp)[51], const float (&Pm)[51], int role,
                                             float (&out)[64]) {
-  float T[64];
-  mel_transfers(Pp, Pm, T, std::make_integer_sequence<int, 64>{});
+  constexpr int N0 = xfer_count<U>(1), N1 = xfer_count<U>(0);   // towards role 1, role 0
+  constexpr int NM = (N0 > N1 ? N0 : N1) > 0 ? (N0 > N1 ? N0 : N1) : 1;
+  float M[NM];
+  xfer_all<U, NM>(Pp, Pm, role != 0, M, std::make_integer_sequence<int, NM>{});
   // Each role sums only the bands it logs (the other half of the wavefront
   // is masked off meanwhile), so no select between the two sets is needed.
   float E[64];
   if (role == 0) {
-    mel_low(Pp, Pm, E, std::make_integer_sequence<int, 64>{});
+    role_bands<U, 0, NM>(Pp, Pm, M, E, std::make_integer_sequence<int, 64>{});
   } else {
-    mel_high(Pp, Pm, T, E, std::make_integer_sequence<int, 64>{});
+    role_bands<U, 1, NM>(Pp, Pm, M, E, std::make_integer_sequence<int, 64>{});
   }
 #pragma unroll
   for (int i = 0; i < 64; ++i) {

@@ -261,18 +261,35 @@ __device__ __forceinline__ void pieces_to_lds(const In* __restrict__ samples, co
 // ---------------------------------------------------------------------------
 // Output types: fp32, or fp16 (each value rounded once to nearest).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void store_bands(float* __restrict__ dst, const float (&o)[64]) {
-  float4* d = reinterpret_cast<float4*>(dst);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) d[i] = make_float4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+// A lane's 64 values are the bands its role logs, in runs of kBandRun<Out>
+// bands (the roles take alternate runs of the row, role 0 the first; see
+// band_role in logmel_frame.h): 4 for fp32 output, 64 for fp16.
+template <typename Out> constexpr int kBandRun = sizeof(Out) == 4 ? 4 : 64;
+
+// Element offset in the row of the lane's value j (the start of a 16-byte
+// piece when j is a multiple of its width).
+template <int U>
+__device__ __forceinline__ int run_offset(int role, int j) {
+  return (j / U) * 2 * U + role * U + j % U;
 }
 
-__device__ __forceinline__ void store_bands(_Float16* __restrict__ dst, const float (&o)[64]) {
-  uint4* d = reinterpret_cast<uint4*>(dst);
+__device__ __forceinline__ void store_bands(float* __restrict__ row, int role, const float (&o)[64]) {
+  constexpr int U = kBandRun<float>;
+  static_assert(U % 4 == 0, "runs of whole 16-byte pieces");
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    *reinterpret_cast<float4*>(row + run_offset<U>(role, 4 * i)) =
+        make_float4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+}
+
+__device__ __forceinline__ void store_bands(_Float16* __restrict__ row, int role, const float (&o)[64]) {
+  constexpr int U = kBandRun<_Float16>;
+  static_assert(U % 8 == 0, "runs of whole 16-byte pieces");
 #pragma unroll
   for (int i = 0; i < 8; ++i)
-    d[i] = make_uint4(pack_half2(o[8 * i], o[8 * i + 1]), pack_half2(o[8 * i + 2], o[8 * i + 3]),
-                      pack_half2(o[8 * i + 4], o[8 * i + 5]), pack_half2(o[8 * i + 6], o[8 * i + 7]));
+    *reinterpret_cast<uint4*>(row + run_offset<U>(role, 8 * i)) =
+        make_uint4(pack_half2(o[8 * i], o[8 * i + 1]), pack_half2(o[8 * i + 2], o[8 * i + 3]),
+                   pack_half2(o[8 * i + 4], o[8 * i + 5]), pack_half2(o[8 * i + 6], o[8 * i + 7]));
 }
 
 template <typename In> struct SpanOf;
@@ -432,11 +449,11 @@ __device__ __forceinline__ void tiles_body(const In* __restrict__ samples,
     load_span(more && nxt.fast ? samples : span_pad, more && nxt.fast ? nxt.s0 : 0, lane, span);
 
     float o[64];
-    pair_logmel(Pp, Pm, role, o);
+    pair_logmel<kBandRun<Out>>(Pp, Pm, role, o);
     const int64_t g = tile * kTile + fl;
     const int64_t row = row_lds[it & 1][ln & 31];
     if (g < total_frames && row >= 0 && row < out_rows)
-      store_bands(out + row * 128 + 64 * role, o);
+      store_bands(out + row * 128, role, o);
     if (!more) break;
     tile = next;
     cur = nxt;
