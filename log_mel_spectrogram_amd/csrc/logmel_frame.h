@@ -394,11 +394,10 @@ __device__ __forceinline__ float mel_part(const float (&Pp)[51], const float (&P
 }
 
 // Which role of a pair logs band m: the roles take alternate runs of U
-// bands of the row, role 0 the first (U = 4 for fp32 output: the two lanes
-// of a pair then store adjacent 16-byte pieces of their frame's row, 32
-// contiguous bytes per store instruction and frame, which the memory
-// pipeline takes faster than 16-byte pieces 256 bytes apart; U = 64 for fp16
-// output, one 128-byte run per role, measured faster there).
+// bands of the row, role 0 the first. With a run of one 16-byte piece (U = 4
+// for fp32 output, 8 for fp16) the two lanes of a pair store adjacent pieces
+// of their frame's row, 32 contiguous bytes per store instruction and frame,
+// which the memory pipeline takes faster than pieces 256 bytes apart.
 template <int U>
 __host__ __device__ constexpr int band_role(int m) { return (m / U) & 1; }
 // The j-th band (j = 0..63) that role r logs.

@@ -263,8 +263,9 @@ __device__ __forceinline__ void pieces_to_lds(const In* __restrict__ samples, co
 // ---------------------------------------------------------------------------
 // A lane's 64 values are the bands its role logs, in runs of kBandRun<Out>
 // bands (the roles take alternate runs of the row, role 0 the first; see
-// band_role in logmel_frame.h): 4 for fp32 output, 64 for fp16.
-template <typename Out> constexpr int kBandRun = sizeof(Out) == 4 ? 4 : 64;
+// band_role in logmel_frame.h): one 16-byte piece, 4 bands of fp32 output or
+// 8 of fp16.
+template <typename Out> constexpr int kBandRun = 16 / (int)sizeof(Out);
 
 // Element offset in the row of the lane's value j (the start of a 16-byte
 // piece when j is a multiple of its width).
