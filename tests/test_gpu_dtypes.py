@@ -169,6 +169,32 @@ def test_fp16_output(env):
     assert bl == 0 and bq == 0
 
 
+
+def test_fp16_config2_is_fp32_rounded(env):
+    """The 64 x 30 s batch (24.6 M values), fp32 and int16 input: the fp16
+    output is the fp32 output rounded once, bit for bit. The two kernels
+    split the bands between a pair's lanes differently (alternate runs of 4
+    bands for fp32 output, of 8 for fp16), so a band whose bins lie in both
+    halves is added up by different lanes; its energy must not depend on
+    that."""
+    lm, plan, torch = env
+    say("fp16 output: config2, fp16 = fp32 rounded, bit for bit")
+    dev = torch.device("cuda", 0)
+    x, so = S.config2(device=dev)
+    fo, co, so_d, fo_d, co_d = offsets(env, so)
+    T = int(fo[-1])
+    f = lm.logmel_compute_ex(plan, x, so_d, fo_d, T)
+    h = lm.logmel_compute_ex(plan, x, so_d, fo_d, T, out_dtype=torch.float16)
+    torch.cuda.synchronize()
+    diff = int((h != f.half()).sum())
+    s16 = torch.clamp(torch.round(x * 32768.0), -32768, 32767).to(torch.int16)
+    f16in = lm.logmel_compute_ex(plan, s16, so_d, fo_d, T)
+    h16 = lm.logmel_compute_ex(plan, s16, so_d, fo_d, T, out_dtype=torch.float16)
+    torch.cuda.synchronize()
+    diff16 = int((h16 != f16in.half()).sum())
+    say(f"fp16 config2: {diff} and {diff16} values differ from the rounded fp32 output")
+    assert diff == 0 and diff16 == 0
+
 def test_unsupported_types(env):
     lm, plan, torch = env
     say("unsupported sample and output types")
