@@ -740,10 +740,18 @@ int lm_push(logmel_stream* s, const void* d_new, int sample_type, const int64_t*
   const int64_t total_frames = fo[n];
   if (total_frames > INT64_MAX / kMels) return LOGMEL_ERR_INPUT_TOO_LONG;
   if (total_frames > 0 && !d_out) return LOGMEL_ERR_INVALID_ARGUMENT;
-  // The prep kernel reads the slot in place (no copy engine in the push's
-  // path) and hands the transform kernel its offsets in meta_dev.
+  // Every stream in the same state and pushing the same number of samples
+  // (a fixed audio clock): the prep kernel derives the records from its
+  // arguments and reads no host memory.
+  StreamUniform uni{1, push_len[0], s->carry_len[0], s->carry_src[0], 0};
+  for (int64_t j = 1; j < n && uni.on; ++j)
+    uni.on = push_len[j] == uni.P && s->carry_len[j] == uni.c &&
+             s->carry_src[j] - j * s->stride == uni.d;
+  uni.F = frames_of(uni.c + uni.P);
+  // Otherwise the prep kernel reads the slot in place (no copy engine in the
+  // push's path). It hands the transform kernel its offsets in meta_dev.
   if (logmel_launch_stream_prep(s->ws, s->stride, d_new, sample_type == LOGMEL_I16,
-                                s->meta_host_dev[slot], s->meta_dev, n, st) != hipSuccess ||
+                                s->meta_host_dev[slot], s->meta_dev, n, uni, st) != hipSuccess ||
       (last && hipEventRecord(s->slot_done[grp], st) != hipSuccess))
     return LOGMEL_ERR_DEVICE;
   s->slot = (slot + 1) % logmel_stream::kSlots;
@@ -959,7 +967,8 @@ int logmel_stream_push_static(const logmel_plan* plan, int64_t n_streams, const 
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   if (hipMemcpyAsync(rec_dev, S.rec, (size_t)n_streams * kStreamMetaRec * 8,
                      hipMemcpyHostToDevice, st) != hipSuccess ||
-      logmel_launch_stream_prep(ws, kStaticStride, d_new, 0, rec_dev, meta_dev, n_streams, st) !=
+      logmel_launch_stream_prep(ws, kStaticStride, d_new, 0, rec_dev, meta_dev, n_streams,
+                                StreamUniform{0, 0, 0, 0, 0}, st) !=
           hipSuccess ||
       logmel_launch_tiles(plan->tables, ws, 0, meta_dev + 4 * n_streams, meta_dev + 5 * n_streams,
                           meta_dev + 6 * n_streams, n_streams, total_frames, d_out, 0,

@@ -30,13 +30,22 @@ hipError_t logmel_launch_chunk_pad(void* out, int out_f16, const int64_t* frame_
                                    const int64_t* chunk_off, int64_t n_clips, int64_t out_rows,
                                    hipStream_t stream);
 
+// A push in which every stream has the same carry length c, its carry at
+// the same place of its workspace row (stream j's at j * row_stride + d),
+// and the same number P of new samples: every field of stream j's record
+// follows from these, and F = frames of c + P (on = 0: read the records).
+struct StreamUniform {
+  int64_t on, P, c, d, F;
+};
+
 // fresh: fp32, or int16 PCM (s / 32768) with in_i16. meta: the host's
 // staging slot (pinned host memory, its device-side address; records as in
-// logmel_stream.hip); the kernel copies what the transform kernel reads into
-// meta_dev ([4n, 7n + 1): segment starts, ends, frame offsets).
+// logmel_stream.hip), read only where the push is not uniform; the kernel
+// writes what the transform kernel reads into meta_dev ([4n, 7n + 1):
+// segment starts, ends, frame offsets).
 hipError_t logmel_launch_stream_prep(float* ws, int64_t row_stride, const void* fresh, int in_i16,
                                      const int64_t* meta, int64_t* meta_dev, int64_t n_streams,
-                                     hipStream_t stream);
+                                     StreamUniform uni, hipStream_t stream);
 
 
 // The fixed device array of logmel_stream_push_static (logmel_static.hip):

@@ -35,24 +35,40 @@ __device__ __forceinline__ float stream_sample(const int16_t* p, int64_t i) {
 // The kernel copies fields 4, 5 and 6 into meta_dev ([4n, 5n), [5n, 6n),
 // [6n + 1, 7n + 1), with 0 at 6n), where the transform kernel that follows
 // reads them.
+// A uniform push (see StreamUniform) takes every field from the kernel's
+// arguments and reads no host memory.
 template <typename In>
 __device__ __forceinline__ void stream_prep_body(float* __restrict__ ws, int64_t row_stride,
                                                  const In* __restrict__ fresh,
                                                  const int64_t* __restrict__ meta,
                                                  int64_t* __restrict__ meta_dev,
-                                                 int64_t n_streams) {
+                                                 int64_t n_streams, StreamUniform u) {
   const int64_t j = blockIdx.x;
   const int t = threadIdx.x;
   const int64_t base = j * row_stride;
-  const int64_t* rec = meta + j * kStreamMetaRec;
-  const int64_t src = rec[0];
-  const int64_t clen = rec[1];
-  const int64_t noff = rec[2];
-  const int64_t nlen = rec[3];
+  int64_t src, clen, noff, nlen, seg0, seg1, fo1;
+  if (u.on) {
+    src = base + u.d;
+    clen = u.c;
+    noff = j * u.P;
+    nlen = u.P;
+    seg0 = base + 400 - u.c;
+    seg1 = base + 400 + u.P;
+    fo1 = (j + 1) * u.F;
+  } else {
+    const int64_t* rec = meta + j * kStreamMetaRec;
+    src = rec[0];
+    clen = rec[1];
+    noff = rec[2];
+    nlen = rec[3];
+    seg0 = rec[4];
+    seg1 = rec[5];
+    fo1 = rec[6];
+  }
   // the transform kernel's inputs: segment start and end, frame offsets
-  if (t == 0) meta_dev[4 * n_streams + j] = rec[4];
-  if (t == 1) meta_dev[5 * n_streams + j] = rec[5];
-  if (t == 2) meta_dev[6 * n_streams + j + 1] = rec[6];
+  if (t == 0) meta_dev[4 * n_streams + j] = seg0;
+  if (t == 1) meta_dev[5 * n_streams + j] = seg1;
+  if (t == 2) meta_dev[6 * n_streams + j + 1] = fo1;
   if (t == 3 && j == 0) meta_dev[6 * n_streams] = 0;
   // The carry can overlap its destination, and the new samples land where
   // the old ones were: read the carry and the first new samples before any
@@ -84,15 +100,15 @@ __device__ __forceinline__ void stream_prep_body(float* __restrict__ ws, int64_t
 extern "C" __global__ void __launch_bounds__(256)
 logmel_stream_prep_kernel(float* __restrict__ ws, int64_t row_stride,
                           const float* __restrict__ fresh, const int64_t* __restrict__ meta,
-                          int64_t* __restrict__ meta_dev, int64_t n_streams) {
-  stream_prep_body(ws, row_stride, fresh, meta, meta_dev, n_streams);
+                          int64_t* __restrict__ meta_dev, int64_t n_streams, StreamUniform u) {
+  stream_prep_body(ws, row_stride, fresh, meta, meta_dev, n_streams, u);
 }
 
 extern "C" __global__ void __launch_bounds__(256)
 logmel_stream_prep_i16_kernel(float* __restrict__ ws, int64_t row_stride,
                               const int16_t* __restrict__ fresh, const int64_t* __restrict__ meta,
-                              int64_t* __restrict__ meta_dev, int64_t n_streams) {
-  stream_prep_body(ws, row_stride, fresh, meta, meta_dev, n_streams);
+                              int64_t* __restrict__ meta_dev, int64_t n_streams, StreamUniform u) {
+  stream_prep_body(ws, row_stride, fresh, meta, meta_dev, n_streams, u);
 }
 
 // A resampling stream's push, step 1: one workgroup per stream builds its
@@ -194,15 +210,15 @@ hipError_t logmel_launch_rstream_prep(float* dst, const float* src, const void* 
 
 hipError_t logmel_launch_stream_prep(float* ws, int64_t row_stride, const void* fresh, int in_i16,
                                      const int64_t* meta, int64_t* meta_dev, int64_t n_streams,
-                                     hipStream_t stream) {
+                                     StreamUniform uni, hipStream_t stream) {
   if (n_streams <= 0) return hipSuccess;
   if (in_i16)
     hipLaunchKernelGGL(logmel::logmel_stream_prep_i16_kernel, dim3((unsigned)n_streams), dim3(256),
                        0, stream, ws, row_stride, static_cast<const int16_t*>(fresh), meta,
-                       meta_dev, n_streams);
+                       meta_dev, n_streams, uni);
   else
     hipLaunchKernelGGL(logmel::logmel_stream_prep_kernel, dim3((unsigned)n_streams), dim3(256), 0,
                        stream, ws, row_stride, static_cast<const float*>(fresh), meta, meta_dev,
-                       n_streams);
+                       n_streams, uni);
   return hipGetLastError();
 }
