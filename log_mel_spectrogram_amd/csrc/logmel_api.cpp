@@ -816,10 +816,21 @@ int rs_push(logmel_stream* s, const void* d_new, int sample_type, const int64_t*
   }
   float* src = s->in_buf[s->in_cur];
   float* dst = s->in_buf[1 - s->in_cur];
-  // The prep kernel reads the slot in place and hands the resampling kernel
-  // its segment arrays in rmeta_dev.
+  // Every stream in the same state and pushing the same number of samples
+  // (a fixed audio clock): the prep kernel derives the records from its
+  // arguments (the carries then lie src_step apart, as they were cut from
+  // equal segments) and reads no host memory.
+  RStreamUniform uni{1, s->rcarry_len[0], flush ? 0 : push_len[0], s->rcarry_src[0],
+                     n > 1 ? s->rcarry_src[1] - s->rcarry_src[0] : 0, s->rs_in[0], s->rs_out[0],
+                     k[0]};
+  for (int64_t j = 1; j < n && uni.on; ++j)
+    uni.on = s->rcarry_len[j] == uni.c && (flush ? 0 : push_len[j]) == uni.p &&
+             s->rcarry_src[j] == uni.src0 + j * uni.src_step && s->rs_in[j] == uni.rs_in &&
+             s->rs_out[j] == uni.rs_out && k[j] == uni.k;
+  // Otherwise the prep kernel reads the slot in place. It hands the
+  // resampling kernel its segment arrays in rmeta_dev.
   if (logmel_launch_rstream_prep(dst, src, flush ? nullptr : d_new, sample_type == LOGMEL_I16,
-                                 s->rmeta_host_dev[slot], s->rmeta_dev, n, st) != hipSuccess ||
+                                 s->rmeta_host_dev[slot], s->rmeta_dev, n, uni, st) != hipSuccess ||
       (last && hipEventRecord(s->rslot_done[grp], st) != hipSuccess))
     return LOGMEL_ERR_DEVICE;
   s->rslot = (slot + 1) % logmel_stream::kSlots;

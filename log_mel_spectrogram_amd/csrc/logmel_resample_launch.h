@@ -44,7 +44,13 @@ hipError_t logmel_launch_resample(const void* x, int in_i16, const int64_t* seg_
 // staging slot (pinned host memory, its device-side address; records as in
 // logmel_stream.hip), of which the kernel copies the resampling kernel's
 // part into meta_dev ([5n, 9n + 1): clip origins, segment ends, first
-// outputs, output offsets).
+// outputs, output offsets). Where every stream is in the same state (carry
+// length c, retained and produced counts rs_in, rs_out, carries spaced
+// src_step apart from src0) and pushes the same p samples for k outputs,
+// every record follows from these and the kernel reads no host memory.
+struct RStreamUniform {
+  int64_t on, c, p, src0, src_step, rs_in, rs_out, k;
+};
 hipError_t logmel_launch_rstream_prep(float* dst, const float* src, const void* fresh, int in_i16,
                                       const int64_t* meta, int64_t* meta_dev, int64_t n_streams,
-                                      hipStream_t stream);
+                                      RStreamUniform uni, hipStream_t stream);

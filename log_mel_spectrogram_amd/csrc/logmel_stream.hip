@@ -127,22 +127,41 @@ __device__ __forceinline__ void rstream_prep_body(float* __restrict__ dst,
                                                   const In* __restrict__ fresh,
                                                   const int64_t* __restrict__ meta,
                                                   int64_t* __restrict__ meta_dev,
-                                                  int64_t n_streams) {
+                                                  int64_t n_streams, RStreamUniform u) {
   const int64_t j = blockIdx.x;
   const int t = threadIdx.x;
-  const int64_t* rec = meta + j * kRStreamMetaRec;
-  const int64_t csrc = rec[0];
-  const int64_t clen = rec[1];
-  const int64_t noff = rec[2];
-  const int64_t nlen = rec[3];
+  int64_t csrc, clen, noff, nlen, seg0, f5, f6, f7, f8;
+  if (u.on) {
+    // every stream in the same state: its record from the arguments
+    csrc = u.src0 + j * u.src_step;
+    clen = u.c;
+    noff = j * u.p;
+    nlen = u.p;
+    seg0 = j * (u.c + u.p);
+    f5 = seg0 - (u.rs_in - u.c);
+    f6 = seg0 + u.c + u.p;
+    f7 = u.rs_out;
+    f8 = (j + 1) * u.k;
+  } else {
+    const int64_t* rec = meta + j * kRStreamMetaRec;
+    csrc = rec[0];
+    clen = rec[1];
+    noff = rec[2];
+    nlen = rec[3];
+    seg0 = rec[4];
+    f5 = rec[5];
+    f6 = rec[6];
+    f7 = rec[7];
+    f8 = rec[8];
+  }
   // the resampling kernel's inputs: segment origin, end, first output
   // number and output offsets
-  if (t == 0) meta_dev[5 * n_streams + j] = rec[5];
-  if (t == 1) meta_dev[6 * n_streams + j] = rec[6];
-  if (t == 2) meta_dev[7 * n_streams + j] = rec[7];
-  if (t == 3) meta_dev[8 * n_streams + j + 1] = rec[8];
+  if (t == 0) meta_dev[5 * n_streams + j] = f5;
+  if (t == 1) meta_dev[6 * n_streams + j] = f6;
+  if (t == 2) meta_dev[7 * n_streams + j] = f7;
+  if (t == 3) meta_dev[8 * n_streams + j + 1] = f8;
   if (t == 4 && j == 0) meta_dev[8 * n_streams] = 0;
-  float* seg = dst + rec[4];
+  float* seg = dst + seg0;
   // src and dst are different buffers: eight loads per thread in flight
   // before their stores
   constexpr int kBatch = 8;
@@ -179,32 +198,32 @@ __device__ __forceinline__ void rstream_prep_body(float* __restrict__ dst,
 extern "C" __global__ void __launch_bounds__(256)
 logmel_rstream_prep_kernel(float* __restrict__ dst, const float* __restrict__ src,
                            const float* __restrict__ fresh, const int64_t* __restrict__ meta,
-                           int64_t* __restrict__ meta_dev, int64_t n_streams) {
-  rstream_prep_body(dst, src, fresh, meta, meta_dev, n_streams);
+                           int64_t* __restrict__ meta_dev, int64_t n_streams, RStreamUniform u) {
+  rstream_prep_body(dst, src, fresh, meta, meta_dev, n_streams, u);
 }
 
 extern "C" __global__ void __launch_bounds__(256)
 logmel_rstream_prep_i16_kernel(float* __restrict__ dst, const float* __restrict__ src,
                                const int16_t* __restrict__ fresh,
                                const int64_t* __restrict__ meta, int64_t* __restrict__ meta_dev,
-                               int64_t n_streams) {
-  rstream_prep_body(dst, src, fresh, meta, meta_dev, n_streams);
+                               int64_t n_streams, RStreamUniform u) {
+  rstream_prep_body(dst, src, fresh, meta, meta_dev, n_streams, u);
 }
 
 }  // namespace logmel
 
 hipError_t logmel_launch_rstream_prep(float* dst, const float* src, const void* fresh, int in_i16,
                                       const int64_t* meta, int64_t* meta_dev, int64_t n_streams,
-                                      hipStream_t stream) {
+                                      RStreamUniform uni, hipStream_t stream) {
   if (n_streams <= 0) return hipSuccess;
   if (in_i16)
     hipLaunchKernelGGL(logmel::logmel_rstream_prep_i16_kernel, dim3((unsigned)n_streams),
                        dim3(256), 0, stream, dst, src, static_cast<const int16_t*>(fresh), meta,
-                       meta_dev, n_streams);
+                       meta_dev, n_streams, uni);
   else
     hipLaunchKernelGGL(logmel::logmel_rstream_prep_kernel, dim3((unsigned)n_streams), dim3(256),
                        0, stream, dst, src, static_cast<const float*>(fresh), meta, meta_dev,
-                       n_streams);
+                       n_streams, uni);
   return hipGetLastError();
 }
 
