@@ -260,7 +260,8 @@ struct logmel_stream {
   std::vector<int64_t> seen, emitted, carry_len, carry_src;
 
   // Streams at another input rate: each push is resampled to 16 kHz first,
-  // and the 16 kHz samples go through the part above. Per stream, the input
+  // straight into the workspace rows above, whose frames are then
+  // transformed as for a 16 kHz push. Per stream, the input
   // samples the next outputs' windows still need (at most 2J) are kept as a
   // carry, in one of two packed input buffers that alternate from push to
   // push.
@@ -271,7 +272,6 @@ struct logmel_stream {
   int64_t in_stride = 0;                // a stream's room in an input buffer
   float* in_buf[2] = {nullptr, nullptr};
   int in_cur = 0;                       // the buffer holding the carries
-  float* res_buf = nullptr;             // one push's 16 kHz samples, packed
   int64_t* rmeta_dev = nullptr;         // [9n + 1], layout in rs_push
   int64_t* rmeta_host[kSlots] = {};      // the same ring for the resampling prep
   int64_t* rmeta_host_dev[kSlots] = {};
@@ -578,7 +578,6 @@ void logmel_stream_destroy(logmel_stream* s) {
   if (s->meta_dev) (void)hipFree(s->meta_dev);
   for (int i = 0; i < 2; ++i)
     if (s->in_buf[i]) (void)hipFree(s->in_buf[i]);
-  if (s->res_buf) (void)hipFree(s->res_buf);
   if (s->rmeta_dev) (void)hipFree(s->rmeta_dev);
   if (s->rs) logmel_resampler_destroy(s->rs);
   delete s;
@@ -635,8 +634,7 @@ int logmel_stream_create_ex(const logmel_plan* plan, int64_t n_streams, int64_t 
   bool ok = true;
   for (int i = 0; ok && i < 2; ++i)
     ok = hipMalloc(&s->in_buf[i], (size_t)n_streams * s->in_stride * sizeof(float)) == hipSuccess;
-  ok = ok && hipMalloc(&s->res_buf, (size_t)n_streams * max16 * sizeof(float)) == hipSuccess &&
-       hipMalloc(&s->rmeta_dev, rmeta_words * 8) == hipSuccess;
+  ok = ok && hipMalloc(&s->rmeta_dev, rmeta_words * 8) == hipSuccess;
   for (int i = 0; ok && i < logmel_stream::kSlots; ++i)
     ok = hipHostMalloc(&s->rmeta_host[i], kRStreamMetaRec * (size_t)n_streams * 8,
                        hipHostMallocDefault) == hipSuccess &&
@@ -703,6 +701,33 @@ int logmel_stream_push(logmel_stream* s, const float* d_new, const int64_t* push
 
 namespace {
 
+// The 16 kHz part of a push once its segments are in place (each stream's
+// carry, then its push_len[j] new samples, from row j's float 400 - carry
+// on, and the transform kernel's offsets in meta_dev): the transform of
+// every completed frame into d_out (frame offsets fo), then the host shadow.
+int lm_transform(logmel_stream* s, const int64_t* push_len, const std::vector<int64_t>& fo,
+                 void* d_out, int out_type, int64_t* fo_out, hipStream_t st) {
+  const int64_t n = s->n;
+  const int64_t total_frames = fo[n];
+  if (logmel_launch_tiles(s->plan->tables, s->ws, 0, s->meta_dev + 4 * n, s->meta_dev + 5 * n,
+                          s->meta_dev + 6 * n, n, total_frames, d_out, out_type == LOGMEL_F16,
+                          s->meta_dev + 6 * n, 1, total_frames, s->plan->resident_waves, st) !=
+      hipSuccess)
+    return LOGMEL_ERR_DEVICE;
+  // Advance the host shadow.
+  for (int64_t j = 0; j < n; ++j) {
+    const int64_t c = s->carry_len[j], p = push_len[j];
+    const int64_t F = frames_of(c + p);
+    const int64_t seg0 = j * s->stride + kRing - c;
+    s->carry_src[j] = seg0 + kHop * F;
+    s->carry_len[j] = c + p - kHop * F;
+    s->seen[j] += p;
+    s->emitted[j] += F;
+  }
+  if (fo_out) std::memcpy(fo_out, fo.data(), (n + 1) * sizeof(int64_t));
+  return LOGMEL_OK;
+}
+
 // The 16 kHz part of a push: push_len[j] <= max_push new samples per stream
 // (checked by the caller), the device on.
 int lm_push(logmel_stream* s, const void* d_new, int sample_type, const int64_t* push_len,
@@ -755,35 +780,24 @@ int lm_push(logmel_stream* s, const void* d_new, int sample_type, const int64_t*
       (last && hipEventRecord(s->slot_done[grp], st) != hipSuccess))
     return LOGMEL_ERR_DEVICE;
   s->slot = (slot + 1) % logmel_stream::kSlots;
-  if (logmel_launch_tiles(s->plan->tables, s->ws, 0, s->meta_dev + 4 * n, s->meta_dev + 5 * n,
-                          s->meta_dev + 6 * n, n, total_frames, d_out, out_type == LOGMEL_F16,
-                          s->meta_dev + 6 * n, 1, total_frames, s->plan->resident_waves, st) !=
-      hipSuccess)
-    return LOGMEL_ERR_DEVICE;
-  // Advance the host shadow.
-  for (int64_t j = 0; j < n; ++j) {
-    const int64_t c = s->carry_len[j], p = push_len[j];
-    const int64_t F = frames_of(c + p);
-    const int64_t seg0 = j * s->stride + kRing - c;
-    s->carry_src[j] = seg0 + kHop * F;
-    s->carry_len[j] = c + p - kHop * F;
-    s->seen[j] += p;
-    s->emitted[j] += F;
-  }
-  if (fo_out) std::memcpy(fo_out, fo.data(), (n + 1) * sizeof(int64_t));
-  return LOGMEL_OK;
+  return lm_transform(s, push_len, fo, d_out, out_type, fo_out, st);
 }
 
 // The resampling part of a push (or, with flush, of the end of the
 // streams): builds each stream's segment (carry, then the new samples) in
-// the other input buffer, resamples every output the segment completes, and
-// passes those 16 kHz samples to lm_push. Slot layout: one record of
+// the other input buffer and moves each stream's 16 kHz carry in its
+// workspace row (one prep kernel), resamples every output the segment
+// completes straight into the rows after those carries, and transforms the
+// completed frames (lm_transform). Slot layout: one record of
 // kRStreamMetaRec int64 per stream (one line of the pinned slot):
 //   0 carry index in the carry buffer    1 carry length
 //   2 offset of the new samples in d_new  3 number of new samples
 //   4 segment start in the new buffer     5 buffer index of the clip's sample 0
 //   6 segment end                         7 number of the first output
-//   8 output offset after the stream
+//   8 output offset after the stream      9 16 kHz carry index in the workspace
+//  10 16 kHz carry length                11 16 kHz samples of the push
+//  12 frame offset after the stream
+static_assert(kRStreamMetaRec >= 13, "a resampling push's record has 13 fields");
 int rs_push(logmel_stream* s, const void* d_new, int sample_type, const int64_t* push_len,
             void* d_out, int out_type, int64_t* fo_out, hipStream_t st, bool flush) {
   const int64_t n = s->n;
@@ -793,7 +807,8 @@ int rs_push(logmel_stream* s, const void* d_new, int sample_type, const int64_t*
   const bool last = slot % logmel_stream::kSlotGroup == logmel_stream::kSlotGroup - 1;
   if (first && hipEventSynchronize(s->rslot_done[grp]) != hipSuccess) return LOGMEL_ERR_DEVICE;
   int64_t* m = s->rmeta_host[slot];
-  std::vector<int64_t> k(n);
+  std::vector<int64_t> k(n), fo(n + 1);
+  fo[0] = 0;
   int64_t seg = 0, noff = 0, total_k = 0;
   for (int64_t j = 0; j < n; ++j) {
     const int64_t c = s->rcarry_len[j];
@@ -811,9 +826,17 @@ int rs_push(logmel_stream* s, const void* d_new, int sample_type, const int64_t*
     r[6] = seg + c + p;
     r[7] = s->rs_out[j];
     r[8] = total_k;
+    fo[j + 1] = fo[j] + frames_of(s->carry_len[j] + k[j]);
+    r[9] = s->carry_src[j];
+    r[10] = s->carry_len[j];
+    r[11] = k[j];
+    r[12] = fo[j + 1];
     seg += c + p;
     noff += p;
   }
+  const int64_t total_frames = fo[n];
+  if (total_frames > INT64_MAX / kMels) return LOGMEL_ERR_INPUT_TOO_LONG;
+  if (total_frames > 0 && !d_out) return LOGMEL_ERR_INVALID_ARGUMENT;
   float* src = s->in_buf[s->in_cur];
   float* dst = s->in_buf[1 - s->in_cur];
   // Every stream in the same state and pushing the same number of samples
@@ -827,19 +850,30 @@ int rs_push(logmel_stream* s, const void* d_new, int sample_type, const int64_t*
     uni.on = s->rcarry_len[j] == uni.c && (flush ? 0 : push_len[j]) == uni.p &&
              s->rcarry_src[j] == uni.src0 + j * uni.src_step && s->rs_in[j] == uni.rs_in &&
              s->rs_out[j] == uni.rs_out && k[j] == uni.k;
+  // and the 16 kHz carries of one length at one place in their rows
+  StreamUniform uni16{uni.on, k[0], s->carry_len[0], s->carry_src[0], 0};
+  for (int64_t j = 1; j < n && uni16.on; ++j)
+    uni16.on = s->carry_len[j] == uni16.c && s->carry_src[j] - j * s->stride == uni16.d;
+  uni16.F = frames_of(uni16.c + uni16.P);
+  uni.on = uni16.on;
   // Otherwise the prep kernel reads the slot in place. It hands the
-  // resampling kernel its segment arrays in rmeta_dev.
+  // resampling kernel its segment arrays in rmeta_dev and the transform
+  // kernel its offsets in meta_dev.
   if (logmel_launch_rstream_prep(dst, src, flush ? nullptr : d_new, sample_type == LOGMEL_I16,
-                                 s->rmeta_host_dev[slot], s->rmeta_dev, n, uni, st) != hipSuccess ||
+                                 s->rmeta_host_dev[slot], s->rmeta_dev, n, uni, s->ws, s->stride,
+                                 s->meta_dev, uni16, st) != hipSuccess ||
       (last && hipEventRecord(s->rslot_done[grp], st) != hipSuccess))
     return LOGMEL_ERR_DEVICE;
   s->rslot = (slot + 1) % logmel_stream::kSlots;
+  // stream j's k[j] <= max_push outputs go to its workspace row from float
+  // 400 on, which holds them (stride >= 400 + max_push)
   if (total_k > 0 &&
       logmel_launch_resample(dst, 0, s->rmeta_dev + 5 * n, s->rmeta_dev + 6 * n,
-                             s->rmeta_dev + 7 * n, s->rmeta_dev + 8 * n, n, total_k, s->res_buf,
-                             s->rs->btab, s->rs->abase, s->rs_k, st) != hipSuccess)
+                             s->rmeta_dev + 7 * n, s->rmeta_dev + 8 * n, n, total_k, s->ws,
+                             s->stride, kRing, s->rs->btab, s->rs->abase, s->rs_k, st) !=
+          hipSuccess)
     return LOGMEL_ERR_DEVICE;
-  const int r = lm_push(s, s->res_buf, LOGMEL_F32, k.data(), d_out, out_type, fo_out, st);
+  const int r = lm_transform(s, k.data(), fo, d_out, out_type, fo_out, st);
   if (r != LOGMEL_OK) return r;
   // Advance the host shadow: keep the input from the first window the next
   // outputs need.
@@ -1225,7 +1259,7 @@ int logmel_resample(const logmel_resampler* r, const void* d_samples, int sample
   }
   if (logmel_launch_resample(d_samples, sample_type == LOGMEL_I16, d_sample_offsets,
                              d_sample_offsets + 1, nullptr, d_out_offsets, n_clips, total_out,
-                             d_out, r->btab, r->abase, r->geo.k, st) !=
+                             d_out, 0, 0, r->btab, r->abase, r->geo.k, st) !=
       hipSuccess)
     return LOGMEL_ERR_DEVICE;
   return LOGMEL_OK;

@@ -120,6 +120,7 @@ __device__ __forceinline__ void rsm_body(const In* __restrict__ x, const int64_t
                                          const int64_t* __restrict__ nfirst,
                                          const int64_t* __restrict__ out_off, int64_t n_segs,
                                          int64_t total_out, float* __restrict__ y,
+                                         int64_t ystep, int64_t ybase,
                                          const float* __restrict__ btab,
                                          const int* __restrict__ abase, const RsmGeometry geo,
                                          int64_t win, float* xs) {
@@ -139,6 +140,9 @@ __device__ __forceinline__ void rsm_body(const In* __restrict__ x, const int64_t
     if (o_hi <= w0 || o_hi <= o_lo) continue;
     const int64_t nf = nfirst ? nfirst[c] : 0;
     const int64_t cnt = o_hi - o_lo;
+    // where the segment's outputs go: packed from y[o_lo] on, or (ystep > 0)
+    // from y[c ystep + ybase] on, row c of a strided layout
+    const int64_t ob = ystep > 0 ? c * ystep + ybase : o_lo;
     const int64_t j_first = nf / TB, j_last = (nf + cnt - 1) / TB;
     const int64_t lo = seg_lo[c], avail_hi = seg_hi[c];
     const int64_t avail_lo = max(lo, c > 0 ? seg_hi[c - 1] : (int64_t)0);
@@ -259,7 +263,7 @@ __device__ __forceinline__ void rsm_body(const In* __restrict__ x, const int64_t
             // offsets that overstate the output (a precondition the device
             // does not check) write nothing outside it
             const int64_t o = o_lo + (nn - nf);
-            if (nn >= nf && nn < nf + cnt && o >= 0 && o < total_out) y[o] = acc[rb][r];
+            if (nn >= nf && nn < nf + cnt && o >= 0 && o < total_out) y[ob + (nn - nf)] = acc[rb][r];
           }
       }
     }
@@ -271,11 +275,11 @@ __device__ __forceinline__ void rsm_body(const In* __restrict__ x, const int64_t
   NAME(const IN* __restrict__ x, const int64_t* __restrict__ seg_lo,                            \
        const int64_t* __restrict__ seg_hi, const int64_t* __restrict__ nfirst,                  \
        const int64_t* __restrict__ out_off, int64_t n_segs, int64_t total_out,                  \
-       float* __restrict__ y, const float* __restrict__ btab, const int* __restrict__ abase,     \
-       RsmGeometry geo, int64_t win) {                                                           \
+       float* __restrict__ y, int64_t ystep, int64_t ybase, const float* __restrict__ btab,     \
+       const int* __restrict__ abase, RsmGeometry geo, int64_t win) {                            \
     extern __shared__ float xs[];                                                                \
-    rsm_body<RB, STG, NTH, IN>(x, seg_lo, seg_hi, nfirst, out_off, n_segs, total_out, y, btab, abase, geo, \
-                     win, xs);                                                                        \
+    rsm_body<RB, STG, NTH, IN>(x, seg_lo, seg_hi, nfirst, out_off, n_segs, total_out, y, ystep, ybase, \
+                               btab, abase, geo, win, xs);                                       \
   }
 
 LOGMEL_RESAMPLE_KERNEL(logmel_resample_kernel, float, 1, 8, 256)
@@ -300,8 +304,8 @@ LOGMEL_RESAMPLE_KERNEL(logmel_resample2_wide_i16_8w_kernel, int16_t, 2, 32, 512)
 hipError_t logmel_launch_resample(const void* x, int in_i16, const int64_t* seg_lo,
                                   const int64_t* seg_hi, const int64_t* nfirst,
                                   const int64_t* out_off, int64_t n_segs, int64_t total_out,
-                                  float* y, const float* btab, const int* abase,
-                                  const RsmGeometry& geo, hipStream_t stream) {
+                                  float* y, int64_t ystep, int64_t ybase, const float* btab,
+                                  const int* abase, const RsmGeometry& geo, hipStream_t stream) {
   if (total_out <= 0 || n_segs <= 0) return hipSuccess;
   // windows of one tile's size; a call of few windows (a stream's push,
   // whose segment edges cut many partial tiles) halves them, down to TB / 8,
@@ -314,7 +318,7 @@ hipError_t logmel_launch_resample(const void* x, int in_i16, const int64_t* seg_
 #define LOGMEL_RSM(K, IN)                                                                        \
   hipLaunchKernelGGL(logmel::K, dim3((unsigned)blocks), dim3(threads), lds, stream,         \
                      static_cast<const IN*>(x), seg_lo, seg_hi, nfirst, out_off, n_segs,         \
-                     total_out, y, btab, abase, geo, win)
+                     total_out, y, ystep, ybase, btab, abase, geo, win)
   // large spans: 32 staged samples per thread in flight, else 8 (fewer
   // registers, more workgroups per compute unit); 8 wavefronts per
   // workgroup when a tile has 8 items or more, else 4

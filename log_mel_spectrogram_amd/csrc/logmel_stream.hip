@@ -113,24 +113,35 @@ logmel_stream_prep_i16_kernel(float* __restrict__ ws, int64_t row_stride,
 
 // A resampling stream's push, step 1: one workgroup per stream builds its
 // segment in dst: the retained input samples (from the previous push's
-// buffer src), then the new ones (fp32, or int16 PCM as s / 32768). meta is
-// the host's staging slot (pinned host memory, read in place), one record of
-// kRStreamMetaRec int64 per stream (one line): 0 carry index in src,
-// 1 carry length, 2 offset of the new samples, 3 their number, 4 segment
-// start in dst, 5 buffer index of the clip's sample 0, 6 segment end,
-// 7 number of the first output, 8 output offset after the stream. The
-// kernel copies fields 5 to 8 into the resampling kernel's segment arrays in
-// meta_dev ([5n, 6n), [6n, 7n), [7n, 8n), [8n + 1, 9n + 1), with 0 at 8n).
+// buffer src), then the new ones (fp32, or int16 PCM as s / 32768). It also
+// moves the stream's 16 kHz carry to sit right before row base + 400 of the
+// workspace ws, where the resampling kernel then writes the push's 16 kHz
+// samples, so that no copy of them follows. meta is the host's staging slot
+// (pinned host memory, read in place), one record of kRStreamMetaRec int64
+// per stream (one line): 0 carry index in src, 1 carry length, 2 offset of
+// the new samples, 3 their number, 4 segment start in dst, 5 buffer index
+// of the clip's sample 0, 6 segment end, 7 number of the first output,
+// 8 output offset after the stream, 9 16 kHz carry index in ws, 10 its
+// length, 11 the push's 16 kHz samples, 12 frame offset after the stream.
+// The kernel copies fields 5 to 8 into the resampling kernel's segment
+// arrays in meta_dev ([5n, 6n), [6n, 7n), [7n, 8n), [8n + 1, 9n + 1), with
+// 0 at 8n) and the transform kernel's segment starts, ends and frame
+// offsets into meta16_dev as the 16 kHz prep kernel does. A uniform push
+// (RStreamUniform and StreamUniform both on) reads no host memory.
 template <typename In>
 __device__ __forceinline__ void rstream_prep_body(float* __restrict__ dst,
                                                   const float* __restrict__ src,
                                                   const In* __restrict__ fresh,
                                                   const int64_t* __restrict__ meta,
                                                   int64_t* __restrict__ meta_dev,
-                                                  int64_t n_streams, RStreamUniform u) {
+                                                  int64_t n_streams, RStreamUniform u,
+                                                  float* __restrict__ ws, int64_t row_stride,
+                                                  int64_t* __restrict__ meta16_dev,
+                                                  StreamUniform u16) {
   const int64_t j = blockIdx.x;
   const int t = threadIdx.x;
-  int64_t csrc, clen, noff, nlen, seg0, f5, f6, f7, f8;
+  const int64_t base = j * row_stride;
+  int64_t csrc, clen, noff, nlen, seg0, f5, f6, f7, f8, src16, clen16, k16, fo1;
   if (u.on) {
     // every stream in the same state: its record from the arguments
     csrc = u.src0 + j * u.src_step;
@@ -142,6 +153,10 @@ __device__ __forceinline__ void rstream_prep_body(float* __restrict__ dst,
     f6 = seg0 + u.c + u.p;
     f7 = u.rs_out;
     f8 = (j + 1) * u.k;
+    src16 = base + u16.d;
+    clen16 = u16.c;
+    k16 = u16.P;
+    fo1 = (j + 1) * u16.F;
   } else {
     const int64_t* rec = meta + j * kRStreamMetaRec;
     csrc = rec[0];
@@ -153,6 +168,10 @@ __device__ __forceinline__ void rstream_prep_body(float* __restrict__ dst,
     f6 = rec[6];
     f7 = rec[7];
     f8 = rec[8];
+    src16 = rec[9];
+    clen16 = rec[10];
+    k16 = rec[11];
+    fo1 = rec[12];
   }
   // the resampling kernel's inputs: segment origin, end, first output
   // number and output offsets
@@ -161,6 +180,18 @@ __device__ __forceinline__ void rstream_prep_body(float* __restrict__ dst,
   if (t == 2) meta_dev[7 * n_streams + j] = f7;
   if (t == 3) meta_dev[8 * n_streams + j + 1] = f8;
   if (t == 4 && j == 0) meta_dev[8 * n_streams] = 0;
+  // the transform kernel's: segment start and end in ws, frame offsets
+  if (t == 5) meta16_dev[4 * n_streams + j] = base + 400 - clen16;
+  if (t == 6) meta16_dev[5 * n_streams + j] = base + 400 + k16;
+  if (t == 7) meta16_dev[6 * n_streams + j + 1] = fo1;
+  if (t == 8 && j == 0) meta16_dev[6 * n_streams] = 0;
+  // The 16 kHz carry can overlap its destination: read it all, then write.
+  float c0 = 0.f, c1 = 0.f;
+  if (t < clen16) c0 = ws[src16 + t];
+  if (t + 256 < clen16) c1 = ws[src16 + t + 256];
+  __syncthreads();
+  if (t < clen16) ws[base + 400 - clen16 + t] = c0;
+  if (t + 256 < clen16) ws[base + 400 - clen16 + t + 256] = c1;
   float* seg = dst + seg0;
   // src and dst are different buffers: eight loads per thread in flight
   // before their stores
@@ -198,32 +229,38 @@ __device__ __forceinline__ void rstream_prep_body(float* __restrict__ dst,
 extern "C" __global__ void __launch_bounds__(256)
 logmel_rstream_prep_kernel(float* __restrict__ dst, const float* __restrict__ src,
                            const float* __restrict__ fresh, const int64_t* __restrict__ meta,
-                           int64_t* __restrict__ meta_dev, int64_t n_streams, RStreamUniform u) {
-  rstream_prep_body(dst, src, fresh, meta, meta_dev, n_streams, u);
+                           int64_t* __restrict__ meta_dev, int64_t n_streams, RStreamUniform u,
+                           float* __restrict__ ws, int64_t row_stride,
+                           int64_t* __restrict__ meta16_dev, StreamUniform u16) {
+  rstream_prep_body(dst, src, fresh, meta, meta_dev, n_streams, u, ws, row_stride, meta16_dev, u16);
 }
 
 extern "C" __global__ void __launch_bounds__(256)
 logmel_rstream_prep_i16_kernel(float* __restrict__ dst, const float* __restrict__ src,
                                const int16_t* __restrict__ fresh,
                                const int64_t* __restrict__ meta, int64_t* __restrict__ meta_dev,
-                               int64_t n_streams, RStreamUniform u) {
-  rstream_prep_body(dst, src, fresh, meta, meta_dev, n_streams, u);
+                               int64_t n_streams, RStreamUniform u, float* __restrict__ ws,
+                               int64_t row_stride, int64_t* __restrict__ meta16_dev,
+                               StreamUniform u16) {
+  rstream_prep_body(dst, src, fresh, meta, meta_dev, n_streams, u, ws, row_stride, meta16_dev, u16);
 }
 
 }  // namespace logmel
 
 hipError_t logmel_launch_rstream_prep(float* dst, const float* src, const void* fresh, int in_i16,
                                       const int64_t* meta, int64_t* meta_dev, int64_t n_streams,
-                                      RStreamUniform uni, hipStream_t stream) {
+                                      RStreamUniform uni, float* ws, int64_t row_stride,
+                                      int64_t* meta16_dev, StreamUniform uni16,
+                                      hipStream_t stream) {
   if (n_streams <= 0) return hipSuccess;
   if (in_i16)
     hipLaunchKernelGGL(logmel::logmel_rstream_prep_i16_kernel, dim3((unsigned)n_streams),
                        dim3(256), 0, stream, dst, src, static_cast<const int16_t*>(fresh), meta,
-                       meta_dev, n_streams, uni);
+                       meta_dev, n_streams, uni, ws, row_stride, meta16_dev, uni16);
   else
     hipLaunchKernelGGL(logmel::logmel_rstream_prep_kernel, dim3((unsigned)n_streams), dim3(256),
                        0, stream, dst, src, static_cast<const float*>(fresh), meta, meta_dev,
-                       n_streams, uni);
+                       n_streams, uni, ws, row_stride, meta16_dev, uni16);
   return hipGetLastError();
 }
 
