@@ -261,16 +261,23 @@ def test_stream_push_ex_rejects_types(env):
     s.close()
 
 
-def resampled_streams_case(env, rate, n, seconds, seed, in_dtype="f32", out_dtype="f32"):
+def resampled_streams_case(env, rate, n, seconds, seed, in_dtype="f32", out_dtype="f32",
+                           uniform=False):
     """Streams at `rate`: ragged pushes around 80 ms, then a flush; each
     stream's frames equal, bit for bit, logmel_resample of the whole input
-    followed by logmel_compute."""
+    followed by logmel_compute. With uniform, every stream is `seconds` long
+    and every push is 80 ms (the last one shorter, the same for all), so
+    the streams stay in one state and each push, the flush included, takes
+    the records that follow from the prep kernel's arguments."""
     lm, plan, torch = env
     dev = torch.device("cuda", 0)
     rng = np.random.default_rng(seed)
-    lens = [int(rng.integers(int(0.2 * rate), int(seconds * rate))) for _ in range(n)]
-    lens[0] = 0
-    lens[1] = 37
+    if uniform:
+        lens = [int(seconds * rate) + 123] * n
+    else:
+        lens = [int(rng.integers(int(0.2 * rate), int(seconds * rate))) for _ in range(n)]
+        lens[0] = 0
+        lens[1] = 37
     clips = [S.speech_like(900 + j, max(L, 1), "cuda", fs=rate)[:L] for j, L in enumerate(lens)]
     if in_dtype == "i16":
         clips = [torch.clamp(torch.round(c * 32768.0), -32768, 32767).to(torch.int16) for c in clips]
@@ -288,7 +295,10 @@ def resampled_streams_case(env, rate, n, seconds, seed, in_dtype="f32", out_dtyp
     pos = np.zeros(n, dtype=np.int64)
     k = 0
     while (pos < np.array(lens)).any():
-        pl = np.full(n, push) if k % 3 else rng.integers(0, push + push // 2 + 1, n)
+        if uniform:
+            pl = np.full(n, push)
+        else:
+            pl = np.full(n, push) if k % 3 else rng.integers(0, push + push // 2 + 1, n)
         pl = np.minimum(pl, np.array(lens) - pos)
         new = torch.cat([clips[j][pos[j]:pos[j] + pl[j]] for j in range(n)]).contiguous()
         fo_pred = lm.logmel_stream_frames_for_push(s, pl)
@@ -325,6 +335,20 @@ def test_resampling_streams_equal_offline(env, rate):
 def test_resampling_streams_int16_fp16(env):
     say("resampling streams at 48 kHz, int16 in, fp16 out")
     resampled_streams_case(env, 48000, 6, 2.0, 5, in_dtype="i16", out_dtype="f16")
+
+
+@pytest.mark.parametrize("rate,in_dtype,out_dtype", [(48000, "f32", "f32"), (44100, "f32", "f32"),
+                                                     (8000, "f32", "f32"), (48000, "i16", "f16")])
+def test_resampling_streams_uniform_pushes(env, rate, in_dtype, out_dtype):
+    """Streams in one state pushing one length (a fixed audio clock): the
+    prep kernel builds every record from its arguments, for the input
+    segments, the resampler's segment arrays, the 16 kHz carries and the
+    transform's offsets; the frames still equal offline resampling then
+    log-mel bit for bit."""
+    say(f"resampling streams at {rate} Hz, uniform pushes, {in_dtype} in, {out_dtype} out")
+    pushes = resampled_streams_case(env, rate, 24, 1.5, 3, in_dtype=in_dtype,
+                                    out_dtype=out_dtype, uniform=True)
+    say(f"{rate} Hz uniform: {pushes} pushes and a flush equal offline")
 
 
 def test_resampling_stream_limits(env):
