@@ -697,3 +697,69 @@ def test_nan_frame_is_nan_in_every_band():
     assert np.all(np.isnan(L[bad]))
     good = [f for f in range(L.shape[0]) if f not in bad]
     assert np.all(np.isfinite(L[good]))
+
+
+def _library_audio_utils():
+    return pytest.importorskip("transformers.audio_utils")
+
+
+def test_filterbank_is_library_htk_bank():
+    """The triangles as read (linear in Hz between vertices evenly spaced on
+    the HTK mel scale, unnormalised; page 1, §2.3 step 4) are the bank that
+    an independent library routine builds for mel_scale "htk", no norm:
+    equal to fp64 rounding. The one cell whose support differs is filter
+    128 at bin 200 (8000 Hz), where the oracle puts the end vertex exactly
+    on 8000 Hz (weight 0) and the library's mel round trip lands a few ulps
+    above it (weight ~1e-14). Both leave the same narrow low filters empty.
+    Catches a triangle built in mel instead of Hz, a normalised bank, or
+    vertices off by one."""
+    au = _library_audio_utils()
+    import warnings
+    with warnings.catch_warnings():
+        warnings.simplefilter("ignore")   # the library warns about the empty filters
+        T = au.mel_filter_bank(201, 128, 0.0, 8000.0, 16000, norm=None, mel_scale="htk").T
+    W = O.mel_filterbank()
+    assert T.shape == W.shape == (128, 201)
+    assert np.max(np.abs(W - T)) < 1e-13
+    differ = np.argwhere((W > 0) != (T > 0))
+    assert [tuple(map(int, ij)) for ij in differ] == [(127, 200)]
+    assert W[127, 200] == 0.0 and T[127, 200] < 1e-13
+    assert np.array_equal(np.where(W.sum(1) == 0)[0], np.where(T.sum(1) == 0)[0])
+    assert np.allclose(au.hertz_to_mel(np.array([0.0, 700.0, 8000.0]), mel_scale="htk"),
+                       O.hz_to_mel(np.array([0.0, 700.0, 8000.0])), rtol=1e-15, atol=0)
+
+
+@pytest.mark.parametrize("kind", ["noise", "tone_1k_full_scale", "dc", "silence_then_noise"])
+def test_logmel_is_library_spectrogram(kind):
+    """The whole chain (page 1, §2.3 steps 1-5: 400-sample frames at hop 160
+    without centring, symmetric Hamming window, 400-point rFFT, power, HTK
+    bank, ln of max(E, 1e-10)) against an independent library spectrogram
+    routine given the same parameters and its own window and bank. The
+    library keeps each frame's spectrum in complex64, so each bin's power
+    carries a relative rounding of about 2**-23 and each band's log up to
+    ~2.5e-7; 1e-6 is the bound. A wrong hop, a periodic window, a centred
+    frame, a dropped partial frame kept, |X| instead of |X|^2 or log10 are
+    all off by far more."""
+    au = _library_audio_utils()
+    import warnings
+    rng = np.random.default_rng(21)
+    n = 16000 + 123
+    if kind == "noise":
+        x = 0.3 * rng.standard_normal(n)
+    elif kind == "tone_1k_full_scale":
+        x = np.sin(2 * np.pi * 1000.0 * np.arange(n) / 16000.0)
+    elif kind == "dc":
+        x = np.full(n, 0.5)
+    else:
+        x = np.concatenate([np.zeros(4000), 0.1 * rng.standard_normal(n - 4000)])
+    x32 = x.astype(np.float32)
+    L, E, _ = O.logmel_packed(x32, np.array([0, n], dtype=np.int64))
+    with warnings.catch_warnings():
+        warnings.simplefilter("ignore")
+        T = au.mel_filter_bank(201, 128, 0.0, 8000.0, 16000, norm=None, mel_scale="htk")
+    w = au.window_function(400, "hamming", periodic=False)
+    S = au.spectrogram(x32.astype(np.float64), w, frame_length=400, hop_length=160,
+                       fft_length=400, power=2.0, center=False, mel_filters=T, mel_floor=1e-10,
+                       log_mel="log", dtype=np.float64).T
+    assert S.shape == L.shape == (O.num_frames(n), 128)
+    assert np.max(np.abs(S - L)) < 1e-6
