@@ -185,43 +185,43 @@ __device__ __forceinline__ void rstream_prep_body(float* __restrict__ dst,
   if (t == 6) meta16_dev[5 * n_streams + j] = base + 400 + k16;
   if (t == 7) meta16_dev[6 * n_streams + j + 1] = fo1;
   if (t == 8 && j == 0) meta16_dev[6 * n_streams] = 0;
-  // The 16 kHz carry can overlap its destination: read it all, then write.
+  // The segment is the carry (from src) followed by the new samples; src and
+  // dst are different buffers, and so are ws and both. The 16 kHz carry can
+  // overlap its destination: read it, and the segment's first kBatch * 256
+  // values (a whole push at the usual clocks), before any write, so that one
+  // round trip to memory serves them all.
+  constexpr int kBatch = 16;
+  const int64_t total = clen + nlen;
+  const In* in = fresh + noff;
+  float* seg = dst + seg0;
   float c0 = 0.f, c1 = 0.f;
   if (t < clen16) c0 = ws[src16 + t];
   if (t + 256 < clen16) c1 = ws[src16 + t + 256];
+  float v[kBatch];
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u) {
+    const int64_t i = t + 256 * u;
+    v[u] = i < clen ? src[csrc + i] : (i < total ? stream_sample(in, i - clen) : 0.0f);
+  }
   __syncthreads();
   if (t < clen16) ws[base + 400 - clen16 + t] = c0;
   if (t + 256 < clen16) ws[base + 400 - clen16 + t + 256] = c1;
-  float* seg = dst + seg0;
-  // src and dst are different buffers: eight loads per thread in flight
-  // before their stores
-  constexpr int kBatch = 8;
-  for (int64_t i0 = 0; i0 < clen; i0 += 256 * kBatch) {
-    float v[kBatch];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int64_t i = i0 + t + 256 * u;
-      v[u] = i < clen ? src[csrc + i] : 0.0f;
-    }
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int64_t i = i0 + t + 256 * u;
-      if (i < clen) seg[i] = v[u];
-    }
+  for (int u = 0; u < kBatch; ++u) {
+    const int64_t i = t + 256 * u;
+    if (i < total) seg[i] = v[u];
   }
-  const In* in = fresh + noff;
-  float* row = seg + clen;
-  for (int64_t i0 = 0; i0 < nlen; i0 += 256 * kBatch) {
-    float v[kBatch];
+  // longer segments (large pushes, high input rates): the rest in batches
+  for (int64_t i0 = 256 * kBatch; i0 < total; i0 += 256 * kBatch) {
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int64_t i = i0 + t + 256 * u;
-      v[u] = i < nlen ? stream_sample(in, i) : 0.0f;
+      v[u] = i < clen ? src[csrc + i] : (i < total ? stream_sample(in, i - clen) : 0.0f);
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int64_t i = i0 + t + 256 * u;
-      if (i < nlen) row[i] = v[u];
+      if (i < total) seg[i] = v[u];
     }
   }
 }
