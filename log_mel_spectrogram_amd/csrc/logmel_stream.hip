@@ -71,13 +71,13 @@ __device__ __forceinline__ void stream_prep_body(float* __restrict__ ws, int64_t
   if (t == 2) meta_dev[6 * n_streams + j + 1] = fo1;
   if (t == 3 && j == 0) meta_dev[6 * n_streams] = 0;
   // The carry can overlap its destination, and the new samples land where
-  // the old ones were: read the carry and the first new samples before any
-  // write.
+  // the old ones were: read the carry and the first new samples (4,096: a
+  // whole push at the 80, 120 and 160 ms clocks) before any write.
   float c0 = 0.f, c1 = 0.f;
   if (t < clen) c0 = ws[src + t];
   if (t + 256 < clen) c1 = ws[src + t + 256];
   const In* in = fresh + noff;
-  constexpr int kBatch = 8;
+  constexpr int kBatch = 16;
   float v[kBatch];
 #pragma unroll
   for (int u = 0; u < kBatch; ++u) {
